@@ -1,0 +1,159 @@
+/* liblrattnres: the LR-AttnRes depth-mix read on AMD Instinct MI355X (gfx950).
+ *
+ * The read (LR-AttnRes paper, §3.1 routing equation with the sliced key of §3.3; the
+ * author's explainer, "A short description chooses a full-width value"): for every token t
+ * at one read site with n sources o_1..o_n (each a row of d values) and the site's static
+ * query q (r values, the same for every token),
+ *
+ *     k_i     = the last r coordinates of o_i                 (a view, no key projection)
+ *     rho_i   = sqrt(mean_j k_ij^2 + eps)                      (parameter-free RMS)
+ *     z_i     = q . k_i / rho_i
+ *     alpha_i = exp(z_i) / sum_j exp(z_j)                      (softmax over sources)
+ *     h       = sum_i alpha_i o_i                              (all d coordinates)
+ *
+ * With r = d this is standard AttnRes. The two-phase block schedule (AttnRes technical-report
+ * summary, "Method": Phase 1 batches a block's static queries against the cached block
+ * representations, Phase 2 merges each site's intra-block partial sum by an online-softmax
+ * update; LR-AttnRes paper §3.4 shows the sliced key keeps both conditions) is exposed as
+ * lrar_forward_stats + lrar_merge. The backward follows the paper's App. B.3 (Lemma 2 and
+ * Corollary 2.1).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named src/out/acc/m/l/q/dout/dsrc/dq/alpha/workspace is a
+ *     DEVICE pointer; arrays of pointers (src, src_ld, dsrc, dsrc_ld) are HOST arrays that
+ *     are read during the call only. The caller owns all memory; the library never
+ *     allocates, frees or synchronises.
+ *   - Matrices are row-major with an explicit row stride in ELEMENTS of their own type
+ *     (ld >= d). A source is [T, d]; several sources may be the same buffer.
+ *   - io selects the element type of sources and of out: LRAR_BF16 (raw bfloat16 bits) or
+ *     LRAR_F32. q, m, l, alpha, dout, dsrc and dq are always float32.
+ *   - Arithmetic: scores, RMS and softmax in float64 (bf16 x fp32 products are exact in
+ *     float64); the value mix accumulates in float32 and rounds to nearest-even on output.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous. Calls that overlap on one device race only on buffers they share.
+ *   - Every function validates all arguments before touching the device and returns a
+ *     status; nothing throws or aborts. lrar_last_error() describes the last failure on
+ *     the calling thread.
+ *   - Rows are fully vectorised (16-byte accesses) when d is a multiple of 8 (bf16) or 4
+ *     (f32) and every row start is 16-byte aligned; other shapes (e.g. d = 513, odd
+ *     strides) take a scalar path that computes the same result more slowly.
+ */
+#ifndef LRATTNRES_H_
+#define LRATTNRES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRAR_MAX_SOURCES 64 /* sources per read (full routing needs 2L+1) */
+#define LRAR_MAX_QUERIES 64 /* site queries per Phase-1 call */
+
+typedef enum lrar_status {
+  LRAR_OK = 0,
+  LRAR_ERR_INVALID = 1,     /* an argument is out of range, null or aliased */
+  LRAR_ERR_UNSUPPORTED = 2, /* valid, but this shape/variant combination is not built */
+  LRAR_ERR_DEVICE = 3       /* the HIP runtime reported an error at launch */
+} lrar_status;
+
+typedef enum lrar_dtype { LRAR_F32 = 0, LRAR_BF16 = 1 } lrar_dtype;
+
+typedef enum lrar_variant {
+  LRAR_VARIANT_AUTO = 0,     /* pick per shape */
+  LRAR_VARIANT_TWO_PASS = 1, /* key slices first, softmax once, then stream the values */
+  LRAR_VARIANT_ONLINE = 2    /* one pass per source with an online-softmax accumulator */
+} lrar_variant;
+
+/* The depth-mix read (LR-AttnRes paper §3.1/§3.3; explainer, "A short description...").
+ *   T, d, r, eps : tokens, width, key width (1 <= r <= d), RMS epsilon (>= 0, finite;
+ *                  eps = 0 is allowed and yields NaN for an all-zero key slice).
+ *   io           : element type of the sources and of out.
+ *   n, src, src_ld : 1 <= n <= LRAR_MAX_SOURCES sources; src[i] is a device [T, src_ld[i]]
+ *                  matrix of which the first d columns are used.
+ *   q            : device float32 [r], the site query.
+ *   out, out_ld  : device [T, out_ld] of type io; receives h. Must not be one of src.
+ *   alpha, alpha_ld : optional device float32 [T, alpha_ld >= n]; receives the weights.
+ *   variant      : lrar_variant. LRAR_ERR_UNSUPPORTED if ONLINE is asked for a d it does
+ *                  not cover (d > 8192 bf16 / 4096 f32 on the vector path).
+ * With n = 1 the output equals src[0] exactly (the embedding-only read is the identity). */
+lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                         int32_t n, const void* const* src, const int64_t* src_ld,
+                         const float* q, void* out, int64_t out_ld, float* alpha,
+                         int64_t alpha_ld, int32_t variant, void* stream);
+
+/* Phase 1 of the two-phase schedule (AttnRes technical-report summary, "Method"; LR-AttnRes
+ * paper §3.4): nq site queries against the same n cached sources. For query s, token t:
+ *     m[s][t]   = max_i z_si  rounded to float32,
+ *     l[s][t]   = sum_i exp(z_si - m[s][t]),
+ *     acc[s][t] = sum_i exp(z_si - m[s][t]) o_i     (d values, NOT normalised).
+ *   q, q_ld       : device float32 [nq, q_ld >= r]; 1 <= nq <= LRAR_MAX_QUERIES.
+ *   m, l, ml_ld   : device float32, element (s, t) at s * ml_ld + t, ml_ld >= T.
+ *   acc           : element (s, t, j) at s * acc_qstride + t * acc_ld + j, in acc_dtype
+ *                   (LRAR_F32 is exact enough for parity; LRAR_BF16 halves the bytes).
+ *                   acc_ld >= d, acc_qstride >= T * acc_ld. Must not overlap the sources. */
+lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                               int32_t n, const void* const* src, const int64_t* src_ld,
+                               int32_t nq, const float* q, int64_t q_ld, float* m, float* l,
+                               int64_t ml_ld, void* acc, lrar_dtype acc_dtype, int64_t acc_ld,
+                               int64_t acc_qstride, void* stream);
+
+/* Phase 2: merge one site's Phase-1 statistics with n >= 0 further sources (normally the
+ * site's intra-block partial sum) by the online-softmax update, and normalise:
+ *     m' = max(m, max_b z_b),  l' = l e^{m-m'} + sum_b e^{z_b-m'},
+ *     h  = (acc e^{m-m'} + sum_b e^{z_b-m'} o_b) / l'.
+ *   m, l          : device float32 [T]; acc: device [T, acc_ld] of acc_dtype.
+ *   n, src, src_ld, q : the extra sources and the site query (q may be NULL when n = 0).
+ *   out, out_ld   : device [T, out_ld] of type io.
+ *   m_out, l_out  : optional device float32 [T]; receive m' (rounded to float32) and l'
+ *                   relative to that rounded m'. */
+lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                       const float* m, const float* l, const void* acc, lrar_dtype acc_dtype,
+                       int64_t acc_ld, int32_t n, const void* const* src,
+                       const int64_t* src_ld, const float* q, void* out, int64_t out_ld,
+                       float* m_out, float* l_out, void* stream);
+
+/* Backward of one read (LR-AttnRes paper App. B.3: Lemma 2 and Corollary 2.1), each source
+ * slot treated as an independent input. With g = dout[t]:
+ *     dz_i    = alpha_i <g, o_i - h>
+ *     dsrc_i  = alpha_i g  +  on the last r coordinates: dz_i (q - z_i kbar_i / r) / rho_i
+ *     dq      = sum_t sum_i dz_i kbar_i,       kbar_i = k_i / rho_i.
+ *   dout, dout_ld : device float32 [T, dout_ld].
+ *   dsrc, dsrc_ld : host array of n distinct device float32 [T, dsrc_ld[i]] pointers.
+ *   accumulate    : 0 overwrites dsrc; 1 adds into it (a source's total gradient sums over
+ *                   every read it takes part in).
+ *   dq            : device float32 [r]; overwritten. The token sum is evaluated in a fixed
+ *                   order, so results are bitwise reproducible.
+ *   workspace     : device scratch of at least lrar_backward_workspace_size(T, d, r, n)
+ *                   bytes, 8-byte aligned; its contents are not needed after the call.
+ * Supported on the vector path for d <= 8192 (bf16) / 4096 (f32), on the scalar path for
+ * d <= 2048; LRAR_ERR_UNSUPPORTED otherwise. */
+lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                          int32_t n, const void* const* src, const int64_t* src_ld,
+                          const float* q, const float* dout, int64_t dout_ld,
+                          float* const* dsrc, const int64_t* dsrc_ld, int32_t accumulate,
+                          float* dq, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace lrar_backward needs for this shape (0 if T = 0). */
+size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n);
+
+/* A plain streaming device-to-device copy of `bytes` bytes (both pointers 16-byte aligned,
+ * bytes a multiple of 16). Not part of the read: it is the reference kernel used to
+ * calibrate hardware traffic counters and to measure the achievable copy bandwidth. */
+lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Static description of a status code. */
+const char* lrar_status_string(lrar_status status);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* lrar_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* lrar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRATTNRES_H_ */

@@ -1,0 +1,117 @@
+"""Tolerances for comparing the HIP path with the oracle.
+
+The bars (element by element):
+  * weights alpha: |alpha - alpha_ref| <= 1e-6;
+  * fp32 output: |y - h_ref| <= 1e-5 * max|v| with v the source values of the read;
+  * bf16 output: |y - h_ref| <= ulp_bf16(h_ref) + (n + 3) * 2^-24 * sum_i alpha_i |o_ij|.
+    The first term is one bf16 ulp of the value; the second is the float32 accumulation
+    slack of a sum of n products (it only matters under cancellation).
+  * Phase-1 statistics: m within one float32 rounding; l and acc within the float32
+    accumulation bound after rescaling the oracle to the kernel's m.
+  * backward: dsrc_i within 1e-5 * max|dsrc_i ref| per source; dq within
+    1e-5 * sum_t sum_i |dz_ti| * max_j |kbar_tij|.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+U = 2.0 ** -24
+
+
+def ulp_bf16(x):
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    tiny = 2.0 ** -126
+    e = np.floor(np.log2(np.maximum(ax, tiny)))
+    return np.where(ax < tiny, 2.0 ** -133, 2.0 ** (e - 7))
+
+
+def _report(err, tol, where):
+    bad = ~(err <= tol)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err / np.maximum(tol, 1e-300), 0)),
+                               err.shape)
+        raise AssertionError(f"{where}: {int(bad.sum())} of {err.size} elements out of "
+                             f"tolerance; worst at {idx}: err {err[idx]:.3e} > tol {tol[idx]:.3e}")
+
+
+def _nan_equal_mask(a, b):
+    return np.isnan(a) & np.isnan(b)
+
+
+def assert_read(y64, h_ref, alpha_ref, srcs64, io, where="read"):
+    """y64: kernel output decoded to float64 [T, d]; h_ref, alpha_ref from the oracle."""
+    n = len(srcs64)
+    if io == "bf16":
+        mag = np.zeros_like(h_ref)
+        for i in range(n):
+            mag += alpha_ref[:, i:i + 1] * np.abs(srcs64[i])
+        tol = ulp_bf16(h_ref) + (n + 3) * U * mag
+    else:
+        vmax = max(float(np.nanmax(np.abs(s))) for s in srcs64)
+        tol = np.full_like(h_ref, 1e-5 * vmax)
+    err = np.abs(y64 - h_ref)
+    err[_nan_equal_mask(y64, h_ref)] = 0.0
+    _report(err, tol, where)
+
+
+def assert_weights(a64, a_ref, where="weights"):
+    err = np.abs(a64 - a_ref)
+    err[_nan_equal_mask(a64, a_ref)] = 0.0
+    _report(err, np.full_like(err, 1e-6), where)
+
+
+def assert_stats(m_g, l_g, acc_g, m_o, l_o, acc_o, z_o, srcs64, acc_io, where="stats"):
+    """Kernel statistics against the oracle's, rescaled to the kernel's rounded maximum.
+    m_*, l_* are [T]; acc_* are [T, d]; z_o [T, n] are the oracle's scores."""
+    n = len(srcs64)
+    _report(np.abs(m_g - m_o), 2.0 ** -23 * np.abs(m_o) + 1e-12, where + " m")
+    s = np.exp(m_o - m_g)
+    l_ref = l_o * s
+    _report(np.abs(l_g - l_ref), 4 * U * l_ref, where + " l")
+    acc_ref = acc_o * s[:, None]
+    e = np.exp(z_o - m_g[:, None])
+    mag = np.zeros_like(acc_ref)
+    for i in range(n):
+        mag += e[:, i:i + 1] * np.abs(srcs64[i])
+    tol = (n + 3) * U * mag
+    if acc_io == "bf16":
+        tol = tol + ulp_bf16(acc_ref)
+    _report(np.abs(acc_g - acc_ref), tol, where + " acc")
+
+
+def assert_merge(y64, h_ref, w_prior, acc_norm, w_extra, extra64, io, where="merge"):
+    """h = w_prior * (acc / l) + sum_b w_b o_b; w_* from the oracle (w_prior [T], w_extra
+    [T, n_extra]); acc_norm = acc / l [T, d]."""
+    mag = w_prior[:, None] * np.abs(acc_norm)
+    for i, b in enumerate(extra64):
+        mag += w_extra[:, i:i + 1] * np.abs(b)
+    n = len(extra64) + 1
+    if io == "bf16":
+        tol = ulp_bf16(h_ref) + (n + 4) * U * mag
+    else:
+        vmax = max([float(np.abs(acc_norm).max())] + [float(np.abs(b).max()) for b in extra64])
+        tol = np.full_like(h_ref, 1e-5 * vmax) + (n + 4) * U * mag
+    err = np.abs(y64 - h_ref)
+    err[_nan_equal_mask(y64, h_ref)] = 0.0
+    _report(err, tol, where)
+
+
+def assert_dsrc(g64, g_ref, where="dsrc"):
+    tol = np.full_like(g_ref, 1e-5 * max(float(np.abs(g_ref).max()), 1e-30))
+    _report(np.abs(g64 - g_ref), tol, where)
+
+
+def dq_bound(srcs64, q, dout64, alpha, h, r, eps):
+    """sum_t sum_i |dz_ti| * max_j |kbar_tij| from oracle outputs alpha, h (for the dq tol)."""
+    d = srcs64[0].shape[1]
+    total = 0.0
+    for i, o in enumerate(srcs64):
+        dz = alpha[:, i] * np.sum(dout64 * (o - h), axis=1)
+        k = o[:, d - r:]
+        rho = np.sqrt(np.mean(k * k, axis=1) + eps)
+        total += float(np.sum(np.abs(dz) * np.max(np.abs(k), axis=1) / rho))
+    return total
+
+
+def assert_dq(dq_g, dq_o, bound, where="dq"):
+    _report(np.abs(dq_g - dq_o), np.full_like(dq_o, 1e-5 * bound + 1e-30), where)

@@ -1,0 +1,154 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects bad
+arguments with a status before touching the device (CPU only; no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_depth_wise_lrar_amd as lrar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrattnres.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrar_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return lrar.lib()
+    except lrar.LibraryNotBuilt as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(lrar.exported_symbols()) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.lrar_version().decode().count(".") == 2
+    for s in range(4):
+        assert L.lrar_status_string(s)
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned host value; never dereferenced
+
+
+def _src(n, ld):
+    k = max(n, 1)
+    return (ctypes.c_void_p * k)(*([FAKE] * k)), (ctypes.c_int64 * k)(*([ld] * k))
+
+
+def fwd(L, T=4, d=8, r=4, eps=1e-6, io=1, n=2, ld=8, q=FAKE, out=FAKE * 2, out_ld=8,
+        alpha=None, alpha_ld=0, variant=0):
+    p, l = _src(n, ld)
+    return L.lrar_forward(T, d, r, eps, io, n, p, l, q, out, out_ld, alpha, alpha_ld, variant,
+                          None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(d=0), dict(r=0), dict(r=9), dict(eps=-1.0), dict(eps=float("nan")),
+    dict(eps=float("inf")), dict(io=7), dict(n=0), dict(n=65), dict(ld=7), dict(q=None),
+    dict(out=None), dict(out_ld=7), dict(alpha=FAKE * 3, alpha_ld=1), dict(variant=3),
+    dict(out=FAKE),  # out aliases a source
+])
+def test_forward_rejects(L, kw):
+    assert fwd(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_last_error().decode().startswith("lrar_forward")
+
+
+def test_forward_empty_is_ok_without_device(L):
+    assert fwd(L, T=0) == lrar.LRAR_OK
+
+
+def test_online_too_wide_is_unsupported(L):
+    assert fwd(L, d=8192 * 2, r=16, ld=8192 * 2, out_ld=8192 * 2, variant=2) == \
+        lrar.LRAR_ERR_UNSUPPORTED
+
+
+def stats(L, T=4, d=8, r=4, n=2, nq=3, q_ld=4, ml_ld=4, acc_ld=8, qstride=32, acc_dtype=0,
+          m=FAKE * 3, l=FAKE * 4, acc=FAKE * 5):
+    p, ld = _src(n, 8)
+    return L.lrar_forward_stats(T, d, r, 1e-6, 1, n, p, ld, nq, FAKE * 2, q_ld, m, l, ml_ld, acc,
+                                acc_dtype, acc_ld, qstride, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(nq=0), dict(nq=65), dict(q_ld=3), dict(ml_ld=3), dict(acc_ld=7), dict(qstride=31),
+    dict(acc_dtype=5), dict(m=None), dict(m=FAKE * 4), dict(acc=FAKE),
+])
+def test_stats_rejects(L, kw):
+    assert stats(L, **kw) == lrar.LRAR_ERR_INVALID
+
+
+def merge(L, T=4, d=8, r=4, n=1, acc_ld=8, out=FAKE * 6, q=FAKE * 2, m_out=None, l_out=None):
+    p, ld = _src(n, 8)
+    return L.lrar_merge(T, d, r, 1e-6, 1, FAKE * 3, FAKE * 4, FAKE * 5, 0, acc_ld, n, p, ld, q,
+                        out, 8, m_out, l_out, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n=-1), dict(acc_ld=7), dict(q=None), dict(out=None), dict(out=FAKE),
+    dict(m_out=FAKE * 7, l_out=FAKE * 7),
+])
+def test_merge_rejects(L, kw):
+    assert merge(L, **kw) == lrar.LRAR_ERR_INVALID
+
+
+def test_merge_without_extra_sources_needs_no_query(L):
+    assert merge(L, T=0, n=0, q=None) == lrar.LRAR_OK
+
+
+def bwd(L, T=4, d=8, r=4, n=2, dsrc=None, accumulate=0, ws=FAKE * 9, ws_bytes=1 << 30,
+        dq=FAKE * 8, dout=FAKE * 7):
+    p, ld = _src(n, 8)
+    dsrc = dsrc if dsrc is not None else [FAKE * (10 + i) for i in range(n)]
+    dp = (ctypes.c_void_p * n)(*dsrc)
+    dl = (ctypes.c_int64 * n)(*([8] * n))
+    return L.lrar_backward(T, d, r, 1e-6, 1, n, p, ld, FAKE * 2, dout, 8, dp, dl, accumulate, dq,
+                           ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dsrc=[FAKE * 10, FAKE * 10]), dict(dsrc=[FAKE, FAKE * 11]), dict(accumulate=2),
+    dict(ws_bytes=8), dict(ws=None), dict(dq=None), dict(dout=FAKE * 10),
+])
+def test_backward_rejects(L, kw):
+    assert bwd(L, **kw) == lrar.LRAR_ERR_INVALID
+
+
+def test_backward_workspace_size(L):
+    assert L.lrar_backward_workspace_size(0, 8, 4, 2) == 0
+    a = L.lrar_backward_workspace_size(16384, 4096, 1024, 10)
+    assert a > 0 and a % 8 == 0
+    assert L.lrar_backward_workspace_size(16384, 4096, 2048, 10) > a
+
+
+def test_backward_too_wide_is_unsupported(L):
+    p, ld = _src(1, 20000)
+    dp = (ctypes.c_void_p * 1)(FAKE * 10)
+    dl = (ctypes.c_int64 * 1)(20000)
+    assert L.lrar_backward(4, 20000, 8, 1e-6, 1, 1, p, ld, FAKE * 2, FAKE * 3, 20000, dp, dl, 0,
+                           FAKE * 4, FAKE * 5, 1 << 30, None) == lrar.LRAR_ERR_UNSUPPORTED
+
+
+def test_copy_rejects(L):
+    assert L.lrar_copy(FAKE, FAKE + 8, 64, None) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_copy(FAKE, FAKE + 16, 64, None) == lrar.LRAR_ERR_INVALID  # overlap
+    assert L.lrar_copy(FAKE, FAKE * 2, 0, None) == lrar.LRAR_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lrar, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(lrar, "_lib", None)
+    with pytest.raises(lrar.LibraryNotBuilt):
+        lrar.lib()

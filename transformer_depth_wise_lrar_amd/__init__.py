@@ -1,0 +1,274 @@
+"""Python binding of liblrattnres, the LR-AttnRes depth-mix read for MI355X (gfx950).
+
+The functions here have the names of the C entry points in include/lrattnres.h and only
+marshal arguments: they take torch tensors on the GPU, pass raw device pointers, strides
+and the current HIP stream to the library, and allocate outputs with torch when the
+caller does not pass them. Every step of the read runs in the library's HIP kernels.
+
+There is no fallback: if liblrattnres.so is missing or cannot be loaded, every call raises
+LibraryNotBuilt. Build it with ``python -m transformer_depth_wise_lrar_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblrattnres.so")
+
+LRAR_OK, LRAR_ERR_INVALID, LRAR_ERR_UNSUPPORTED, LRAR_ERR_DEVICE = 0, 1, 2, 3
+LRAR_F32, LRAR_BF16 = 0, 1
+VARIANTS = {"auto": 0, "two_pass": 1, "online": 2}
+MAX_SOURCES = 64
+MAX_QUERIES = 64
+
+
+class LibraryNotBuilt(RuntimeError):
+    """liblrattnres.so is not built or cannot be loaded."""
+
+
+class LrarError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+_i64, _i32, _f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+_vp = ctypes.c_void_p
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def lib():
+    """The loaded library (raises LibraryNotBuilt if it is absent)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise LibraryNotBuilt(
+                    f"{LIB_PATH} is missing; build it with "
+                    "`python -m transformer_depth_wise_lrar_amd.build`")
+            try:
+                L = ctypes.CDLL(LIB_PATH)
+            except OSError as e:
+                raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
+            L.lrar_forward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
+                                       _vp, _i64, _vp, _i64, _i32, _vp]
+            L.lrar_forward_stats.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
+                                             _i32, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64,
+                                             _i64, _vp]
+            L.lrar_merge.argtypes = [_i64, _i32, _i32, _f64, _i32, _vp, _vp, _vp, _i32, _i64,
+                                     _i32, _vpp, _i64p, _vp, _vp, _i64, _vp, _vp, _vp]
+            L.lrar_backward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
+                                        _vp, _i64, _vpp, _i64p, _i32, _vp, _vp, ctypes.c_size_t,
+                                        _vp]
+            L.lrar_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
+            L.lrar_backward_workspace_size.restype = ctypes.c_size_t
+            L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+            for fn in ("lrar_forward", "lrar_forward_stats", "lrar_merge", "lrar_backward",
+                       "lrar_copy"):
+                getattr(L, fn).restype = ctypes.c_int
+            L.lrar_status_string.argtypes = [ctypes.c_int]
+            L.lrar_status_string.restype = ctypes.c_char_p
+            L.lrar_last_error.restype = ctypes.c_char_p
+            L.lrar_version.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def exported_symbols() -> list[str]:
+    """The C entry points this binding expects the library to export."""
+    return ["lrar_forward", "lrar_forward_stats", "lrar_merge", "lrar_backward",
+            "lrar_backward_workspace_size", "lrar_copy", "lrar_status_string",
+            "lrar_last_error", "lrar_version"]
+
+
+def _check(status: int):
+    if status != LRAR_OK:
+        L = lib()
+        raise LrarError(status, f"{L.lrar_status_string(status).decode()}: "
+                                f"{L.lrar_last_error().decode()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LRAR_BF16
+    if t.dtype == torch.float32:
+        return LRAR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr(), t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _src_table(srcs: Sequence, io: int | None):
+    n = len(srcs)
+    if n > MAX_SOURCES:
+        raise ValueError(f"at most {MAX_SOURCES} sources")
+    ptrs = (ctypes.c_void_p * max(n, 1))()
+    lds = (ctypes.c_int64 * max(n, 1))()
+    T = d = None
+    for i, s in enumerate(srcs):
+        if io is not None and _dtype_code(s) != io:
+            raise TypeError("all sources must share one dtype")
+        io = _dtype_code(s)
+        p, ld = _rows(s, f"src[{i}]")
+        ptrs[i], lds[i] = p, ld
+        if T is None:
+            T, d = s.shape
+        elif tuple(s.shape) != (T, d):
+            raise ValueError("all sources must share one shape")
+    return ptrs, lds, io, T, d
+
+
+def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=None,
+                 variant: str = "auto", stream=None):
+    """h = sum_i softmax_i(q . RMSNorm(tail_r(o_i))) o_i for every row.
+
+    srcs: n tensors [T, d] (bf16 or fp32, unit column stride); q: fp32 [r].
+    out: optional [T, d] of the sources' dtype. alpha: True to return the weights, or an
+    fp32 [T, >=n] tensor to write them into. Returns (out, alpha or None)."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    if out is None:
+        out = torch.empty((T, d), dtype=srcs[0].dtype, device=srcs[0].device)
+    op, old = _rows(out, "out")
+    if alpha is True:
+        alpha = torch.empty((T, len(srcs)), dtype=torch.float32, device=srcs[0].device)
+    ap, ald = (_rows(alpha, "alpha") if alpha is not None and alpha is not False else (None, 0))
+    if alpha is False:
+        alpha = None
+    _check(lib().lrar_forward(T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op,
+                              old, ap, ald, VARIANTS[variant], _stream(stream)))
+    return out, alpha
+
+
+def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=None,
+                       m=None, l=None, acc=None, stream=None):
+    """Phase-1 statistics of queries qs [nq, r] against the sources.
+
+    Returns (m [nq, T], l [nq, T], acc [nq, T, d]); acc is unnormalised, fp32 by default."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    if qs.dim() == 1:
+        qs = qs.view(1, -1)
+    nq = qs.shape[0]
+    dev = srcs[0].device
+    acc_dtype = torch.float32 if acc_dtype is None else acc_dtype
+    if m is None:
+        m = torch.empty((nq, T), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((nq, T), dtype=torch.float32, device=dev)
+    if acc is None:
+        acc = torch.empty((nq, T, d), dtype=acc_dtype, device=dev)
+    if acc.stride(2) != 1 or m.stride(1) != 1 or l.stride(1) != 1 or m.stride(0) != l.stride(0):
+        raise ValueError("m, l, acc need unit inner stride and m, l one row stride")
+    _check(lib().lrar_forward_stats(T, d, r, float(eps), io, len(srcs), ptrs, lds, nq,
+                                    qs.data_ptr(), qs.stride(0), m.data_ptr(), l.data_ptr(),
+                                    m.stride(0), acc.data_ptr(), _dtype_code(acc),
+                                    acc.stride(1), acc.stride(0), _stream(stream)))
+    return m, l, acc
+
+
+def lrar_merge(m, l, acc, srcs: Sequence, q, r: int, eps: float = 1e-6, out=None,
+               stats_out: bool = False, io_dtype=None, stream=None):
+    """Phase-2 merge of one site's statistics (m [T], l [T], acc [T, d]) with extra sources.
+
+    Returns out, or (out, m', l') with stats_out=True."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    if io is None:
+        if out is None and io_dtype is None:
+            raise ValueError("with no extra sources pass out= or io_dtype=")
+        io = _dtype_code(out) if out is not None else (
+            LRAR_BF16 if io_dtype == torch.bfloat16 else LRAR_F32)
+    T, d = acc.shape
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16 if io == LRAR_BF16 else torch.float32,
+                          device=acc.device)
+    op, old = _rows(out, "out")
+    accp, accld = _rows(acc, "acc")
+    m_out = l_out = None
+    if stats_out:
+        m_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
+        l_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
+    _check(lib().lrar_merge(T, d, r, float(eps), io, m.data_ptr(), l.data_ptr(), accp,
+                            _dtype_code(acc), accld, len(srcs), ptrs, lds,
+                            q.data_ptr() if q is not None else None, op, old,
+                            m_out.data_ptr() if m_out is not None else None,
+                            l_out.data_ptr() if l_out is not None else None, _stream(stream)))
+    return (out, m_out, l_out) if stats_out else out
+
+
+def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
+    """Bytes of device workspace lrar_backward needs."""
+    return int(lib().lrar_backward_workspace_size(T, d, r, n))
+
+
+def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
+                  accumulate: bool = False, dq=None, workspace=None, stream=None):
+    """Source and query gradients of one read for upstream gradient dout (fp32 [T, d]).
+
+    Returns (dsrc list of fp32 [T, d], dq fp32 [r])."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    n = len(srcs)
+    dev = srcs[0].device
+    if dsrc is None:
+        dsrc = [torch.zeros((T, d), dtype=torch.float32, device=dev) if accumulate
+                else torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(n)]
+    dptrs = (ctypes.c_void_p * max(n, 1))()
+    dlds = (ctypes.c_int64 * max(n, 1))()
+    for i, g in enumerate(dsrc):
+        dptrs[i], dlds[i] = _rows(g, f"dsrc[{i}]")
+    if dq is None:
+        dq = torch.empty((r,), dtype=torch.float32, device=dev)
+    need = lrar_backward_workspace_size(T, d, r, n)
+    if workspace is None:
+        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
+    gp, gld = _rows(dout, "dout")
+    _check(lib().lrar_backward(T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr(), gp, gld,
+                               dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream)))
+    return dsrc, dq
+
+
+def lrar_copy(dst, src, stream=None):
+    """Plain streaming copy of src into dst (same byte size, 16-byte multiples)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src must have the same byte size")
+    _check(lib().lrar_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
+    return dst
+
+
+def version() -> str:
+    return lib().lrar_version().decode()

@@ -1,0 +1,363 @@
+// The C-ABI entry points of liblrattnres: argument validation, path selection and launch.
+// Every check runs before any device work; nothing here allocates, frees or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lrattnres.h"
+#include "lrar_device.h"
+#include "lrar_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lrar_status fail(lrar_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lrar_status fail(lrar_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lrar_status device_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return LRAR_OK;
+  return fail(LRAR_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(lrar_dtype t) { return t == LRAR_BF16 ? 2 : 4; }
+
+// Elements per 16-byte unit, or 0 for an unknown type.
+int vec_of(lrar_dtype t) { return t == LRAR_BF16 ? 8 : (t == LRAR_F32 ? 4 : 0); }
+
+bool dtype_ok(lrar_dtype t) { return t == LRAR_BF16 || t == LRAR_F32; }
+
+lrar_status check_shape(const char* fn, int64_t T, int32_t d, int32_t r, double eps,
+                        lrar_dtype io) {
+  if (T < 0) return fail(LRAR_ERR_INVALID, "%s: T = %lld < 0", fn, (long long)T);
+  if (d < 1) return fail(LRAR_ERR_INVALID, "%s: d = %d < 1", fn, d);
+  if (r < 1 || r > d) return fail(LRAR_ERR_INVALID, "%s: r = %d outside [1, d = %d]", fn, r, d);
+  if (!(eps >= 0.0) || !std::isfinite(eps))
+    return fail(LRAR_ERR_INVALID, "%s: eps = %g must be finite and >= 0", fn, eps);
+  if (!dtype_ok(io)) return fail(LRAR_ERR_INVALID, "%s: unknown io dtype %d", fn, (int)io);
+  return LRAR_OK;
+}
+
+// Fills the source table; also reports whether every row start is 16-byte aligned.
+lrar_status check_sources(const char* fn, int64_t T, int32_t d, lrar_dtype io, int32_t n,
+                          int32_t n_min, const void* const* src, const int64_t* src_ld,
+                          lrar::SrcList& S, bool& vec_ok) {
+  if (n < n_min || n > LRAR_MAX_SOURCES)
+    return fail(LRAR_ERR_INVALID, "%s: n = %d outside [%d, %d]", fn, n, n_min, LRAR_MAX_SOURCES);
+  std::memset(&S, 0, sizeof(S));
+  if (n == 0) return LRAR_OK;
+  if (src == nullptr || src_ld == nullptr)
+    return fail(LRAR_ERR_INVALID, "%s: null source table", fn);
+  const int vec = vec_of(io);
+  for (int i = 0; i < n; ++i) {
+    if (src[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: src[%d] is null", fn, i);
+    if (src_ld[i] < d)
+      return fail(LRAR_ERR_INVALID, "%s: src_ld[%d] = %lld < d = %d", fn, i, (long long)src_ld[i], d);
+    S.ptr[i] = src[i];
+    S.ld[i] = src_ld[i];
+    if (!aligned16(src[i]) || (src_ld[i] % vec) != 0) vec_ok = false;
+  }
+  if (d % vec != 0) vec_ok = false;
+  return LRAR_OK;
+}
+
+bool overlaps_source(const void* p, const lrar::SrcList& S, int n) {
+  for (int i = 0; i < n; ++i)
+    if (S.ptr[i] == p) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
+                         const void* const* src, const int64_t* src_ld, const float* q, void* out,
+                         int64_t out_ld, float* alpha, int64_t alpha_ld, int32_t variant,
+                         void* stream) {
+  const char* fn = "lrar_forward";
+  lrar_status st = check_shape(fn, T, d, r, eps, io);
+  if (st != LRAR_OK) return st;
+  lrar::ReadParams p;
+  std::memset(&p, 0, sizeof(p));
+  bool vec_ok = true;
+  st = check_sources(fn, T, d, io, n, 1, src, src_ld, p.src, vec_ok);
+  if (st != LRAR_OK) return st;
+  if (q == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: q is null", fn);
+  if (out == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: out is null", fn);
+  if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
+  if (out != nullptr && overlaps_source(out, p.src, n))
+    return fail(LRAR_ERR_INVALID, "%s: out aliases a source", fn);
+  if (alpha != nullptr && alpha_ld < n)
+    return fail(LRAR_ERR_INVALID, "%s: alpha_ld = %lld < n = %d", fn, (long long)alpha_ld, n);
+  if (variant < LRAR_VARIANT_AUTO || variant > LRAR_VARIANT_ONLINE)
+    return fail(LRAR_ERR_INVALID, "%s: unknown variant %d", fn, variant);
+  const int vec = vec_of(io);
+  if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
+  const int use_vec = vec_ok ? vec : 1;
+  const int nur = (d + use_vec - 1) / use_vec;
+  const bool online_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::online_max_units();
+  lrar::ReadKind kind;
+  if (variant == LRAR_VARIANT_ONLINE) {
+    if (!online_fits)
+      return fail(LRAR_ERR_UNSUPPORTED, "%s: the online variant holds a whole row in registers; "
+                  "d = %d is too wide on this path", fn, d);
+    kind = lrar::ReadKind::kOnline;
+  } else if (variant == LRAR_VARIANT_TWO_PASS) {
+    kind = lrar::ReadKind::kTwoPass;
+  } else {
+    // A key wider than half the row is cheaper to read once (online); a narrow key is
+    // cheaper to score first and stream the values once (two-pass).
+    kind = (online_fits && 2 * r > d) ? lrar::ReadKind::kOnline : lrar::ReadKind::kTwoPass;
+  }
+  if (T == 0) return LRAR_OK;
+  p.n = n;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.q = q;
+  p.out = out;
+  p.out_ld = out_ld;
+  p.alpha = alpha;
+  p.alpha_ld = alpha_ld;
+  return device_status(lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0,
+                                         static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                               int32_t n, const void* const* src, const int64_t* src_ld,
+                               int32_t nq, const float* q, int64_t q_ld, float* m, float* l,
+                               int64_t ml_ld, void* acc, lrar_dtype acc_dtype, int64_t acc_ld,
+                               int64_t acc_qstride, void* stream) {
+  const char* fn = "lrar_forward_stats";
+  lrar_status st = check_shape(fn, T, d, r, eps, io);
+  if (st != LRAR_OK) return st;
+  lrar::StatsParams p;
+  std::memset(&p, 0, sizeof(p));
+  bool vec_ok = true;
+  st = check_sources(fn, T, d, io, n, 1, src, src_ld, p.src, vec_ok);
+  if (st != LRAR_OK) return st;
+  if (nq < 1 || nq > LRAR_MAX_QUERIES)
+    return fail(LRAR_ERR_INVALID, "%s: nq = %d outside [1, %d]", fn, nq, LRAR_MAX_QUERIES);
+  if (q_ld < r) return fail(LRAR_ERR_INVALID, "%s: q_ld = %lld < r", fn, (long long)q_ld);
+  if (ml_ld < T) return fail(LRAR_ERR_INVALID, "%s: ml_ld = %lld < T", fn, (long long)ml_ld);
+  if (!dtype_ok(acc_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown acc dtype", fn);
+  if (acc_ld < d) return fail(LRAR_ERR_INVALID, "%s: acc_ld = %lld < d", fn, (long long)acc_ld);
+  if (nq > 1 && acc_qstride < T * acc_ld)
+    return fail(LRAR_ERR_INVALID, "%s: acc_qstride = %lld < T * acc_ld", fn, (long long)acc_qstride);
+  if (T > 0 && (q == nullptr || m == nullptr || l == nullptr || acc == nullptr))
+    return fail(LRAR_ERR_INVALID, "%s: null q, m, l or acc", fn);
+  if (m == l && m != nullptr) return fail(LRAR_ERR_INVALID, "%s: m and l alias", fn);
+  if (acc != nullptr && overlaps_source(acc, p.src, n))
+    return fail(LRAR_ERR_INVALID, "%s: acc aliases a source", fn);
+  const int vec = vec_of(io);
+  // acc units are VEC elements of acc_dtype; rows must start 16-byte aligned when acc is fp32
+  // and units are 8 wide (two 16-byte halves), or whenever acc is written 16 bytes at a time.
+  const int acc_elems_per_16 = acc_dtype == LRAR_BF16 ? 8 : 4;
+  const bool acc_vec_needed = (esize(acc_dtype) * vec) % 16 == 0;
+  if (acc_vec_needed &&
+      (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0 || acc_qstride % acc_elems_per_16 != 0))
+    vec_ok = false;
+  if (T == 0) return LRAR_OK;
+  p.n = n;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.nq = nq;
+  p.q = q;
+  p.q_ld = q_ld;
+  p.m = m;
+  p.l = l;
+  p.ml_ld = ml_ld;
+  p.acc = acc;
+  p.acc_ld = acc_ld;
+  p.acc_qstride = acc_qstride;
+  return device_status(lrar::launch_stats(p, io == LRAR_BF16, vec_ok ? vec : 1,
+                                          acc_dtype == LRAR_BF16,
+                                          static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                       const float* m, const float* l, const void* acc, lrar_dtype acc_dtype,
+                       int64_t acc_ld, int32_t n, const void* const* src, const int64_t* src_ld,
+                       const float* q, void* out, int64_t out_ld, float* m_out, float* l_out,
+                       void* stream) {
+  const char* fn = "lrar_merge";
+  lrar_status st = check_shape(fn, T, d, r, eps, io);
+  if (st != LRAR_OK) return st;
+  lrar::ReadParams p;
+  std::memset(&p, 0, sizeof(p));
+  bool vec_ok = true;
+  st = check_sources(fn, T, d, io, n, 0, src, src_ld, p.src, vec_ok);
+  if (st != LRAR_OK) return st;
+  if (!dtype_ok(acc_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown acc dtype", fn);
+  if (acc_ld < d) return fail(LRAR_ERR_INVALID, "%s: acc_ld = %lld < d", fn, (long long)acc_ld);
+  if (T > 0 && (m == nullptr || l == nullptr || acc == nullptr || out == nullptr))
+    return fail(LRAR_ERR_INVALID, "%s: null m, l, acc or out", fn);
+  if (T > 0 && n > 0 && q == nullptr) return fail(LRAR_ERR_INVALID, "%s: q is null", fn);
+  if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
+  if (out != nullptr && overlaps_source(out, p.src, n))
+    return fail(LRAR_ERR_INVALID, "%s: out aliases a source", fn);
+  if (m_out != nullptr && m_out == l_out) return fail(LRAR_ERR_INVALID, "%s: m_out and l_out alias", fn);
+  const int vec = vec_of(io);
+  if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
+  const int acc_elems_per_16 = acc_dtype == LRAR_BF16 ? 8 : 4;
+  if ((esize(acc_dtype) * vec) % 16 == 0 && (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0))
+    vec_ok = false;
+  if (T == 0) return LRAR_OK;
+  p.n = n;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.q = q;
+  p.out = out;
+  p.out_ld = out_ld;
+  p.m_in = m;
+  p.l_in = l;
+  p.acc = acc;
+  p.acc_ld = acc_ld;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  return device_status(lrar::launch_read(p, lrar::ReadKind::kMerge, io == LRAR_BF16,
+                                         vec_ok ? vec : 1, acc_dtype == LRAR_BF16,
+                                         static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n) {
+  (void)d;
+  (void)n;
+  if (T <= 0 || r < 1) return 0;
+  return lrar::backward_workspace(T, r);
+}
+
+lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
+                          const void* const* src, const int64_t* src_ld, const float* q,
+                          const float* dout, int64_t dout_ld, float* const* dsrc,
+                          const int64_t* dsrc_ld, int32_t accumulate, float* dq, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const char* fn = "lrar_backward";
+  lrar_status st = check_shape(fn, T, d, r, eps, io);
+  if (st != LRAR_OK) return st;
+  lrar::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  bool vec_ok = true;
+  st = check_sources(fn, T, d, io, n, 1, src, src_ld, p.src, vec_ok);
+  if (st != LRAR_OK) return st;
+  if (accumulate != 0 && accumulate != 1)
+    return fail(LRAR_ERR_INVALID, "%s: accumulate must be 0 or 1", fn);
+  if (dout_ld < d) return fail(LRAR_ERR_INVALID, "%s: dout_ld = %lld < d", fn, (long long)dout_ld);
+  if (dsrc == nullptr || dsrc_ld == nullptr) return fail(LRAR_ERR_INVALID, "%s: null dsrc table", fn);
+  if (T > 0 && (q == nullptr || dout == nullptr || dq == nullptr))
+    return fail(LRAR_ERR_INVALID, "%s: null q, dout or dq", fn);
+  const int vec = vec_of(io);
+  if (!aligned16(dout) || dout_ld % 4 != 0) vec_ok = false;
+  for (int i = 0; i < n; ++i) {
+    if (dsrc[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] is null", fn, i);
+    if (dsrc_ld[i] < d)
+      return fail(LRAR_ERR_INVALID, "%s: dsrc_ld[%d] = %lld < d", fn, i, (long long)dsrc_ld[i]);
+    for (int j = 0; j < i; ++j)
+      if (dsrc[j] == dsrc[i]) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] and dsrc[%d] alias", fn, j, i);
+    if (overlaps_source(dsrc[i], p.src, n))
+      return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases a source", fn, i);
+    if (dsrc[i] == dout) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases dout", fn, i);
+    if (!aligned16(dsrc[i]) || dsrc_ld[i] % 4 != 0) vec_ok = false;
+    p.dsrc.ptr[i] = dsrc[i];
+    p.dsrc.ld[i] = dsrc_ld[i];
+  }
+  const int use_vec = vec_ok ? vec : 1;
+  if (!lrar::backward_supported(d, r, use_vec))
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: d = %d is too wide for the %s path", fn, d,
+                use_vec > 1 ? "vector" : "scalar");
+  const size_t need = lrar::backward_workspace(T, r);
+  if (T > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(LRAR_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace_bytes);
+  if (T > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+    return fail(LRAR_ERR_INVALID, "%s: workspace must be 8-byte aligned", fn);
+  if (T == 0) return LRAR_OK;
+  p.n = n;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.q = q;
+  p.dout = dout;
+  p.dout_ld = dout_ld;
+  p.accumulate = accumulate;
+  p.dq = dq;
+  p.workspace = workspace;
+  return device_status(lrar::launch_backward(p, io == LRAR_BF16, use_vec,
+                                             static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  const char* fn = "lrar_copy";
+  if (bytes == 0) return LRAR_OK;
+  if (dst == nullptr || src == nullptr) return fail(LRAR_ERR_INVALID, "%s: null pointer", fn);
+  if (!aligned16(dst) || !aligned16(src) || bytes % 16 != 0)
+    return fail(LRAR_ERR_INVALID, "%s: pointers and size must be 16-byte multiples", fn);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(dst), b = reinterpret_cast<uintptr_t>(src);
+  if (a < b + bytes && b < a + bytes) return fail(LRAR_ERR_INVALID, "%s: buffers overlap", fn);
+  return device_status(lrar::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)), fn);
+}
+
+const char* lrar_status_string(lrar_status s) {
+  switch (s) {
+    case LRAR_OK: return "ok";
+    case LRAR_ERR_INVALID: return "invalid argument";
+    case LRAR_ERR_UNSUPPORTED: return "unsupported shape or variant";
+    case LRAR_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* lrar_last_error(void) { return g_last_error.c_str(); }
+
+const char* lrar_version(void) { return "0.1.0"; }
+
+}  // extern "C"
+
+// ---- the calibration copy kernel ---------------------------------------------------------------
+
+namespace lrar {
+
+__global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
+                                                 const u32x4* __restrict__ src, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  int64_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
+  return hipGetLastError();
+}
+
+}  // namespace lrar

@@ -1,0 +1,324 @@
+// Device-side building blocks of liblrattnres (internal; not installed).
+//
+// Layout conventions used by every kernel:
+//   * One 64-lane wavefront owns one token row at a time; a 256-thread workgroup holds four
+//     such rows. Rows are visited with a grid-stride loop.
+//   * A row is cut into "units" of VEC consecutive elements, 16 bytes on the vector path
+//     (8 bf16 or 4 fp32) and one element on the scalar path. Lane l touches units
+//     l, l + 64, l + 128, ... so each load instruction of a wave covers one contiguous
+//     1 KiB stretch of the row.
+//   * The key slice is the columns [d - r, d). Units that straddle d - r mask their leading
+//     elements out of the key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrar {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kMaxSources = 64;
+constexpr int kMaxQueries = 64;
+
+// Source pointer table, passed by value in the kernel arguments (1 KiB).
+struct SrcList {
+  const void* ptr[kMaxSources];
+  int64_t ld[kMaxSources];
+};
+
+struct DstList {
+  float* ptr[kMaxSources];
+  int64_t ld[kMaxSources];
+};
+
+using bf16_bits = uint16_t;
+
+// Native 16-byte vector types (accepted by the non-temporal load/store builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- scalar conversions ------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN (quietened).
+__device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_bits>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_bits>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<bf16_bits>(bf16_bits v) { return bf16_to_f32(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float v) { return f32_to_bf16(v); }
+
+// ---- unit loads and stores ------------------------------------------------------------------
+
+// A unit of VEC elements of type T held in raw (undecoded) form.
+template <typename T, int VEC>
+struct Unit;
+
+template <>
+struct Unit<bf16_bits, 8> {
+  u32x4 raw;
+  __device__ __forceinline__ void load(const bf16_bits* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ void load_cached(const bf16_bits* p) {
+    raw = *reinterpret_cast<const u32x4*>(p);
+  }
+  __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = __uint_as_float(raw.x << 16);
+    x[1] = __uint_as_float(raw.x & 0xffff0000u);
+    x[2] = __uint_as_float(raw.y << 16);
+    x[3] = __uint_as_float(raw.y & 0xffff0000u);
+    x[4] = __uint_as_float(raw.z << 16);
+    x[5] = __uint_as_float(raw.z & 0xffff0000u);
+    x[6] = __uint_as_float(raw.w << 16);
+    x[7] = __uint_as_float(raw.w & 0xffff0000u);
+  }
+};
+
+template <>
+struct Unit<float, 4> {
+  f32x4 raw;
+  __device__ __forceinline__ void load(const float* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  }
+  __device__ __forceinline__ void load_cached(const float* p) {
+    raw = *reinterpret_cast<const f32x4*>(p);
+  }
+  __device__ __forceinline__ void zero() { raw = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void get(float (&x)[4]) const {
+    x[0] = raw.x;
+    x[1] = raw.y;
+    x[2] = raw.z;
+    x[3] = raw.w;
+  }
+};
+
+template <typename T>
+struct Unit<T, 1> {
+  T raw;
+  __device__ __forceinline__ void load(const T* p) { raw = *p; }
+  __device__ __forceinline__ void load_cached(const T* p) { raw = *p; }
+  __device__ __forceinline__ void zero() { raw = T(0); }
+  __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = to_f32<T>(raw); }
+};
+
+// Store VEC floats as VEC elements of T at p (16-byte aligned on the vector path).
+template <typename T, int VEC>
+__device__ __forceinline__ void store_unit(T* p, const float (&x)[VEC]);
+
+template <>
+__device__ __forceinline__ void store_unit<bf16_bits, 8>(bf16_bits* p, const float (&x)[8]) {
+  u32x4 v;
+  v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+  v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+  v.z = static_cast<uint32_t>(f32_to_bf16(x[4])) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
+  v.w = static_cast<uint32_t>(f32_to_bf16(x[6])) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+template <>
+__device__ __forceinline__ void store_unit<float, 4>(float* p, const float (&x)[4]) {
+  __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+}
+
+template <>
+__device__ __forceinline__ void store_unit<float, 8>(float* p, const float (&x)[8]) {
+  __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p) + 1);
+}
+
+template <>
+__device__ __forceinline__ void store_unit<float, 1>(float* p, const float (&x)[1]) { *p = x[0]; }
+
+template <>
+__device__ __forceinline__ void store_unit<bf16_bits, 1>(bf16_bits* p, const float (&x)[1]) {
+  *p = f32_to_bf16(x[0]);
+}
+
+// Load VEC float32 values (16-byte aligned on the vector path).
+template <int VEC>
+__device__ __forceinline__ void load_f32(const float* p, float (&x)[VEC]) {
+  if constexpr (VEC % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC / 4; ++v) {
+      const f32x4 t = reinterpret_cast<const f32x4*>(p)[v];
+      x[4 * v + 0] = t.x;
+      x[4 * v + 1] = t.y;
+      x[4 * v + 2] = t.z;
+      x[4 * v + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) x[v] = p[v];
+  }
+}
+
+// Load VEC accumulator values of type A (float or bf16) as floats.
+template <typename A, int VEC>
+__device__ __forceinline__ void load_acc(const A* p, float (&x)[VEC]) {
+  if constexpr (sizeof(A) == 4) {
+    load_f32<VEC>(reinterpret_cast<const float*>(p), x);
+  } else if constexpr (VEC == 8) {
+    Unit<bf16_bits, 8> u;
+    u.load(reinterpret_cast<const bf16_bits*>(p));
+    u.get(x);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) x[v] = to_f32<A>(p[v]);
+  }
+}
+
+template <typename A, int VEC>
+__device__ __forceinline__ void store_acc(A* p, const float (&x)[VEC]) {
+  if constexpr (sizeof(A) == 4 && VEC % 4 == 0) {
+    store_unit<float, VEC>(reinterpret_cast<float*>(p), x);
+  } else if constexpr (sizeof(A) == 2 && VEC == 8) {
+    store_unit<bf16_bits, 8>(reinterpret_cast<bf16_bits*>(p), x);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) p[v] = from_f32<A>(x[v]);
+  }
+}
+
+// ---- cross-lane reductions -------------------------------------------------------------------
+// Butterfly (xor) reductions: every lane ends with the same, bitwise identical result because
+// each step adds the same two operands on both partners.
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ __forceinline__ double group_sum(double v, int group) {
+  for (int o = group >> 1; o >= 1; o >>= 1) v += shfl_xor_f64(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += shfl_xor_f64(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, shfl_xor_f64(v, o));
+  return v;
+}
+
+// Value of a float held in lane `lane` (lane must be wave-uniform).
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ double lane_f64(double v, int lane) {
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffff), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// ---- key-slice geometry ----------------------------------------------------------------------
+
+struct KeyGeom {
+  int c0;      // first key column, d - r
+  int ub;      // first unit touching the key
+  int nur;     // units per row
+  int group;   // lanes that cooperate on one source's key (a power of two <= 64)
+  int per_it;  // sources handled per iteration of the key pass (64 / group)
+};
+
+template <int VEC>
+__device__ __forceinline__ KeyGeom key_geom(int d, int r) {
+  KeyGeom g;
+  g.c0 = d - r;
+  g.ub = g.c0 / VEC;
+  g.nur = (d + VEC - 1) / VEC;
+  const int nut = g.nur - g.ub;
+  int G = 1;
+  while (G < nut && G < kWave) G <<= 1;
+  g.group = G;
+  g.per_it = kWave / G;
+  return g;
+}
+
+// The query value of key column `col` (>= c0), or 0 for a column outside the key.
+__device__ __forceinline__ double q_at(const float* __restrict__ q, int col, int c0) {
+  return col >= c0 ? static_cast<double>(q[col - c0]) : 0.0;
+}
+
+// Slice scores of the n sources of one row. On return lane i (< n) holds z_i and rho_i of
+// source i; other lanes hold unspecified values. float64 throughout: each bf16 x fp32 product
+// is exact in float64, so the only rounding is in the sums.
+template <typename IO, int VEC>
+__device__ __forceinline__ void row_scores(const SrcList& S, int n, int64_t row, int d, int r,
+                                           double eps, const float* __restrict__ q, int lane,
+                                           double& z_mine, double& rho_mine) {
+  const KeyGeom g = key_geom<VEC>(d, r);
+  const int slot = lane / g.group;
+  const int sub = lane % g.group;
+  const int iters = (n + g.per_it - 1) / g.per_it;
+  z_mine = 0.0;
+  rho_mine = 1.0;
+  for (int it = 0; it < iters; ++it) {
+    // The source of this lane's group; the pointer table is indexed with a uniform index
+    // per candidate and selected per lane, so the table stays in scalar registers.
+    const int i = it * g.per_it + slot;
+    const IO* base = nullptr;
+    int64_t ld = 0;
+    for (int c = 0; c < g.per_it; ++c) {
+      const int ic = it * g.per_it + c;
+      if (ic < n && c == slot) {
+        base = static_cast<const IO*>(S.ptr[ic]);
+        ld = S.ld[ic];
+      }
+    }
+    double dot = 0.0, ss = 0.0;
+    if (i < n) {
+      const IO* rowp = base + row * ld;
+      for (int u = g.ub + sub; u < g.nur; u += g.group) {
+        Unit<IO, VEC> un;
+        un.load_cached(rowp + u * VEC);
+        float x[VEC];
+        un.get(x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int col = u * VEC + e;
+          const double k = (col >= g.c0) ? static_cast<double>(x[e]) : 0.0;
+          dot = fma(q_at(q, col, g.c0), k, dot);
+          ss = fma(k, k, ss);
+        }
+      }
+    }
+    dot = group_sum(dot, g.group);
+    ss = group_sum(ss, g.group);
+    const double rho = sqrt(ss / r + eps);
+    const double z = dot / rho;
+    const int src_lane = (lane % g.per_it) * g.group;
+    const double zt = __shfl(z, src_lane, kWave);
+    const double rt = __shfl(rho, src_lane, kWave);
+    if (lane / g.per_it == it) {
+      z_mine = zt;
+      rho_mine = rt;
+    }
+  }
+}
+
+}  // namespace lrar

@@ -1,0 +1,86 @@
+// Kernel parameter blocks and launchers of liblrattnres (internal; not installed).
+// Every launcher assumes its arguments were validated by the entry points in lrar_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lrar_device.h"
+
+namespace lrar {
+
+// The read (lrar_forward) and the merge (lrar_merge, which adds a prior accumulator).
+struct ReadParams {
+  SrcList src;
+  int n;
+  int d, r;
+  int64_t T;
+  double eps;
+  const float* q;
+  void* out;
+  int64_t out_ld;
+  float* alpha;  // nullable
+  int64_t alpha_ld;
+  // merge only
+  const float* m_in;
+  const float* l_in;
+  const void* acc;
+  int64_t acc_ld;
+  float* m_out;  // nullable
+  float* l_out;  // nullable
+};
+
+enum class ReadKind { kTwoPass, kOnline, kMerge };
+
+// Phase-1 statistics (lrar_forward_stats).
+struct StatsParams {
+  SrcList src;
+  int n;
+  int d, r;
+  int64_t T;
+  double eps;
+  int nq;
+  const float* q;
+  int64_t q_ld;
+  float* m;
+  float* l;
+  int64_t ml_ld;
+  void* acc;
+  int64_t acc_ld;
+  int64_t acc_qstride;
+};
+
+// Backward (lrar_backward).
+struct BwdParams {
+  SrcList src;
+  DstList dsrc;
+  int n;
+  int d, r;
+  int64_t T;
+  double eps;
+  const float* q;
+  const float* dout;
+  int64_t dout_ld;
+  int accumulate;
+  float* dq;
+  void* workspace;  // [grid + reduce groups][r] float64 dq partials
+};
+
+hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
+                       hipStream_t s);
+int online_max_units();
+
+hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s);
+
+// Backward: grid size (workgroups) used for T rows, and the launcher.
+int backward_grid(int64_t T);
+int backward_max_units();
+// Lanes' register window for dq partials must cover the key; false if this shape needs more.
+bool backward_supported(int d, int r, int vec);
+size_t backward_workspace(int64_t T, int r);
+hipError_t launch_backward(const BwdParams& p, int io_bf16, int vec, hipStream_t s);
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+}  // namespace lrar
