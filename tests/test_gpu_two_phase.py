@@ -12,6 +12,7 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
 def check_stats(srcs, qs, r, eps, acc_dtype, where):
+    qs = qs.reshape(-1, r) if qs.dim() == 1 else qs
     say(f"[stats] {where} T={srcs[0].shape[0]} d={srcs[0].shape[1]} r={r} n={len(srcs)} "
         f"nq={qs.shape[0]} acc={acc_dtype}")
     m, l, acc = lrar.lrar_forward_stats(srcs, qs, r, eps, acc_dtype=acc_dtype)

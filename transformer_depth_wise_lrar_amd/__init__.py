@@ -120,6 +120,30 @@ def _rows(t, name):
     return t.data_ptr(), t.stride(0)
 
 
+def _need(t, shape, dtype, name):
+    """t is a GPU tensor of `dtype` whose leading dims are at least `shape` (None = any).
+    Every buffer the library writes or reads is checked here, so a wrongly sized tensor
+    fails on the host instead of in a kernel."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape):
+        raise ValueError(f"{name} must have {len(shape)} dims, got shape {tuple(t.shape)}")
+    for k, (have, want) in enumerate(zip(t.shape, shape)):
+        if want is not None and have < want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; dim {k} must be >= {want}")
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a unit inner stride")
+    return t
+
+
+def _query(q, r, name="q"):
+    torch = _torch()
+    _need(q, (r,), torch.float32, name)
+    return q
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
@@ -157,14 +181,18 @@ def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=N
     fp32 [T, >=n] tensor to write them into. Returns (out, alpha or None)."""
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, None)
+    _query(q, r)
     if out is None:
         out = torch.empty((T, d), dtype=srcs[0].dtype, device=srcs[0].device)
+    _need(out, (T, d), srcs[0].dtype, "out")
     op, old = _rows(out, "out")
     if alpha is True:
         alpha = torch.empty((T, len(srcs)), dtype=torch.float32, device=srcs[0].device)
-    ap, ald = (_rows(alpha, "alpha") if alpha is not None and alpha is not False else (None, 0))
     if alpha is False:
         alpha = None
+    if alpha is not None:
+        _need(alpha, (T, len(srcs)), torch.float32, "alpha")
+    ap, ald = _rows(alpha, "alpha") if alpha is not None else (None, 0)
     _check(lib().lrar_forward(T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op,
                               old, ap, ald, VARIANTS[variant], _stream(stream)))
     return out, alpha
@@ -179,6 +207,7 @@ def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=
     ptrs, lds, io, T, d = _src_table(srcs, None)
     if qs.dim() == 1:
         qs = qs.view(1, -1)
+    _need(qs, (1, r), torch.float32, "qs")
     nq = qs.shape[0]
     dev = srcs[0].device
     acc_dtype = torch.float32 if acc_dtype is None else acc_dtype
@@ -188,6 +217,9 @@ def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=
         l = torch.empty((nq, T), dtype=torch.float32, device=dev)
     if acc is None:
         acc = torch.empty((nq, T, d), dtype=acc_dtype, device=dev)
+    _need(m, (nq, T), torch.float32, "m")
+    _need(l, (nq, T), torch.float32, "l")
+    _need(acc, (nq, T, d), None, "acc")
     if acc.stride(2) != 1 or m.stride(1) != 1 or l.stride(1) != 1 or m.stride(0) != l.stride(0):
         raise ValueError("m, l, acc need unit inner stride and m, l one row stride")
     _check(lib().lrar_forward_stats(T, d, r, float(eps), io, len(srcs), ptrs, lds, nq,
@@ -209,10 +241,18 @@ def lrar_merge(m, l, acc, srcs: Sequence, q, r: int, eps: float = 1e-6, out=None
             raise ValueError("with no extra sources pass out= or io_dtype=")
         io = _dtype_code(out) if out is not None else (
             LRAR_BF16 if io_dtype == torch.bfloat16 else LRAR_F32)
+    if T is not None and tuple(acc.shape) != (T, d):
+        raise ValueError("acc and the extra sources must share one shape [T, d]")
     T, d = acc.shape
+    _need(acc, (T, d), None, "acc")
+    _need(m, (T,), torch.float32, "m")
+    _need(l, (T,), torch.float32, "l")
+    if len(srcs):
+        _query(q, r)
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16 if io == LRAR_BF16 else torch.float32,
                           device=acc.device)
+    _need(out, (T, d), torch.bfloat16 if io == LRAR_BF16 else torch.float32, "out")
     op, old = _rows(out, "out")
     accp, accld = _rows(acc, "acc")
     m_out = l_out = None
@@ -244,12 +284,18 @@ def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
     if dsrc is None:
         dsrc = [torch.zeros((T, d), dtype=torch.float32, device=dev) if accumulate
                 else torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(n)]
+    if len(dsrc) != n:
+        raise ValueError(f"dsrc needs {n} tensors, got {len(dsrc)}")
+    _query(q, r)
+    _need(dout, (T, d), torch.float32, "dout")
     dptrs = (ctypes.c_void_p * max(n, 1))()
     dlds = (ctypes.c_int64 * max(n, 1))()
     for i, g in enumerate(dsrc):
+        _need(g, (T, d), torch.float32, f"dsrc[{i}]")
         dptrs[i], dlds[i] = _rows(g, f"dsrc[{i}]")
     if dq is None:
         dq = torch.empty((r,), dtype=torch.float32, device=dev)
+    _need(dq, (r,), torch.float32, "dq")
     need = lrar_backward_workspace_size(T, d, r, n)
     if workspace is None:
         workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
