@@ -1,0 +1,396 @@
+"""Throughput of the LR-AttnRes depth-mix read on one MI355X (gfx950).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
+
+One step is the depth mix of one forward pass of the full-routing model shape of the
+LR-AttnRes paper's 0.5B runs (§4.1: d = 1024, 24 layers = 48 sub-layer writes, so 49
+sources and 49 read sites, site t reading sources 0..t-1) over 8 x 2048 tokens, with the
+routing key the last r = 64 coordinates (§3.3). Every read site is one lrar_forward call
+(bf16 sources and output, fp32 query) on torch's current stream.
+
+Timing. Each launch is bracketed by HIP events recorded on the stream the library launches
+on. Before every launch a 512 MiB device copy evicts the 256 MiB Infinity Cache and the L2s,
+so every source byte comes from HBM, as it would after the sub-layers that run between two
+reads in a real model. The step time is the sum of the read launches' durations; the
+eviction copies are outside it (their cost is shown separately as wall time).
+
+Output: ONE JSON line on stdout. `value` is tokens/s per read site averaged over the 49
+sites (tokens x sites / total read time); `roofline` prices the read kernel's algorithmic
+bytes, e (n + 1) d per token at a site with n sources, against MI355X's 8 TB/s HBM peak;
+`rows` reports the other hot-path steps (block routing at d = 2048, production width
+d = 7168 single-pass and two-phase, and the backward) on their own workloads;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+EVICT_BYTES = 256 << 20         # copied per eviction: 256 MiB read + 256 MiB written
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "transformer_depth_wise_lrar_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources: counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Evictor:
+    """A device copy big enough to push every earlier line out of L2 and the MALL."""
+
+    def __init__(self, torch, lrar):
+        self.a = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
+        self.b = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
+        self.a.fill_(1)
+        self.lrar = lrar
+
+    def __call__(self):
+        self.lrar.lrar_copy(self.b, self.a)
+
+
+class Timer:
+    """Per-launch durations from HIP events on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def collect_ms(self):
+        self.torch.cuda.synchronize()
+        out = [s.elapsed_time(e) for s, e in self.pairs]
+        self.pairs = []
+        return out
+
+
+def gen_sources(torch, n, T, d, scale, seed, dtype):
+    """n [T, d] sources N(0,1) x U[scale] drawn on the device (seeded)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    sc = torch.empty(n, dtype=torch.float64).uniform_(
+        scale[0], scale[1], generator=torch.Generator().manual_seed(seed + 1))
+    out = []
+    for i in range(n):
+        x = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+        x.mul_(float(sc[i]))
+        out.append(x.to(dtype))
+        del x
+    return out
+
+
+def gen_queries(torch, nq, r, seed, std=1.0):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((nq, r), generator=g, device="cuda", dtype=torch.float32) * std
+
+
+# ---- the headline workload ----------------------------------------------------------------------
+
+FULL = dict(T=8 * 2048, d=1024, r=64, eps=1e-6, n_sources=49, scale=(0.5, 2.0))
+
+
+def fwd_bytes(T, d, n, e):
+    return e * (n + 1) * d * T
+
+
+def headline(torch, lrar, args, ev):
+    c = FULL
+    T, d, r, eps, S = c["T"], c["d"], c["r"], c["eps"], c["n_sources"]
+    srcs = gen_sources(torch, S, T, d, c["scale"], seed=1000, dtype=torch.bfloat16)
+    qs = gen_queries(torch, S, r, seed=1001)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
+
+    def step(timed):
+        for n in range(1, S + 1):
+            ev()
+            call = (lambda n=n: lrar.lrar_forward(srcs[:n], qs[n - 1], r, eps, out=out))
+            if timed:
+                tm.run(call)
+            else:
+                call()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = tm.collect_ms()
+    per_site = [[ms[k * S + (n - 1)] for k in range(args.steps)] for n in range(1, S + 1)]
+    site_ms = [sorted(v)[len(v) // 2] for v in per_site]          # median per site
+    step_ms = sum(ms) / args.steps                                   # mean read time per step
+    bytes_step = sum(fwd_bytes(T, d, n, 2) for n in range(1, S + 1))
+    gbps = bytes_step / (step_ms * 1e-3) / 1e9
+    sites = {str(n): dict(ms=round(site_ms[n - 1], 5),
+                          GBps=round(fwd_bytes(T, d, n, 2) / (site_ms[n - 1] * 1e-3) / 1e9, 1))
+             for n in (1, 2, 5, 9, 13, 25, 37, 49)}
+    del srcs
+    return dict(step_ms=step_ms, wall_ms=wall * 1e3 / args.steps, gbps=gbps, T=T, S=S,
+                bytes_step=bytes_step, launches=S, sites=sites)
+
+
+# ---- the other hot-path steps on their own workloads --------------------------------------------
+
+def time_calls(torch, ev, fn, reps, warm=2):
+    tm = Timer(torch)
+    for _ in range(warm):
+        ev()
+        fn()
+    for _ in range(reps):
+        ev()
+        tm.run(fn)
+    ms = sorted(tm.collect_ms())
+    return ms[len(ms) // 2]
+
+
+def row_entry(ms, nbytes):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return dict(ms=round(ms, 5), GBps=round(g, 1), frac=round(g / HBM_PEAK_GBPS, 4))
+
+
+def rows_block_routing(torch, lrar, ev, reps):
+    """Block routing, d = 2048, T = 16 x 4096: the widest site (n = 9) and the capacity
+    site (n = 10), r in {16, 64, 512, 2048 = d}, both read variants."""
+    T, d = 16 * 4096, 2048
+    srcs = gen_sources(torch, 10, T, d, (0.5, 4.0), seed=2000, dtype=torch.bfloat16)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for r in (16, 64, 512, 2048):
+        q = gen_queries(torch, 1, r, seed=2001 + r)[0]
+        for n in (9, 10):
+            for var in ("two_pass", "online"):
+                ms = time_calls(torch, ev, lambda: lrar.lrar_forward(
+                    srcs[:n], q, r, 1e-6, out=out, variant=var), reps)
+                res[f"r{r}_n{n}_{var}"] = row_entry(ms, fwd_bytes(T, d, n, 2))
+    del srcs, out
+    return res
+
+
+def rows_production(torch, lrar, ev, reps):
+    """Production width d = 7168, T = 32768, 93 writes in 8 blocks (n <= 9): single-pass
+    reads at r in {64, 1792, 7168}; the two-phase schedule of the largest block (Phase 1:
+    8 cached sources x 12 site queries; Phase 2: one merge per site with the partial sum)."""
+    T, d, nq = 32768, 7168, 12
+    srcs = gen_sources(torch, 9, T, d, (0.5, 4.0), seed=3000, dtype=torch.bfloat16)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for r in (64, 1792, 7168):
+        q = gen_queries(torch, 1, r, seed=3001 + r)[0]
+        for var in ("two_pass", "online"):
+            ms = time_calls(torch, ev, lambda: lrar.lrar_forward(
+                srcs, q, r, 1e-6, out=out, variant=var), reps)
+            res[f"single_pass_r{r}_n9_{var}"] = row_entry(ms, fwd_bytes(T, d, 9, 2))
+    r = 1792
+    qs = gen_queries(torch, nq, r, seed=3100)
+    for acc_name, acc_dt, ae in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        m = torch.empty((nq, T), dtype=torch.float32, device="cuda")
+        l = torch.empty((nq, T), dtype=torch.float32, device="cuda")
+        acc = torch.empty((nq, T, d), dtype=acc_dt, device="cuda")
+        ms1 = time_calls(torch, ev, lambda: lrar.lrar_forward_stats(
+            srcs[:8], qs, r, 1e-6, m=m, l=l, acc=acc), reps)
+        b1 = 2 * 8 * d * T + nq * (ae * d + 8) * T
+        res[f"phase1_r{r}_ninter8_q{nq}_acc{acc_name}"] = row_entry(ms1, b1)
+        ms2 = time_calls(torch, ev, lambda: lrar.lrar_merge(
+            m[0], l[0], acc[0], srcs[8:9], qs[0], r, 1e-6, out=out), reps)
+        b2 = (ae * d + 8 + 2 * d + 2 * d) * T
+        res[f"phase2_r{r}_acc{acc_name}"] = row_entry(ms2, b2)
+        del m, l, acc
+    del srcs, out
+    return res
+
+
+def rows_backward(torch, lrar, ev, reps):
+    """Backward of block routing: d = 4096, r = 1024, n = 10, T = 16384, fp32 gradients."""
+    T, d, r, n = 16384, 4096, 1024, 10
+    srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=4000, dtype=torch.bfloat16)
+    q = gen_queries(torch, 1, r, seed=4001)[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4002)
+    dout = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+    dsrc = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(n)]
+    dq = torch.empty((r,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((lrar.lrar_backward_workspace_size(T, d, r, n),), dtype=torch.uint8,
+                     device="cuda")
+    ms = time_calls(torch, ev, lambda: lrar.lrar_backward(
+        srcs, q, dout, r, 1e-6, dsrc=dsrc, dq=dq, workspace=ws), reps)
+    nbytes = (2 * n * d + 4 * d + 4 * n * d) * T + 4 * r
+    res = {f"backward_r{r}_n{n}": row_entry(ms, nbytes)}
+    del srcs, dsrc, dout
+    return res
+
+
+# ---- the CPU baseline: the oracle on a bounded sample -------------------------------------------
+
+def cpu_baseline(torch, budget_s=12.0):
+    """The fp64 oracle on the first R rows of the headline workload, all 49 sites, run on
+    host threads over row chunks (the oracle itself is single-threaded)."""
+    import numpy as np
+
+    import oracle
+    from transformer_depth_wise_lrar_amd import synth
+
+    c = FULL
+    d, r, eps, S = c["d"], c["r"], c["eps"], c["n_sources"]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    srcs_dev = gen_sources(torch, S, 4096, d, c["scale"], seed=1000, dtype=torch.bfloat16)
+    qs = synth.to_f64(gen_queries(torch, S, r, seed=1001))
+    srcs = [synth.to_f64(s) for s in srcs_dev]
+    del srcs_dev
+
+    def run(R):
+        chunk = (R + threads - 1) // threads
+
+        def work(lo):
+            hi = min(R, lo + chunk)
+            for n in range(1, S + 1):
+                oracle.forward([s[lo:hi] for s in srcs[:n]], qs[n - 1], r, eps)
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(0, R, chunk)))
+        return time.perf_counter() - t0
+
+    R = threads * 4
+    dt = run(R)
+    R = int(min(4096, max(R, R * budget_s / max(dt, 1e-3))))
+    R -= R % threads or 0
+    dt = run(R)
+    rate = R * S / dt
+    return dict(value=round(rate, 1), unit="tokens/s per read site", cores=threads,
+                kind="oracle",
+                sample=f"full routing d=1024 r=64: rows 0..{R - 1} of T=16384, all 49 sites, "
+                       f"fp64 oracle on {threads} host threads ({dt:.1f} s)")
+
+
+def copy_ceiling(torch, lrar, ev, reps):
+    """A plain 1 GiB device copy (2 GiB of traffic): what streaming reaches on this GPU."""
+    nbytes = 1 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(3)
+    ms = time_calls(torch, ev, lambda: lrar.lrar_copy(b, a), reps)
+    del a, b
+    return row_entry(ms, 2 * nbytes)
+
+
+# ---- main ------------------------------------------------------------------------------------------
+
+def traffic_entry(digest, launches_bytes):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=10, help="launches per extra row")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the depth-mix read shards by token rows with no "
+              "exchange in the forward, so there is no multi-GPU run here (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_depth_wise_lrar_amd as lrar
+
+    lrar.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    ev = Evictor(torch, lrar)
+    log(f"bench: headline full routing, steps={args.steps} warmup={args.warmup}")
+    h = headline(torch, lrar, args, ev)
+    log(f"bench: headline {h['step_ms']:.3f} ms/step, {h['gbps']:.0f} GB/s")
+    rows = {}
+    copy = copy_ceiling(torch, lrar, ev, args.reps)
+    log(f"bench: copy ceiling {copy['GBps']:.0f} GB/s")
+    if not args.no_rows:
+        for name, fn in (("block_routing_d2048", rows_block_routing),
+                         ("production_d7168", rows_production),
+                         ("backward_d4096", rows_backward)):
+            log(f"bench: row {name}")
+            rows[name] = fn(torch, lrar, ev, args.reps)
+            torch.cuda.empty_cache()
+    digest = source_digest()
+    bytes_launch = h["bytes_step"] / h["launches"]
+    avg_launch_s = h["step_ms"] * 1e-3 / h["launches"]
+    achieved = bytes_launch / avg_launch_s / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4),
+                    traffic=traffic_entry(digest, bytes_launch),
+                    kernel="k_read_two_pass (bf16, d=1024)",
+                    algorithmic_bytes_per_launch=round(bytes_launch),
+                    avg_launch_us=round(avg_launch_s * 1e6, 3))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(torch)
+    tokens_site_per_s = h["T"] * h["S"] / (h["step_ms"] * 1e-3)
+    line = {
+        "metric": "depth-mix tokens/sec and effective HBM GB/s (% of MI355X peak), bf16, per site",
+        "value": round(tokens_site_per_s, 1),
+        "unit": "tokens/s per read site (mean over 49 sites)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(h["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full routing d=1024 r=64, 49 sources / 49 read sites, "
+                               "T=8x2048 tokens, bf16 sources, fp32 queries",
+                   "global_batch": 8, "seq_len": 2048, "parallelism": "none (1 GPU)"},
+        "effective_GBps": round(h["gbps"], 1),
+        "copy_ceiling": copy,
+        "wall_ms_per_step_with_eviction": round(h["wall_ms"], 3),
+        "sites": h["sites"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "source_digest": digest,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
