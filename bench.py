@@ -361,7 +361,7 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic_entry(digest, bytes_launch),
-                    kernel="k_read_two_pass (bf16, d=1024)",
+                    kernel="k_read_tile (online, bf16, d=1024, r=64)",
                     algorithmic_bytes_per_launch=round(bytes_launch),
                     avg_launch_us=round(avg_launch_s * 1e6, 3))
     cpu = None

@@ -165,3 +165,17 @@ def test_empty_batch():
     out, al = lrar.lrar_forward(srcs, query(64, seed=85), 64, 1e-6, alpha=True)
     torch.cuda.synchronize()
     assert out.shape == (0, 1024)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("r", [1, 16, 63, 64, 65, 100, 127, 128, 129, 200, 254, 256, 257, 384,
+                               512, 1000, 1024])
+def test_key_paths(io, r):
+    """Every way the key is scored: spread pieces of 1, 2 or 4 elements per lane (r up to 64,
+    128, 256 when the key start allows), key units in the last slot or in every slot; on a
+    ragged row count so the last tile is partial."""
+    srcs = sources(10, 77, 1024, io, seed=90 + r)
+    q = query(r, seed=91)
+    for n in (3, 10):
+        for variant in VARIANTS:
+            run_and_check(srcs[:n], q, r, 1e-6, variant, f"key path r={r} n={n}")

@@ -112,19 +112,19 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
   if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
   const int use_vec = vec_ok ? vec : 1;
   const int nur = (d + use_vec - 1) / use_vec;
-  const bool online_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::online_max_units();
+  // A row fits a register tile when each lane holds at most tile_max_units() units of it.
+  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_units();
   lrar::ReadKind kind;
   if (variant == LRAR_VARIANT_ONLINE) {
-    if (!online_fits)
+    if (!tile_fits)
       return fail(LRAR_ERR_UNSUPPORTED, "%s: the online variant holds a whole row in registers; "
                   "d = %d is too wide on this path", fn, d);
     kind = lrar::ReadKind::kOnline;
   } else if (variant == LRAR_VARIANT_TWO_PASS) {
     kind = lrar::ReadKind::kTwoPass;
   } else {
-    // A key wider than half the row is cheaper to read once (online); a narrow key is
-    // cheaper to score first and stream the values once (two-pass).
-    kind = (online_fits && 2 * r > d) ? lrar::ReadKind::kOnline : lrar::ReadKind::kTwoPass;
+    // Reading every byte once (online) is the cheapest whenever the row fits a tile.
+    kind = tile_fits ? lrar::ReadKind::kOnline : lrar::ReadKind::kTwoPass;
   }
   if (T == 0) return LRAR_OK;
   p.n = n;
@@ -137,9 +137,10 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
   p.out_ld = out_ld;
   p.alpha = alpha;
   p.alpha_ld = alpha_ld;
-  return device_status(lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0,
-                                         static_cast<hipStream_t>(stream)),
-                       fn);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = tile_fits ? lrar::launch_tile(p, kind, io == LRAR_BF16, use_vec, 0, hs)
+                                 : lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0, hs);
+  return device_status(e, fn);
 }
 
 lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
@@ -239,10 +240,16 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
   p.acc_ld = acc_ld;
   p.m_out = m_out;
   p.l_out = l_out;
-  return device_status(lrar::launch_read(p, lrar::ReadKind::kMerge, io == LRAR_BF16,
-                                         vec_ok ? vec : 1, acc_dtype == LRAR_BF16,
-                                         static_cast<hipStream_t>(stream)),
-                       fn);
+  const int use_vec = vec_ok ? vec : 1;
+  const int nur = (d + use_vec - 1) / use_vec;
+  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_units();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      tile_fits ? lrar::launch_tile(p, lrar::ReadKind::kMerge, io == LRAR_BF16, use_vec,
+                                    acc_dtype == LRAR_BF16, hs)
+                : lrar::launch_read(p, lrar::ReadKind::kMerge, io == LRAR_BF16, use_vec,
+                                    acc_dtype == LRAR_BF16, hs);
+  return device_status(e, fn);
 }
 
 size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n) {

@@ -223,6 +223,128 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
+// ---- DPP reductions ----------------------------------------------------------------------------
+// Cross-lane data movement through the DPP modifier of VALU moves: no LDS crossbar, a few
+// cycles per step. A float64 moves as its two 32-bit halves. `OLD` is what lanes of disabled
+// rows keep.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double v, double old) {
+  const int64_t b = __double_as_longlong(v);
+  const int64_t o = __double_as_longlong(old);
+  const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(o), static_cast<int>(b), CTRL,
+                                             ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(o >> 32), static_cast<int>(b >> 32),
+                                             CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each row of 16
+constexpr int kDppBcast15 = 0x142;     // lane 15 of each row -> the next row
+constexpr int kDppBcast31 = 0x143;     // lane 31 -> rows 2 and 3
+
+// Sum over the 64 lanes, returned wave-uniform. The order of the additions is fixed, so the
+// result is reproducible; it is the value that accumulates in lane 63.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_f64<kDppXor1>(v, 0.0);
+  v += dpp_f64<kDppXor2>(v, 0.0);
+  v += dpp_f64<kDppHalfMirror>(v, 0.0);
+  v += dpp_f64<kDppMirror>(v, 0.0);
+  v += dpp_f64<kDppBcast15, 0xa>(v, 0.0);
+  v += dpp_f64<kDppBcast31, 0xc>(v, 0.0);
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// N independent sums reduced together: the DPP chains interleave, so their latencies
+// overlap. Each result is wave-uniform and added in the same fixed order as wave_sum_dpp.
+template <int N>
+__device__ __forceinline__ void wave_sums_dpp(double (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppXor1>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppXor2>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppHalfMirror>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppMirror>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppBcast15, 0xa>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppBcast31, 0xc>(v[k], 0.0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int64_t b = __double_as_longlong(v[k]);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+    v[k] = __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+  }
+}
+
+// N sums over lanes [0, gp) (gp a power of two in [1, 64], wave-uniform), each returned
+// wave-uniform. Lanes from gp up are not read, and every lane must hold its own value.
+template <int N>
+__device__ __forceinline__ void lanes_sums_dpp(double (&v)[N], int gp) {
+  if (gp >= 2) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppXor1>(v[k], 0.0);
+  }
+  if (gp >= 4) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppXor2>(v[k], 0.0);
+  }
+  if (gp >= 8) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppHalfMirror>(v[k], 0.0);
+  }
+  if (gp >= 16) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppMirror>(v[k], 0.0);
+  }
+  if (gp >= 32) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppBcast15, 0xa>(v[k], 0.0);
+  }
+  if (gp >= 64) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += dpp_f64<kDppBcast31, 0xc>(v[k], 0.0);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int64_t b = __double_as_longlong(v[k]);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), gp - 1);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), gp - 1);
+    v[k] = __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+  }
+}
+
+// Maximum over the 64 lanes, wave-uniform (NaN lanes are ignored, as by fmax).
+__device__ __forceinline__ double wave_max_dpp(double v) {
+  v = fmax(v, dpp_f64<kDppXor1>(v, v));
+  v = fmax(v, dpp_f64<kDppXor2>(v, v));
+  v = fmax(v, dpp_f64<kDppHalfMirror>(v, v));
+  v = fmax(v, dpp_f64<kDppMirror>(v, v));
+  v = fmax(v, dpp_f64<kDppBcast15, 0xa>(v, v));
+  v = fmax(v, dpp_f64<kDppBcast31, 0xc>(v, v));
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// A wave-uniform float64 moved into scalar registers (its value is the same in every lane;
+// this only frees the two vector registers that would otherwise hold it).
+__device__ __forceinline__ double uniform_f64(double v) {
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(b));
+  const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
 // Value of a float held in lane `lane` (lane must be wave-uniform).
 __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

@@ -67,9 +67,14 @@ struct BwdParams {
   void* workspace;  // [grid + reduce groups][r] float64 dq partials
 };
 
+// Column-chunked two-pass read (any width; also the merge when a row does not fit a tile).
 hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s);
-int online_max_units();
+// Register-tile read (online, two-pass or merge) for rows of at most tile_max_units() units
+// per lane.
+hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
+                       hipStream_t s);
+int tile_max_units();
 
 hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s);
 

@@ -1,20 +1,14 @@
-// The depth-mix read and the Phase-2 merge (LR-AttnRes paper §3.1/§3.3 and §3.4; AttnRes
+// The column-chunked read and merge (LR-AttnRes paper §3.1/§3.3 and §3.4; AttnRes
 // technical-report summary, "Method", for the two-phase schedule).
 //
-// Two kernel families, both one wavefront per token row:
+// k_read_two_pass, one wavefront per token row: the key slices of all n sources are loaded
+// and reduced (float64), the softmax is taken once, then the full rows are streamed in column
+// chunks with float32 accumulation. It handles any width, so it serves the rows that do not
+// fit a register tile (lrar_tile.hip), including the scalar-element path for wide unaligned
+// rows.
 //
-//   k_read_two_pass  scores first: the key slices of all n sources are loaded and reduced
-//                    (float64), the softmax is taken once, then the full rows are streamed in
-//                    column chunks with float32 accumulation. The key slice is touched twice
-//                    (once more in the value stream), which costs r/d extra reads that
-//                    normally hit in L2. Handles any d.
-//   k_read_online    one pass over the sources: each source row is loaded whole into
-//                    registers, its score is reduced, and an online-softmax accumulator is
-//                    rescaled in batches of B sources. Every byte is read once, which suits
-//                    r close to d; the whole row must fit in registers.
-//
-// With PRIOR the kernels merge Phase-1 statistics (m, l, acc) of earlier sources into the
-// softmax as one more term; that is lrar_merge.
+// With PRIOR the kernel merges Phase-1 statistics (m, l, acc) of earlier sources into the
+// softmax as one more term; that is lrar_merge for such rows.
 
 #include "lrar_device.h"
 #include "lrar_launch.h"
@@ -147,108 +141,6 @@ __global__ __launch_bounds__(kBlock) void k_read_two_pass(ReadParams p) {
   }
 }
 
-template <typename IO, int VEC, int NU, int B>
-__global__ __launch_bounds__(kBlock) void k_read_online(ReadParams p) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t step = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  const int nur = (p.d + VEC - 1) / VEC;
-  const int c0 = p.d - p.r;
-  const int ub = c0 / VEC;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; row < p.T;
-       row += step) {
-    float acc[NU][VEC];
-#pragma unroll
-    for (int k = 0; k < NU; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
-    double m_run = -INFINITY, l_run = 0.0, z_mine = 0.0;
-    for (int i = 0; i < p.n; i += B) {
-      const int nb = (p.n - i) < B ? (p.n - i) : B;
-      Unit<IO, VEC> un[B][NU];
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        if (b < nb) {
-          const IO* srow = static_cast<const IO*>(p.src.ptr[i + b]) + row * p.src.ld[i + b];
-#pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            const int u = lane + kWave * k;
-            if (u < nur) un[b][k].load(srow + u * VEC); else un[b][k].zero();
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < NU; ++k) un[b][k].zero();
-        }
-      }
-      double zb[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        double dot = 0.0, ss = 0.0;
-#pragma unroll
-        for (int k = 0; k < NU; ++k) {
-          const int u = lane + kWave * k;
-          if (u >= ub && u < nur) {
-            float x[VEC];
-            un[b][k].get(x);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const int col = u * VEC + e;
-              const double kv = (col >= c0) ? static_cast<double>(x[e]) : 0.0;
-              dot = fma(q_at(p.q, col, c0), kv, dot);
-              ss = fma(kv, kv, ss);
-            }
-          }
-        }
-        dot = wave_sum(dot);
-        ss = wave_sum(ss);
-        zb[b] = dot / sqrt(ss / p.r + p.eps);
-        if (lane == i + b) z_mine = zb[b];
-      }
-      double m_new = m_run;
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-        if (b < nb) m_new = fmax(m_new, zb[b]);
-      const double scale = exp(m_run - m_new);  // 0 on the first batch
-      l_run *= scale;
-      const float scale_f = static_cast<float>(scale);
-#pragma unroll
-      for (int k = 0; k < NU; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[k][e] *= scale_f;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        if (b < nb) {
-          const double eb = exp(zb[b] - m_new);
-          l_run += eb;
-          const float ef = static_cast<float>(eb);
-#pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            float x[VEC];
-            un[b][k].get(x);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(ef, x[e], acc[k][e]);
-          }
-        }
-      }
-      m_run = m_new;
-    }
-    const float inv = static_cast<float>(1.0 / l_run);
-    IO* out_row = static_cast<IO*>(p.out) + row * p.out_ld;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = lane + kWave * k;
-      if (u < nur) {
-        float y[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) y[e] = acc[k][e] * inv;
-        store_unit<IO, VEC>(out_row + u * VEC, y);
-      }
-    }
-    if (p.alpha != nullptr && lane < p.n)
-      p.alpha[row * p.alpha_ld + lane] = static_cast<float>(exp(z_mine - m_run) / l_run);
-  }
-}
-
 // ---- launchers ---------------------------------------------------------------------------------
 
 namespace {
@@ -272,37 +164,11 @@ hipError_t launch_two_pass_t(const ReadParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename IO, int VEC>
-hipError_t launch_online_t(const ReadParams& p, hipStream_t s) {
-  const int grid = grid_for_rows(p.T);
-  const int nur = (p.d + VEC - 1) / VEC;
-  const int nu = (nur + kWave - 1) / kWave;
-  if (nu <= 1)
-    hipLaunchKernelGGL((k_read_online<IO, VEC, 1, 8>), dim3(grid), dim3(kBlock), 0, s, p);
-  else if (nu <= 2)
-    hipLaunchKernelGGL((k_read_online<IO, VEC, 2, 4>), dim3(grid), dim3(kBlock), 0, s, p);
-  else if (nu <= 4)
-    hipLaunchKernelGGL((k_read_online<IO, VEC, 4, 4>), dim3(grid), dim3(kBlock), 0, s, p);
-  else if (nu <= 8)
-    hipLaunchKernelGGL((k_read_online<IO, VEC, 8, 2>), dim3(grid), dim3(kBlock), 0, s, p);
-  else if (nu <= 16)
-    hipLaunchKernelGGL((k_read_online<IO, VEC, 16, 1>), dim3(grid), dim3(kBlock), 0, s, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 }  // namespace
-
-int online_max_units() { return 16; }
 
 hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s) {
-  if (kind == ReadKind::kOnline) {
-    if (io_bf16) return vec > 1 ? launch_online_t<bf16_bits, 8>(p, s) : launch_online_t<bf16_bits, 1>(p, s);
-    return vec > 1 ? launch_online_t<float, 4>(p, s) : launch_online_t<float, 1>(p, s);
-  }
-  if (kind == ReadKind::kTwoPass) {
+  if (kind == ReadKind::kTwoPass || kind == ReadKind::kOnline) {
     if (io_bf16) return vec > 1 ? launch_two_pass_t<bf16_bits, 8, false, float>(p, s)
                                 : launch_two_pass_t<bf16_bits, 1, false, float>(p, s);
     return vec > 1 ? launch_two_pass_t<float, 4, false, float>(p, s)
