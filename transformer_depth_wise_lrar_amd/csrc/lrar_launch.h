@@ -78,6 +78,15 @@ int tile_max_units();
 
 hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s);
 
+// Phase 1 on whole workgroups (lrar_stats_tile.hip): vector path, at most kStatsMaxSrc sources,
+// queries in groups of stats_tile_query_group() (0 if one query's LDS slice does not fit).
+constexpr int kStatsMaxSrc = 8;
+constexpr int kStatsMaxQ = 12;
+constexpr int kStatsKeySlots = 2;  // key unit slots loaded together per source
+int stats_tile_query_group(int d, int r, int vec);
+hipError_t launch_stats_tile(const StatsParams& p, int io_bf16, int acc_bf16, int qg,
+                             hipStream_t s);
+
 // Backward: grid size (workgroups) used for T rows, and the launcher.
 int backward_grid(int64_t T);
 int backward_max_units();

@@ -2,7 +2,9 @@
 // a block's static queries are batched into one inter-block attention over the cached block
 // representations; LR-AttnRes paper §3.4: the sliced key keeps this valid).
 //
-// One wavefront per token row. For a group of up to QB queries the kernel
+// k_stats serves the shapes the workgroup kernel of lrar_stats_tile.hip does not (the
+// scalar-element path, more than kStatsMaxSrc sources). One wavefront per token row. For a
+// group of up to QB queries the kernel
 //   1. reduces, per source, the key's sum of squares once and its dot product with every
 //      query of the group (float64), so each key element is loaded once per group;
 //   2. forms per query m = max z (rounded to float32), e_i = exp(z_i - m), l = sum e_i;
@@ -190,6 +192,10 @@ hipError_t launch_stats_t(const StatsParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s) {
+  if (vec > 1 && p.n <= kStatsMaxSrc) {
+    const int qg = stats_tile_query_group(p.d, p.r, vec);
+    if (qg >= 1) return launch_stats_tile(p, io_bf16, acc_bf16, qg, s);
+  }
   if (io_bf16) {
     if (acc_bf16) return vec > 1 ? launch_stats_t<bf16_bits, 8, bf16_bits>(p, s)
                                  : launch_stats_t<bf16_bits, 1, bf16_bits>(p, s);

@@ -1,0 +1,255 @@
+// Phase 1 of the two-phase block schedule on whole workgroups (AttnRes technical-report
+// summary, "Method": a block's static site queries are batched into one inter-block attention
+// over the cached block representations; LR-AttnRes paper §3.4: the sliced key keeps this
+// valid).
+//
+// For up to kStatsMaxSrc cached sources and a group of up to kStatsMaxQ site queries:
+//   * one 768-thread workgroup per CU (12 wavefronts) shares one LDS copy of the group's
+//     queries, laid out from the first key unit's column (columns of that unit before the key
+//     hold zero), so each key element is dotted with every query of the group from LDS;
+//   * each wave takes one token row at a time, rows dealt out in bands over all waves;
+//   * score pass: per source, the key units are loaded together, float64 partial sums of
+//     q_s . k for every query s and of k . k accumulate per lane, and the (queries + 1) sums
+//     are reduced by interleaved DPP chains; lane i keeps z_si;
+//   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
+//     l = sum_i e_si (float64 on the lanes), written once per row;
+//   * value pass: the row is walked in chunks of 64 units; each chunk of every source is loaded
+//     once and folded into two queries' accumulators at a time, which are written straight out
+//     (acc = sum_i e_si o_i, not normalised). The other waves of the CU keep HBM busy while a
+//     wave folds.
+// Each cached source row is read from HBM once per query group (its key again from L2), and
+// every accumulator element is written once.
+
+#include "lrar_device.h"
+#include "lrar_launch.h"
+
+namespace lrar {
+
+namespace {
+
+constexpr int kStatsBlock = 768;
+constexpr int kStatsWaves = kStatsBlock / kWave;
+
+}  // namespace
+
+template <typename IO, int VEC, typename ACC>
+__global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nqg) {
+  extern __shared__ float q_lds[];  // [nqg][rq]
+  // Scores of the wave's current row: z[s][i] for query s, source i.
+  __shared__ double z_lds[kStatsWaves][kStatsMaxQ][kStatsMaxSrc];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kStatsWaves + threadIdx.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kStatsWaves;
+  const int n = p.n;
+  const int nur = (p.d + VEC - 1) / VEC;
+  const int nslot = (nur + kWave - 1) / kWave;  // unit slots per lane
+  const int c0 = p.d - p.r;
+  const int ub = c0 / VEC;
+  const int rq = p.d - ub * VEC;  // staged query columns
+  const int k_lo = ub / kWave;    // first slot that can hold key units
+  for (int idx = threadIdx.x; idx < nqg * rq; idx += kStatsBlock) {
+    const int s = idx / rq;
+    const int col = ub * VEC + (idx - s * rq);
+    q_lds[idx] = col >= c0 ? p.q[static_cast<int64_t>(q0 + s) * p.q_ld + (col - c0)] : 0.f;
+  }
+  __syncthreads();
+
+  for (int64_t row = wave; row < p.T; row += nwaves) {
+    // ---- score pass: z_si of every (query, source) pair into z_lds
+    for (int i = 0; i < n; ++i) {
+      const IO* rowp = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
+      double red[kStatsMaxQ + 1];
+#pragma unroll
+      for (int s = 0; s <= kStatsMaxQ; ++s) red[s] = 0.0;
+      for (int kb = k_lo; kb < nslot; kb += kStatsKeySlots) {
+        Unit<IO, VEC> ku[kStatsKeySlots];
+#pragma unroll
+        for (int t = 0; t < kStatsKeySlots; ++t) {
+          const int u = lane + kWave * (kb + t);
+          if (kb + t < nslot && u >= ub && u < nur) ku[t].load_cached(rowp + u * VEC);
+          else ku[t].zero();
+        }
+#pragma unroll
+        for (int t = 0; t < kStatsKeySlots; ++t) {
+          const int u = lane + kWave * (kb + t);
+          if (kb + t < nslot && u >= ub && u < nur) {
+            float x[VEC];
+            ku[t].get(x);
+            double kv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              kv[e] = (u * VEC + e) >= c0 ? static_cast<double>(x[e]) : 0.0;
+              red[kStatsMaxQ] = fma(kv[e], kv[e], red[kStatsMaxQ]);
+            }
+            const float* qc = q_lds + (u - ub) * VEC;
+            // One query at a time: the scheduling barrier keeps the query values of later
+            // queries from being read ahead into registers.
+#pragma unroll
+            for (int s = 0; s < kStatsMaxQ; ++s) {
+              if (s < nqg) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                  red[s] = fma(static_cast<double>(qc[s * rq + e]), kv[e], red[s]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+      wave_sums_dpp(red);
+      const double rho = sqrt(red[kStatsMaxQ] / p.r + p.eps);
+#pragma unroll
+      for (int s = 0; s < kStatsMaxQ; ++s)
+        if (lane == s && s < nqg) z_lds[wv][s][i] = red[s] / rho;
+    }
+
+    // ---- statistics per query (lanes = sources)
+    float ew[kStatsMaxQ];
+#pragma unroll
+    for (int s = 0; s < kStatsMaxQ; ++s) {
+      ew[s] = 0.f;
+      if (s < nqg) {
+        const double z = lane < n ? z_lds[wv][s][lane] : -INFINITY;
+        const double m = wave_max_dpp(z);
+        const float mf = static_cast<float>(m);
+        const double e = lane < n ? exp(z - static_cast<double>(mf)) : 0.0;
+        const double L = wave_sum_dpp(e);
+        ew[s] = static_cast<float>(e);
+        if (lane == 0) {
+          int64_t off = static_cast<int64_t>(q0 + s) * p.ml_ld + row;
+          asm volatile("" : "+v"(off));  // computed here, not hoisted out of the row loop
+          p.m[off] = mf;
+          p.l[off] = static_cast<float>(L);
+        }
+      }
+    }
+
+    // ---- value pass: chunks of 64 units, every source's part of a chunk loaded together
+    Unit<IO, VEC> buf[kStatsMaxSrc];
+    const auto load_chunk = [&](Unit<IO, VEC> (&b)[kStatsMaxSrc], int c) {
+      const int u = lane + kWave * c;
+#pragma unroll
+      for (int i = 0; i < kStatsMaxSrc; ++i) {
+        if (i < n && u < nur)
+          b[i].load(static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i] + u * VEC);
+        else
+          b[i].zero();
+      }
+    };
+    const auto fold_chunk = [&](const Unit<IO, VEC> (&b)[kStatsMaxSrc], int c) {
+      const int u = lane + kWave * c;
+#pragma unroll
+      for (int s = 0; s < kStatsMaxQ; s += 2) {
+        if (s < nqg) {
+          float a0[VEC], a1[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) a0[e] = a1[e] = 0.f;
+          // The weights are broadcast from their lanes here, once per chunk: hoisting all
+          // (query, source) broadcasts out of the chunk loop would not fit in scalar registers.
+          float e0 = ew[s], e1 = ew[s + 1];
+          asm volatile("" : "+v"(e0), "+v"(e1));
+#pragma unroll
+          for (int i = 0; i < kStatsMaxSrc; ++i) {
+            if (i < n) {
+              const float w0 = lane_f32(e0, i);
+              const float w1 = lane_f32(e1, i);
+              float x[VEC];
+              b[i].get(x);
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) {
+                a0[e] = fmaf(w0, x[e], a0[e]);
+                a1[e] = fmaf(w1, x[e], a1[e]);
+              }
+            }
+          }
+          if (u < nur) {
+            int64_t off = static_cast<int64_t>(q0 + s) * p.acc_qstride + row * p.acc_ld;
+            asm volatile("" : "+v"(off));
+            ACC* d0 = static_cast<ACC*>(p.acc) + off + u * VEC;
+            store_acc<ACC, VEC>(d0, a0);
+            if (s + 1 < nqg) store_acc<ACC, VEC>(d0 + p.acc_qstride, a1);
+          }
+        }
+      }
+    };
+    for (int c = 0; c < nslot; ++c) {
+      load_chunk(buf, c);
+      fold_chunk(buf, c);
+    }
+  }
+}
+
+namespace {
+
+int device_cus_stats() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Largest LDS allocation one workgroup may use on this device.
+size_t lds_limit() {
+  static size_t lim = 0;
+  if (lim == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0)
+      lim = static_cast<size_t>(v);
+    else
+      lim = 64 * 1024;
+  }
+  return lim;
+}
+
+template <typename IO, int VEC, typename ACC>
+hipError_t launch_stats_tile_t(const StatsParams& p, int qg, hipStream_t s) {
+  auto kern = k_stats_tile<IO, VEC, ACC>;
+  const int ub = (p.d - p.r) / VEC;
+  const int rq = p.d - ub * VEC;
+  for (int q0 = 0; q0 < p.nq; q0 += qg) {
+    const int nqg = (p.nq - q0) < qg ? (p.nq - q0) : qg;
+    const size_t lds = static_cast<size_t>(nqg) * rq * sizeof(float);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStatsBlock, lds) !=
+            hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    const int64_t need = (p.T + kStatsWaves - 1) / kStatsWaves;
+    int64_t blocks = static_cast<int64_t>(per_cu) * device_cus_stats();
+    if (blocks > need) blocks = need;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kStatsBlock), lds, s, p,
+                       q0, nqg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+int stats_tile_query_group(int d, int r, int vec) {
+  const int ub = (d - r) / vec;
+  const size_t per_q = static_cast<size_t>(d - ub * vec) * sizeof(float);
+  size_t fit = lds_limit() / per_q;
+  if (fit > static_cast<size_t>(kStatsMaxQ)) fit = kStatsMaxQ;
+  return static_cast<int>(fit);
+}
+
+hipError_t launch_stats_tile(const StatsParams& p, int io_bf16, int acc_bf16, int qg,
+                             hipStream_t s) {
+  if (io_bf16) return acc_bf16 ? launch_stats_tile_t<bf16_bits, 8, bf16_bits>(p, qg, s)
+                               : launch_stats_tile_t<bf16_bits, 8, float>(p, qg, s);
+  return acc_bf16 ? launch_stats_tile_t<float, 4, bf16_bits>(p, qg, s)
+                  : launch_stats_tile_t<float, 4, float>(p, qg, s);
+}
+
+}  // namespace lrar
