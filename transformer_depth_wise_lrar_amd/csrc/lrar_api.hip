@@ -112,8 +112,8 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
   if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
   const int use_vec = vec_ok ? vec : 1;
   const int nur = (d + use_vec - 1) / use_vec;
-  // A row fits a register tile when each lane holds at most tile_max_units() units of it.
-  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_units();
+  // A row fits a register tile when it has at most tile_max_chunks() chunks of 64 units.
+  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_chunks();
   lrar::ReadKind kind;
   if (variant == LRAR_VARIANT_ONLINE) {
     if (!tile_fits)
@@ -242,7 +242,7 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
   p.l_out = l_out;
   const int use_vec = vec_ok ? vec : 1;
   const int nur = (d + use_vec - 1) / use_vec;
-  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_units();
+  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_chunks();
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e =
       tile_fits ? lrar::launch_tile(p, lrar::ReadKind::kMerge, io == LRAR_BF16, use_vec,

@@ -70,11 +70,11 @@ struct BwdParams {
 // Column-chunked two-pass read (any width; also the merge when a row does not fit a tile).
 hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s);
-// Register-tile read (online, two-pass or merge) for rows of at most tile_max_units() units
-// per lane.
+// Register-tile read (online, two-pass or merge) for rows of at most tile_max_chunks() chunks
+// of 64 units.
 hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s);
-int tile_max_units();
+int tile_max_chunks();
 
 hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s);
 

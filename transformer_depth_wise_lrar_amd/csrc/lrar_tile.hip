@@ -148,6 +148,10 @@ struct TileGeom {
   int64_t r0;  // first row of the tile
   int nrow;    // rows of the tile that exist (<= R)
   int lane, nur, ub, c0, r;
+  int w, wpr;  // this wave's place among the wpr waves that share a row
+  // Unit held in slot k: the row is cut into chunks of 64 units and chunk c belongs to wave
+  // c % wpr, so the waves of a row share the chunks (and the key) evenly.
+  __device__ __forceinline__ int unit(int k) const { return (k * wpr + w) * kWave + lane; }
 };
 
 // Loads one source's tile. KEYS_ONLY: only the key (the spread pieces, or the key units when
@@ -166,7 +170,7 @@ __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
     if constexpr (!(KEYS_ONLY && KS > 0)) {
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
-        const int u = g.lane + kWave * k;
+        const int u = g.unit(k);
         const bool want = j < g.nrow && u < g.nur && (!KEYS_ONLY || u >= g.ub);
         if (want) st.t.u[j][k].load(rowp + u * VEC);
         else st.t.u[j][k].zero();
@@ -186,7 +190,7 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
   ss = 0.0;
 #pragma unroll
   for (int k = NU - TU; k < NU; ++k) {
-    const int u = g.lane + kWave * k;
+    const int u = g.unit(k);
     if (u >= g.ub && u < g.nur) {
       float x[VEC];
       row[k].get(x);
@@ -253,14 +257,21 @@ constexpr int ks_slots(int ks) { return ks > 0 ? ks : 1; }
 
 }  // namespace
 
-template <typename IO, int VEC, int NU, int TU, int KS, int R, int PF, int MODE, typename ACC>
+template <typename IO, int VEC, int NU, int TU, int KS, int R, int PF, int WPR, int MODE,
+          typename ACC>
 __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
+  static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   extern __shared__ float q_lds[];
+  // Partial key sums of the waves that share a row (two slots, alternating by source).
+  __shared__ double xch[2][kWavesPerBlock][2 * R];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+  const int wib = threadIdx.x / kWave;  // wave in block
+  const int64_t group = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wib) / WPR;
   const int n = p.n;
   TileGeom g;
   g.lane = lane;
+  g.w = wib % WPR;
+  g.wpr = WPR;
   g.nur = (p.d + VEC - 1) / VEC;
   g.c0 = p.d - p.r;
   g.ub = g.c0 / VEC;
@@ -294,11 +305,13 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
     while (gp < used) gp <<= 1;
   }
 
-  // Tiles are dealt out in bands: in its k-th step wave w takes tile w + k * nwaves, so the
-  // resident waves together read one contiguous window of rows of every source at a time.
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  // Tiles are dealt out in bands: in its k-th step row group w takes tile w + k * ngroups, so
+  // the resident waves together read one contiguous window of rows of every source at a time.
+  // (All waves of a group see the same tiles, so they meet the same barriers.)
+  const int64_t ngroups = static_cast<int64_t>(gridDim.x) * kWavesPerBlock / WPR;
   const int64_t ntiles = (p.T + R - 1) / R;
-  for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
+  int parity = 0;
+  for (int64_t tile = group; tile < ntiles; tile += ngroups) {
     g.r0 = tile * R;
     g.nrow = (p.T - g.r0) < R ? static_cast<int>(p.T - g.r0) : R;
     const int64_t r0 = g.r0;
@@ -328,7 +341,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
           const ACC* prow = static_cast<const ACC*>(p.acc) + (r0 + j) * p.acc_ld;
 #pragma unroll
           for (int k = 0; k < NU; ++k) {
-            const int u = lane + kWave * k;
+            const int u = g.unit(k);
             if (u < g.nur) load_acc<ACC, VEC>(prow + u * VEC, acc[j][k]);
           }
         }
@@ -350,8 +363,30 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
         else
           key_partial_units<TU>(st.t.u[j], q_lds, g, red[2 * j], red[2 * j + 1]);
       }
-      if constexpr (KS > 0) lanes_sums_dpp(red, gp);
-      else wave_sums_dpp(red);
+      if constexpr (KS > 0) {
+        lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
+      } else {
+        wave_sums_dpp(red);
+        if constexpr (WPR > 1) {
+          // add the partial sums of the row's other waves, in a fixed order (so every wave
+          // of the row gets bitwise the same score)
+          double mine = red[0];
+#pragma unroll
+          for (int j = 1; j < 2 * R; ++j)
+            if (lane == j) mine = red[j];
+          if (lane < 2 * R) xch[parity][wib][lane] = mine;
+          __syncthreads();
+          const int base = wib - g.w;
+#pragma unroll
+          for (int j = 0; j < 2 * R; ++j) {
+            double t = xch[parity][base][j];
+#pragma unroll
+            for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][j];
+            red[j] = t;
+          }
+          parity ^= 1;
+        }
+      }
       return row_scores_to_lanes<R>(red, lane, p.r, p.eps);
     };
 
@@ -459,7 +494,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
       IO* orow = static_cast<IO*>(p.out) + row * p.out_ld;
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
-        const int u = lane + kWave * k;
+        const int u = g.unit(k);
         if (u < g.nur) {
           float y[VEC];
 #pragma unroll
@@ -467,14 +502,14 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
           store_unit<IO, VEC>(orow + u * VEC, y);
         }
       }
-      if (p.alpha != nullptr) {
+      if (p.alpha != nullptr && g.w == 0) {
         double a = zk[j];
         if constexpr (MODE != kTileTwoPass) a = exp(zk[j] - lane_f64(mref, j)) / lane_f64(lsum, j);
         if (lane < n) p.alpha[row * p.alpha_ld + lane] = static_cast<float>(a);
       }
     }
     if constexpr (MODE == kTileMerge) {
-      if (lane < nrow) {
+      if (lane < nrow && g.w == 0) {
         const float mf = static_cast<float>(mtop);
         if (p.m_out) p.m_out[r0 + lane] = mf;
         if (p.l_out) p.l_out[r0 + lane] = static_cast<float>(lsum * exp(mref - static_cast<double>(mf)));
@@ -514,11 +549,11 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
 constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
 #endif
 
-template <typename IO, int VEC, int NU, int TU, int KS, int MODE, typename ACC>
+template <typename IO, int VEC, int NU, int TU, int KS, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
   constexpr int R = tile_rows(NU);
   constexpr int PF = tile_prefetch(NU);
-  auto kern = k_read_tile<IO, VEC, NU, TU, KS, R, PF, MODE, ACC>;
+  auto kern = k_read_tile<IO, VEC, NU, TU, KS, R, PF, WPR, MODE, ACC>;
   const int ub = (p.d - p.r) / VEC;
   const size_t lds = KS > 0 ? 0 : static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
   // Workgroups per CU for this instantiation and LDS size (cached: the query is not free).
@@ -533,49 +568,56 @@ hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
     cached_lds = lds;
   }
   const int per_cu = cached_per_cu;
-  // As many waves as fit at once, trimmed so that no wave gets more tiles than needed: the
-  // grid runs in one round and the waves' tile counts differ by at most one.
-  const int64_t resident_waves = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock;
+  // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
+  // the grid runs in one round and the groups' tile counts differ by at most one.
+  const int64_t resident = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock / WPR;
   const int64_t tiles = (p.T + R - 1) / R;
-  const int64_t per_wave = (tiles + resident_waves - 1) / resident_waves;
-  const int64_t waves = (tiles + per_wave - 1) / per_wave;
-  const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t per_group = (tiles + resident - 1) / resident;
+  const int64_t groups = (tiles + per_group - 1) / per_group;
+  constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
+  const int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p);
   return hipGetLastError();
 }
 
 // Key path: spread pieces of KS elements when the key is short and its start is KS-aligned;
-// otherwise the row units, with TU = 1 when the key starts in the last unit slot.
-template <typename IO, int VEC, int NU, int MODE, typename ACC>
+// otherwise the row units, with TU = 1 when every key chunk lands in a wave's last slot.
+template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, hipStream_t s) {
   const int c0 = p.d - p.r;
   if constexpr (VEC > 1) {
-    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, MODE, ACC>(p, s);
-    if (p.r <= 2 * kWave && c0 % 2 == 0) return launch_tile_t<IO, VEC, NU, 1, 2, MODE, ACC>(p, s);
-    if (p.r <= 4 * kWave && c0 % 4 == 0) return launch_tile_t<IO, VEC, NU, 1, 4, MODE, ACC>(p, s);
+    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, WPR, MODE, ACC>(p, s);
+    if (p.r <= 2 * kWave && c0 % 2 == 0)
+      return launch_tile_t<IO, VEC, NU, 1, 2, WPR, MODE, ACC>(p, s);
+    if (p.r <= 4 * kWave && c0 % 4 == 0)
+      return launch_tile_t<IO, VEC, NU, 1, 4, WPR, MODE, ACC>(p, s);
   }
-  const int ub = c0 / VEC;
+  const int first_key_chunk = (c0 / VEC) / kWave;
   if constexpr (NU > 1) {
-    if (ub >= kWave * (NU - 1)) return launch_tile_t<IO, VEC, NU, 1, 0, MODE, ACC>(p, s);
+    if (first_key_chunk / WPR >= NU - 1)
+      return launch_tile_t<IO, VEC, NU, 1, 0, WPR, MODE, ACC>(p, s);
   }
-  return launch_tile_t<IO, VEC, NU, NU, 0, MODE, ACC>(p, s);
+  return launch_tile_t<IO, VEC, NU, NU, 0, WPR, MODE, ACC>(p, s);
 }
 
+// Rows of up to 4 chunks of 64 units are held by one wave; wider rows by the 4 waves of a
+// workgroup, each taking every fourth chunk.
 template <typename IO, int VEC, int MODE, typename ACC>
 hipError_t launch_tile_nu(const ReadParams& p, hipStream_t s) {
   const int nur = (p.d + VEC - 1) / VEC;
-  const int nu = (nur + kWave - 1) / kWave;
-  if (nu <= 1) return launch_tile_key<IO, VEC, 1, MODE, ACC>(p, s);
-  if (nu <= 2) return launch_tile_key<IO, VEC, 2, MODE, ACC>(p, s);
-  if (nu <= 4) return launch_tile_key<IO, VEC, 4, MODE, ACC>(p, s);
-  if (nu <= 8) return launch_tile_key<IO, VEC, 8, MODE, ACC>(p, s);
-  if (nu <= 16) return launch_tile_key<IO, VEC, 16, MODE, ACC>(p, s);
+  const int chunks = (nur + kWave - 1) / kWave;
+  if (chunks <= 1) return launch_tile_key<IO, VEC, 1, 1, MODE, ACC>(p, s);
+  if (chunks <= 2) return launch_tile_key<IO, VEC, 2, 1, MODE, ACC>(p, s);
+  if (chunks <= 4) return launch_tile_key<IO, VEC, 4, 1, MODE, ACC>(p, s);
+  if (chunks <= 8) return launch_tile_key<IO, VEC, 2, 4, MODE, ACC>(p, s);
+  if (chunks <= 16) return launch_tile_key<IO, VEC, 4, 4, MODE, ACC>(p, s);
+  if (chunks <= 32) return launch_tile_key<IO, VEC, 8, 4, MODE, ACC>(p, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int tile_max_units() { return 16; }
+int tile_max_chunks() { return 32; }
 
 hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s) {
