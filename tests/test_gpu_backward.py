@@ -71,3 +71,11 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(dqa, dqb)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("d,r,io", [(4096, 512, "f32"), (12288, 256, "bf16"),
+                                    (16384, 16384, "bf16"), (8192, 4000, "f32")])
+def test_backward_wide_rows(d, r, io):
+    """Rows shared by the four waves of a workgroup, up to the widest tile (32 chunks)."""
+    srcs = sources(3, 19, d, io, seed=250, scale=(0.5, 4.0))
+    check_backward(srcs, query(r, seed=251), r, 1e-6, False, f"wide d{d} r{r} {io}", seed=252)

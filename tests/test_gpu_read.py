@@ -179,3 +179,14 @@ def test_key_paths(io, r):
     for n in (3, 10):
         for variant in VARIANTS:
             run_and_check(srcs[:n], q, r, 1e-6, variant, f"key path r={r} n={n}")
+
+
+@pytest.mark.parametrize("d,r,io", [(4096, 512, "f32"), (8192, 8192, "f32"), (12288, 64, "bf16"),
+                                    (12288, 3000, "bf16"), (16384, 16384, "bf16")])
+def test_wide_rows(d, r, io):
+    """Rows shared by the four waves of a workgroup, up to the widest tile (32 chunks), for
+    every variant and the merge."""
+    srcs = sources(4, 21, d, io, seed=95, scale=(0.5, 4.0))
+    q = query(r, seed=96)
+    for variant in VARIANTS:
+        run_and_check(srcs, q, r, 1e-6, variant, f"wide d{d} r={r}")

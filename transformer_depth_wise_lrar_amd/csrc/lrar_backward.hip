@@ -1,4 +1,5 @@
-// Backward of the depth-mix read (LR-AttnRes paper App. B.3: Lemma 2 gives
+// Backward of the depth-mix read, scalar-element path and the dq reduction (LR-AttnRes paper
+// App. B.3: Lemma 2 gives
 // dL/do_i = alpha_i g + alpha_i <g, o_i - h> grad z_i; Corollary 2.1 gives the slice-RMS
 // gradient grad z_i = P_r^T (q - z_i kbar_i / r) / rho_i; the query gradient follows from
 // z_i = q . kbar_i). Each source slot is an independent input, as in the paper.
@@ -289,7 +290,7 @@ int backward_max_units() { return 16; }
 bool backward_supported(int d, int r, int vec) {
   const int nur = (d + vec - 1) / vec;
   const int nu = (nur + kWave - 1) / kWave;
-  return vec > 1 ? nu <= 16 : nu <= 32;
+  return vec > 1 ? nu <= backward_tile_max_chunks() : nu <= 32;
 }
 
 // Workspace: [grid][r] float64 workgroup partials, then [kReduceGroups][r] float64.
@@ -299,14 +300,19 @@ size_t backward_workspace(int64_t T, int r) {
 }
 
 hipError_t launch_backward(const BwdParams& p, int io_bf16, int vec, hipStream_t s) {
-  const int grid = backward_grid(p.T);
+  // The workspace holds backward_grid(T) workgroup rows; a launch may fill fewer of them.
+  const int max_grid = backward_grid(p.T);
+  int grid = max_grid;
   double* block_dq = static_cast<double*>(p.workspace);
-  double* level2 = block_dq + static_cast<int64_t>(grid) * p.r;
+  double* level2 = block_dq + static_cast<int64_t>(max_grid) * p.r;
   hipError_t e;
-  if (io_bf16)
-    e = vec > 1 ? launch_bwd_t<bf16_bits, 8>(p, block_dq, grid, s) : launch_bwd_t<bf16_bits, 1>(p, block_dq, grid, s);
-  else
-    e = vec > 1 ? launch_bwd_t<float, 4>(p, block_dq, grid, s) : launch_bwd_t<float, 1>(p, block_dq, grid, s);
+  if (vec > 1) {
+    // the vector path runs on row tiles (lrar_backward_tile.hip)
+    e = launch_backward_tile(p, io_bf16, block_dq, max_grid, &grid, s);
+  } else {
+    e = io_bf16 ? launch_bwd_t<bf16_bits, 1>(p, block_dq, grid, s)
+                : launch_bwd_t<float, 1>(p, block_dq, grid, s);
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dq_reduce1, dim3((p.r + kWave - 1) / kWave, kReduceGroups), dim3(kBlock), 0, s,
                      block_dq, grid, p.r, level2);

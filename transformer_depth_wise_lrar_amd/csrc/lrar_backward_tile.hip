@@ -1,0 +1,318 @@
+// Backward of the depth-mix read on row tiles (LR-AttnRes paper App. B.3: Lemma 2 gives
+// dL/do_i = alpha_i g + alpha_i <g, o_i - h> grad z_i; Corollary 2.1 gives the slice-RMS
+// gradient grad z_i = P_r^T (q - z_i kbar_i / r) / rho_i; the query gradient follows from
+// z_i = q . kbar_i). Each source slot is an independent input, as in the paper.
+//
+// A row group (one wave, or the four waves of a workgroup for wide rows, each holding every
+// fourth chunk of 64 units as in lrar_tile.hip) takes one token row at a time, rows dealt out
+// in bands:
+//   pass A  the upstream gradient g of the row is loaded once into registers; the sources
+//           stream through a prefetch ring and, from each row, the float64 sums q . k, k . k
+//           and s_i = <g, o_i> are reduced (DPP, then across the row's waves through LDS in a
+//           fixed order); lane i keeps z_i, rho_i, s_i;
+//   then    alpha = softmax(z), sbar = sum_j alpha_j s_j, dz_i = alpha_i (s_i - sbar), which
+//           equals alpha_i <g, o_i - h>;
+//   pass B  dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns
+//           (the key units are read again, from L2), written as float32 (or added to the
+//           existing gradient); dz_i k_i / rho_i accumulates into per-lane dq partials kept in
+//           registers across the group's rows.
+// The dq partials of a workgroup are combined in a fixed order and written as one float64 row
+// of the workspace; the reduction kernels of lrar_backward.hip then sum the workgroups' rows in
+// a fixed order, so dq is bitwise reproducible.
+
+#include "lrar_device.h"
+#include "lrar_launch.h"
+#include "lrar_tile.h"
+
+namespace lrar {
+
+template <typename IO, int VEC, int NU, int TU, int WPR>
+__global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* __restrict__ block_dq) {
+  static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
+  constexpr int PF = 2;
+  constexpr int K0 = NU - TU;  // first unit slot that may hold key columns
+  extern __shared__ float q_lds[];
+  __shared__ double xch[2][kWavesPerBlock][3];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wib = threadIdx.x / kWave;
+  const int64_t group = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wib) / WPR;
+  const int64_t ngroups = static_cast<int64_t>(gridDim.x) * kWavesPerBlock / WPR;
+  const int n = p.n;
+  TileGeom g;
+  g.lane = lane;
+  g.w = wib % WPR;
+  g.wpr = WPR;
+  g.nur = (p.d + VEC - 1) / VEC;
+  g.c0 = p.d - p.r;
+  g.ub = g.c0 / VEC;
+  g.r = p.r;
+  for (int k = threadIdx.x; k < p.d - g.ub * VEC; k += kBlock) {
+    const int col = g.ub * VEC + k;
+    q_lds[k] = col >= g.c0 ? p.q[col - g.c0] : 0.f;
+  }
+  __syncthreads();
+
+  float dqa[TU][VEC];
+#pragma unroll
+  for (int t = 0; t < TU; ++t)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dqa[t][e] = 0.f;
+
+  int parity = 0;
+  const auto src_base = [&](int i) { return static_cast<const IO*>(p.src.ptr[i]); };
+  for (int64_t row = group; row < p.T; row += ngroups) {
+    g.r0 = row;
+    g.nrow = 1;
+    // upstream gradient of the row
+    float gr[NU][VEC];
+    const float* grow = p.dout + row * p.dout_ld;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = g.unit(k);
+      if (u < g.nur) {
+        load_f32<VEC>(grow + u * VEC, gr[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) gr[k][e] = 0.f;
+      }
+    }
+
+    // ---- pass A: z_i, rho_i, s_i (lane i)
+    double zi = 0.0, rhoi = 1.0, si = 0.0;
+    Stage<IO, VEC, NU, 1, 0> ring[PF + 1];
+    const auto fold_a = [&](const Stage<IO, VEC, NU, 1, 0>& st, int i) {
+      double red[3];
+      key_partial_units<TU>(st.t.u[0], q_lds, g, red[0], red[1]);
+      double s = 0.0;
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        float x[VEC];
+        st.t.u[0][k].get(x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          // the float64 copy of g stays local to the product (hoisting it out of the source
+          // loop would double g's register footprint)
+          float gv = gr[k][e];
+          asm volatile("" : "+v"(gv));
+          s = fma(static_cast<double>(gv), static_cast<double>(x[e]), s);
+        }
+      }
+      red[2] = s;
+      wave_sums_dpp(red);
+      if constexpr (WPR > 1) {
+        double mine = lane == 0 ? red[0] : (lane == 1 ? red[1] : red[2]);
+        if (lane < 3) xch[parity][wib][lane] = mine;
+        __syncthreads();
+        const int base = wib - g.w;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          double t = xch[parity][base][j];
+#pragma unroll
+          for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][j];
+          red[j] = t;
+        }
+        parity ^= 1;
+      }
+      const double rho = sqrt(red[1] / p.r + p.eps);
+      if (lane == i) {
+        zi = red[0] / rho;
+        rhoi = rho;
+        si = red[2];
+      }
+    };
+#pragma unroll
+    for (int b = 0; b < PF; ++b)
+      if (b < n) load_stage<false>(ring[b], src_base(b), p.src.ld[b], g);
+    for (int i0 = 0; i0 < n; i0 += PF + 1) {
+#pragma unroll
+      for (int b = 0; b <= PF; ++b) {
+        const int i = i0 + b;
+        if (i < n) {
+          if (i + PF < n)
+            load_stage<false>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
+          fold_a(ring[b], i);
+        }
+      }
+    }
+
+    // ---- weights and score gradients (lanes = sources)
+    const double m = wave_max_dpp(lane < n ? zi : -INFINITY);
+    const double ex = lane < n ? exp(zi - m) : 0.0;
+    const double a = ex / wave_sum_dpp(ex);
+    const double sbar = wave_sum_dpp(lane < n ? a * si : 0.0);
+    const double dz = a * (si - sbar);
+    const float af = static_cast<float>(a);
+    const float c1f = static_cast<float>(dz / rhoi);                          // dz / rho
+    const float c2f = static_cast<float>(dz * zi / (p.r * rhoi * rhoi));      // dz z / (r rho^2)
+
+    // ---- pass B: source gradients (the key units stream through the ring again)
+    const auto store_b = [&](const Stage<IO, VEC, NU, 1, 0>& st, int i) {
+      const float ai = lane_f32(af, i);
+      const float c1 = lane_f32(c1f, i);
+      const float c2 = lane_f32(c2f, i);
+      float* drow = p.dsrc.ptr[i] + row * p.dsrc.ld[i];
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = g.unit(k);
+        if (u < g.nur) {
+          float v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];
+          if (k >= K0 && u >= g.ub) {
+            float x[VEC];
+            st.t.u[0][k].get(x);
+            const float* qv = q_lds + (u - g.ub) * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              if (u * VEC + e >= g.c0) {
+                v[e] += c1 * qv[e] - c2 * x[e];
+                dqa[k >= K0 ? k - K0 : 0][e] = fmaf(c1, x[e], dqa[k >= K0 ? k - K0 : 0][e]);
+              }
+            }
+          }
+          if (p.accumulate) {
+            float old[VEC];
+            load_f32<VEC>(drow + u * VEC, old);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] += old[e];
+          }
+          store_unit<float, VEC>(drow + u * VEC, v);
+        }
+      }
+    };
+#pragma unroll
+    for (int b = 0; b < PF; ++b)
+      if (b < n) load_stage<true>(ring[b], src_base(b), p.src.ld[b], g);
+    for (int i0 = 0; i0 < n; i0 += PF + 1) {
+#pragma unroll
+      for (int b = 0; b <= PF; ++b) {
+        const int i = i0 + b;
+        if (i < n) {
+          if (i + PF < n)
+            load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
+          store_b(ring[b], i);
+        }
+      }
+    }
+  }
+
+  // ---- this workgroup's dq partial: one float64 row of the workspace
+  double* out = block_dq + static_cast<int64_t>(blockIdx.x) * p.r;
+  if constexpr (WPR == kWavesPerBlock) {
+    // the four waves hold disjoint key columns
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+      const int u = g.unit(K0 + t);
+      if (u >= g.ub && u < g.nur) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int col = u * VEC + e;
+          if (col >= g.c0) out[col - g.c0] = static_cast<double>(dqa[t][e]);
+        }
+      }
+    }
+  } else {
+    // every wave holds the same columns: sum them in wave order, one slot at a time
+    __shared__ float dq_lds[kWavesPerBlock][kWave * VEC];
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dq_lds[wib][lane * VEC + e] = dqa[t][e];
+      __syncthreads();
+      const int u = g.unit(K0 + t);
+      if (wib == 0 && u >= g.ub && u < g.nur) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int col = u * VEC + e;
+          if (col >= g.c0) {
+            double sum = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWavesPerBlock; ++w)
+              sum += static_cast<double>(dq_lds[w][lane * VEC + e]);
+            out[col - g.c0] = sum;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+namespace {
+
+int device_cus_bwd() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <typename IO, int VEC, int NU, int TU, int WPR>
+hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_blocks, int* grid_out,
+                             hipStream_t s) {
+  auto kern = k_backward_tile<IO, VEC, NU, TU, WPR>;
+  const int ub = (p.d - p.r) / VEC;
+  const size_t lds = static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
+  static thread_local size_t cached_lds = ~size_t(0);
+  static thread_local int cached_per_cu = 0;
+  if (cached_lds != lds) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kBlock, lds) != hipSuccess ||
+        per < 1)
+      per = 1;
+    cached_per_cu = per;
+    cached_lds = lds;
+  }
+  constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
+  int64_t blocks = static_cast<int64_t>(cached_per_cu) * device_cus_bwd();
+  const int64_t need = (p.T + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  if (blocks > need) blocks = need;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  *grid_out = static_cast<int>(blocks);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p, block_dq);
+  return hipGetLastError();
+}
+
+template <typename IO, int VEC, int NU, int WPR>
+hipError_t launch_bwd_tile_tu(const BwdParams& p, double* block_dq, int max_blocks, int* grid,
+                              hipStream_t s) {
+  const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
+  if constexpr (NU > 1) {
+    if (first_key_chunk / WPR >= NU - 1)
+      return launch_bwd_tile_t<IO, VEC, NU, 1, WPR>(p, block_dq, max_blocks, grid, s);
+  }
+  return launch_bwd_tile_t<IO, VEC, NU, NU, WPR>(p, block_dq, max_blocks, grid, s);
+}
+
+template <typename IO, int VEC>
+hipError_t launch_bwd_tile_io(const BwdParams& p, double* block_dq, int max_blocks, int* grid,
+                              hipStream_t s) {
+  const int nur = (p.d + VEC - 1) / VEC;
+  const int chunks = (nur + kWave - 1) / kWave;
+  if (chunks <= 1) return launch_bwd_tile_tu<IO, VEC, 1, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 2) return launch_bwd_tile_tu<IO, VEC, 2, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 4) return launch_bwd_tile_tu<IO, VEC, 4, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 8) return launch_bwd_tile_tu<IO, VEC, 2, 4>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 16) return launch_bwd_tile_tu<IO, VEC, 4, 4>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 32) return launch_bwd_tile_tu<IO, VEC, 8, 4>(p, block_dq, max_blocks, grid, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int backward_tile_max_chunks() { return 32; }
+
+hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, double* block_dq, int max_blocks,
+                                int* grid, hipStream_t s) {
+  return io_bf16 ? launch_bwd_tile_io<bf16_bits, 8>(p, block_dq, max_blocks, grid, s)
+                 : launch_bwd_tile_io<float, 4>(p, block_dq, max_blocks, grid, s);
+}
+
+}  // namespace lrar

@@ -31,231 +31,10 @@
 
 #include "lrar_device.h"
 #include "lrar_launch.h"
+#include "lrar_tile.h"
 
 namespace lrar {
 
-enum TileMode : int { kTileOnline = 0, kTileTwoPass = 1, kTileMerge = 2 };
-
-namespace {
-
-constexpr double kLazyRescale = 8.0;
-
-template <typename IO, int VEC, int NU, int R>
-struct Tile {
-  Unit<IO, VEC> u[R][NU];
-};
-
-// KS consecutive key elements of one row, raw.
-template <typename IO, int KS>
-struct KeyPiece;
-
-template <typename IO>
-struct KeyPiece<IO, 0> {
-  __device__ __forceinline__ void load(const IO*) {}
-  __device__ __forceinline__ void zero() {}
-};
-
-template <>
-struct KeyPiece<bf16_bits, 1> {
-  uint32_t raw;
-  __device__ __forceinline__ void load(const bf16_bits* p) { raw = *p; }
-  __device__ __forceinline__ void zero() { raw = 0u; }
-  __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = __uint_as_float(raw << 16); }
-};
-
-template <>
-struct KeyPiece<bf16_bits, 2> {
-  uint32_t raw;
-  __device__ __forceinline__ void load(const bf16_bits* p) {
-    raw = *reinterpret_cast<const uint32_t*>(p);
-  }
-  __device__ __forceinline__ void zero() { raw = 0u; }
-  __device__ __forceinline__ void get(float (&x)[2]) const {
-    x[0] = __uint_as_float(raw << 16);
-    x[1] = __uint_as_float(raw & 0xffff0000u);
-  }
-};
-
-template <>
-struct KeyPiece<bf16_bits, 4> {
-  uint32_t raw[2];
-  __device__ __forceinline__ void load(const bf16_bits* p) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    raw[0] = v.x;
-    raw[1] = v.y;
-  }
-  __device__ __forceinline__ void zero() { raw[0] = raw[1] = 0u; }
-  __device__ __forceinline__ void get(float (&x)[4]) const {
-    x[0] = __uint_as_float(raw[0] << 16);
-    x[1] = __uint_as_float(raw[0] & 0xffff0000u);
-    x[2] = __uint_as_float(raw[1] << 16);
-    x[3] = __uint_as_float(raw[1] & 0xffff0000u);
-  }
-};
-
-template <>
-struct KeyPiece<float, 1> {
-  float raw;
-  __device__ __forceinline__ void load(const float* p) { raw = *p; }
-  __device__ __forceinline__ void zero() { raw = 0.f; }
-  __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = raw; }
-};
-
-template <>
-struct KeyPiece<float, 2> {
-  float raw[2];
-  __device__ __forceinline__ void load(const float* p) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const f32x2 v = *reinterpret_cast<const f32x2*>(p);
-    raw[0] = v.x;
-    raw[1] = v.y;
-  }
-  __device__ __forceinline__ void zero() { raw[0] = raw[1] = 0.f; }
-  __device__ __forceinline__ void get(float (&x)[2]) const {
-    x[0] = raw[0];
-    x[1] = raw[1];
-  }
-};
-
-template <>
-struct KeyPiece<float, 4> {
-  float raw[4];
-  __device__ __forceinline__ void load(const float* p) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-    raw[0] = v.x;
-    raw[1] = v.y;
-    raw[2] = v.z;
-    raw[3] = v.w;
-  }
-  __device__ __forceinline__ void zero() { raw[0] = raw[1] = raw[2] = raw[3] = 0.f; }
-  __device__ __forceinline__ void get(float (&x)[4]) const {
-    x[0] = raw[0];
-    x[1] = raw[1];
-    x[2] = raw[2];
-    x[3] = raw[3];
-  }
-};
-
-// One source's tile in flight: the rows and, with KS > 0, the spread key pieces of each row.
-template <typename IO, int VEC, int NU, int R, int KS>
-struct Stage {
-  Tile<IO, VEC, NU, R> t;
-  KeyPiece<IO, KS> kp[R];
-};
-
-struct TileGeom {
-  int64_t r0;  // first row of the tile
-  int nrow;    // rows of the tile that exist (<= R)
-  int lane, nur, ub, c0, r;
-  int w, wpr;  // this wave's place among the wpr waves that share a row
-  // Unit held in slot k: the row is cut into chunks of 64 units and chunk c belongs to wave
-  // c % wpr, so the waves of a row share the chunks (and the key) evenly.
-  __device__ __forceinline__ int unit(int k) const { return (k * wpr + w) * kWave + lane; }
-};
-
-// Loads one source's tile. KEYS_ONLY: only the key (the spread pieces, or the key units when
-// KS = 0). ROWS: whether the row units are loaded at all.
-template <bool KEYS_ONLY, typename IO, int VEC, int NU, int R, int KS>
-__device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
-                                           const IO* __restrict__ base, int64_t ld,
-                                           const TileGeom& g) {
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const IO* rowp = base + (g.r0 + j) * ld;  // wave-uniform: lane offsets stay 32-bit
-    if constexpr (KS > 0) {
-      if (j < g.nrow && g.lane * KS < g.r) st.kp[j].load(rowp + g.c0 + g.lane * KS);
-      else st.kp[j].zero();
-    }
-    if constexpr (!(KEYS_ONLY && KS > 0)) {
-#pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = g.unit(k);
-        const bool want = j < g.nrow && u < g.nur && (!KEYS_ONLY || u >= g.ub);
-        if (want) st.t.u[j][k].load(rowp + u * VEC);
-        else st.t.u[j][k].zero();
-      }
-    }
-  }
-}
-
-// This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the
-// last TU unit slots can hold key columns (the host picks TU so that the key starts in slot
-// NU - TU or later).
-template <int TU, typename IO, int VEC, int NU>
-__device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU],
-                                                  const float* __restrict__ q_lds,
-                                                  const TileGeom& g, double& dot, double& ss) {
-  dot = 0.0;
-  ss = 0.0;
-#pragma unroll
-  for (int k = NU - TU; k < NU; ++k) {
-    const int u = g.unit(k);
-    if (u >= g.ub && u < g.nur) {
-      float x[VEC];
-      row[k].get(x);
-      const float* qv = q_lds + (u - g.ub) * VEC;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int col = u * VEC + e;
-        const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
-        dot = fma(static_cast<double>(qv[e]), kv, dot);
-        ss = fma(kv, kv, ss);
-      }
-    }
-  }
-}
-
-// The same from this lane's spread key piece (KS > 0); qs holds the matching query values
-// (0 beyond the key).
-template <typename IO, int KS>
-__device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
-                                                   const double (&qs)[KS], double& dot,
-                                                   double& ss) {
-  float x[KS];
-  kp.get(x);
-  dot = 0.0;
-  ss = 0.0;
-#pragma unroll
-  for (int e = 0; e < KS; ++e) {
-    const double kv = static_cast<double>(x[e]);
-    dot = fma(qs[e], kv, dot);
-    ss = fma(kv, kv, ss);
-  }
-}
-
-// Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
-// lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
-// division run once for all rows.
-template <int R>
-__device__ __forceinline__ double row_scores_to_lanes(const double (&red)[2 * R], int lane, int r,
-                                                      double eps) {
-  double dot = red[0], ss = red[1];
-#pragma unroll
-  for (int j = 1; j < R; ++j) {
-    if (lane == j) {
-      dot = red[2 * j];
-      ss = red[2 * j + 1];
-    }
-  }
-  return dot / sqrt(ss / r + eps);
-}
-
-template <typename IO, int VEC, int NU>
-__device__ __forceinline__ void fma_row(float (&acc)[NU][VEC], float w,
-                                        const Unit<IO, VEC> (&row)[NU]) {
-#pragma unroll
-  for (int k = 0; k < NU; ++k) {
-    float x[VEC];
-    row[k].get(x);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(w, x[e], acc[k][e]);
-  }
-}
-
-constexpr int ks_slots(int ks) { return ks > 0 ? ks : 1; }
-
-}  // namespace
 
 template <typename IO, int VEC, int NU, int TU, int KS, int R, int PF, int WPR, int MODE,
           typename ACC>
