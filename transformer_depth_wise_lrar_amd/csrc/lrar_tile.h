@@ -195,6 +195,41 @@ __device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
   }
 }
 
+// z = dot / sqrt(ss / r + eps) as dot * rsq(ss / r + eps): the hardware reciprocal square root
+// refined by two Newton steps y <- y (3 - a y^2) / 2, each of which squares the relative error,
+// so the result is good to a few float64 ulp. A zero key with eps = 0 gives 0 * inf = NaN, as
+// the division does.
+__device__ __forceinline__ double score_from_sums(double dot, double ss, int r, double eps) {
+  const double a = ss / r + eps;
+  double y = __builtin_amdgcn_rsq(a);
+  y = y * fma(-0.5 * a, y * y, 1.5);
+  y = y * fma(-0.5 * a, y * y, 1.5);
+  return dot * y;
+}
+
+// e^x for x <= kLazyRescale, accurate to about 2^-31 relative (the weights it feeds are
+// rounded to float32): x = k ln 2 + f with |f| <= ln 2 / 2, e^f by its Taylor series to the
+// 8th power (truncation < 2^-31), then scaled by 2^k. Arguments below -745 give 0; NaN stays
+// NaN.
+__device__ __forceinline__ double exp_weight(double x) {
+  constexpr double kLog2e = 1.4426950408889634;
+  constexpr double kLn2Hi = 6.93147180369123816490e-01;  // ln 2 split so k * kLn2Hi is exact
+  constexpr double kLn2Lo = 1.90821492927058770002e-10;
+  const double xc = x < -745.0 ? -745.0 : x;  // a comparison, so NaN passes through
+  const double k = rint(xc * kLog2e);
+  const double f = fma(-k, kLn2Lo, fma(-k, kLn2Hi, xc));
+  double p = 1.0 / 40320.0;
+  p = fma(p, f, 1.0 / 5040.0);
+  p = fma(p, f, 1.0 / 720.0);
+  p = fma(p, f, 1.0 / 120.0);
+  p = fma(p, f, 1.0 / 24.0);
+  p = fma(p, f, 1.0 / 6.0);
+  p = fma(p, f, 0.5);
+  p = fma(p, f, 1.0);
+  p = fma(p, f, 1.0);
+  return ldexp(p, static_cast<int>(k));
+}
+
 // Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
 // lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
 // division run once for all rows.
@@ -209,7 +244,7 @@ __device__ __forceinline__ double row_scores_to_lanes(const double (&red)[2 * R]
       ss = red[2 * j + 1];
     }
   }
-  return dot / sqrt(ss / r + eps);
+  return score_from_sums(dot, ss, r, eps);
 }
 
 template <typename IO, int VEC, int NU>

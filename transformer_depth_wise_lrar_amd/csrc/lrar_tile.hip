@@ -1,427 +1,21 @@
-// The depth-mix read on register-resident row tiles (LR-AttnRes paper §3.1/§3.3; the Phase-2
-// merge of §3.4 and of the AttnRes technical-report summary, "Method").
-//
-// Layout. Each 64-lane wavefront owns tiles of R token rows. Lane l holds units l, l + 64, ...
-// (NU of them, 16 bytes each on the vector path) of every row of the tile, so the tile's rows
-// and their float32 accumulators live in registers for the whole read. The wave visits the
-// sources in order and keeps PF sources in flight ahead of the one it folds in. Tiles are
-// dealt to the waves in bands, so at any moment the resident waves read one contiguous window
-// of rows of the same few sources: long sequential HBM streams instead of one short stream per
-// (row, source).
-//
-// Modes.
-//   kTileOnline   one pass: every source byte is read once. Each source's score is computed
-//                 from the tile already in flight, and an online softmax folds the rows in.
-//                 The accumulator is rescaled only when a score passes the running reference
-//                 by more than kLazyRescale, so the weights stay <= e^8 and each rescale
-//                 shrinks every earlier rounding error together with the terms it scales.
-//   kTileTwoPass  pass 1 reads only the key slices and scores them; the softmax is taken once
-//                 per row in float64; pass 2 streams the full rows with the fixed float32
-//                 weights. The key bytes are read twice (normally from L2 the second time).
-//   kTileMerge    kTileOnline started from Phase-1 statistics (m, l, acc): lrar_merge.
-//
-// Key arithmetic (float64: bf16/fp32 x fp32 products are exact in float64).
-//   KS = 0   the key is taken from the row units in registers: only the last TU unit slots of
-//            a lane can hold key columns, and the site query is staged once per workgroup in
-//            LDS. Used for wide keys, where the key fills whole slots.
-//   KS > 0   "spread" key for r <= 64 KS: each lane also loads KS consecutive key elements
-//            (an ordinary cached load issued just before the row's streaming load, so the row
-//            load finds those lines in L2) and the products use every lane instead of the few
-//            that hold the key's units. The query's matching KS values stay in registers.
+// Dispatch of the register-tile read (lrar_tile_impl.h) to its per-mode instantiations.
 
-#include "lrar_device.h"
 #include "lrar_launch.h"
-#include "lrar_tile.h"
 
 namespace lrar {
 
-
-template <typename IO, int VEC, int NU, int TU, int KS, int R, int PF, int WPR, int MODE,
-          typename ACC>
-__global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
-  static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
-  extern __shared__ float q_lds[];
-  // Partial key sums of the waves that share a row (two slots, alternating by source).
-  __shared__ double xch[2][kWavesPerBlock][2 * R];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wib = threadIdx.x / kWave;  // wave in block
-  const int64_t group = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wib) / WPR;
-  const int n = p.n;
-  TileGeom g;
-  g.lane = lane;
-  g.w = wib % WPR;
-  g.wpr = WPR;
-  g.nur = (p.d + VEC - 1) / VEC;
-  g.c0 = p.d - p.r;
-  g.ub = g.c0 / VEC;
-  g.r = p.r;
-  // The query: spread over the lanes (KS > 0), or staged in LDS from the first key unit's
-  // column (KS = 0; the columns of that unit that precede the key hold zero).
-  double qs[ks_slots(KS)];
-#pragma unroll
-  for (int e = 0; e < ks_slots(KS); ++e) qs[e] = 0.0;
-  if constexpr (KS > 0) {
-    if (n > 0) {
-#pragma unroll
-      for (int e = 0; e < KS; ++e) {
-        const int idx = lane * KS + e;
-        if (idx < p.r) qs[e] = static_cast<double>(p.q[idx]);
-      }
-    }
-  } else {
-    if (n > 0) {
-      for (int k = threadIdx.x; k < p.d - g.ub * VEC; k += kBlock) {
-        const int col = g.ub * VEC + k;
-        q_lds[k] = col >= g.c0 ? p.q[col - g.c0] : 0.f;
-      }
-    }
-    __syncthreads();
-  }
-  // Spread key pieces sit in lanes [0, gp) (gp: a power of two).
-  int gp = 1;
-  if constexpr (KS > 0) {
-    const int used = (p.r + KS - 1) / KS;
-    while (gp < used) gp <<= 1;
-  }
-
-  // Tiles are dealt out in bands: in its k-th step row group w takes tile w + k * ngroups, so
-  // the resident waves together read one contiguous window of rows of every source at a time.
-  // (All waves of a group see the same tiles, so they meet the same barriers.)
-  const int64_t ngroups = static_cast<int64_t>(gridDim.x) * kWavesPerBlock / WPR;
-  const int64_t ntiles = (p.T + R - 1) / R;
-  int parity = 0;
-  for (int64_t tile = group; tile < ntiles; tile += ngroups) {
-    g.r0 = tile * R;
-    g.nrow = (p.T - g.r0) < R ? static_cast<int>(p.T - g.r0) : R;
-    const int64_t r0 = g.r0;
-    const int nrow = g.nrow;
-    float acc[R][NU][VEC];
-    double zk[R];  // lane i: score (two-pass: weight) of source i in row j
-    // Online-softmax state of row j, held in lane j: reference mref, running sum lsum of
-    // e^{z - mref}, running maximum mtop. One vector exp then serves all R rows.
-    double mref = -INFINITY, lsum = 0.0, mtop = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      zk[j] = 0.0;
-#pragma unroll
-      for (int k = 0; k < NU; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[j][k][e] = 0.f;
-    }
-    if constexpr (MODE == kTileMerge) {
-      if (lane < nrow) {
-        mref = static_cast<double>(p.m_in[r0 + lane]);
-        mtop = mref;
-        lsum = static_cast<double>(p.l_in[r0 + lane]);
-      }
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if (j < nrow) {
-          const ACC* prow = static_cast<const ACC*>(p.acc) + (r0 + j) * p.acc_ld;
-#pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            const int u = g.unit(k);
-            if (u < g.nur) load_acc<ACC, VEC>(prow + u * VEC, acc[j][k]);
-          }
-        }
-      }
-    }
-
-    // Ring of PF + 1 stages: source i + PF is loading while source i is folded in. The source
-    // loop is unrolled by PF + 1 so that every stage index is a constant and no stage is
-    // copied (a copy would wait for its loads).
-    Stage<IO, VEC, NU, R, KS> ring[PF + 1];
-    const auto src_base = [&](int i) { return static_cast<const IO*>(p.src.ptr[i]); };
-    // Scores of one stage's rows; lane j returns row j's.
-    const auto stage_scores = [&](const Stage<IO, VEC, NU, R, KS>& st) {
-      double red[2 * R];
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if constexpr (KS > 0)
-          key_partial_spread<IO, KS>(st.kp[j], qs, red[2 * j], red[2 * j + 1]);
-        else
-          key_partial_units<TU>(st.t.u[j], q_lds, g, red[2 * j], red[2 * j + 1]);
-      }
-      if constexpr (KS > 0) {
-        lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
-      } else {
-        wave_sums_dpp(red);
-        if constexpr (WPR > 1) {
-          // add the partial sums of the row's other waves, in a fixed order (so every wave
-          // of the row gets bitwise the same score)
-          double mine = red[0];
-#pragma unroll
-          for (int j = 1; j < 2 * R; ++j)
-            if (lane == j) mine = red[j];
-          if (lane < 2 * R) xch[parity][wib][lane] = mine;
-          __syncthreads();
-          const int base = wib - g.w;
-#pragma unroll
-          for (int j = 0; j < 2 * R; ++j) {
-            double t = xch[parity][base][j];
-#pragma unroll
-            for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][j];
-            red[j] = t;
-          }
-          parity ^= 1;
-        }
-      }
-      return row_scores_to_lanes<R>(red, lane, p.r, p.eps);
-    };
-
-    if constexpr (MODE == kTileTwoPass) {
-      // pass 1: scores from the key slices
-#pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<true>(ring[b], src_base(b), p.src.ld[b], g);
-      for (int i0 = 0; i0 < n; i0 += PF + 1) {
-#pragma unroll
-        for (int b = 0; b <= PF; ++b) {
-          const int i = i0 + b;
-          if (i < n) {
-            if (i + PF < n)
-              load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
-            const double z = stage_scores(ring[b]);
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-              const double zj = lane_f64(z, j);
-              if (lane == i) zk[j] = zj;
-            }
-          }
-        }
-      }
-      // softmax once per row (lanes = sources)
-      float w[R];
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const double m = wave_max_dpp(lane < n ? zk[j] : -INFINITY);
-        const double e = lane < n ? exp(zk[j] - m) : 0.0;
-        const double L = wave_sum_dpp(e);
-        zk[j] = e / L;
-        w[j] = static_cast<float>(zk[j]);
-      }
-      // pass 2: the values (the row units only)
-      Stage<IO, VEC, NU, R, 0> vring[PF + 1];
-#pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<false>(vring[b], src_base(b), p.src.ld[b], g);
-      for (int i0 = 0; i0 < n; i0 += PF + 1) {
-#pragma unroll
-        for (int b = 0; b <= PF; ++b) {
-          const int i = i0 + b;
-          if (i < n) {
-            if (i + PF < n)
-              load_stage<false>(vring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
-#pragma unroll
-            for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(w[j], i), vring[b].t.u[j]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<false>(ring[b], src_base(b), p.src.ld[b], g);
-      for (int i0 = 0; i0 < n; i0 += PF + 1) {
-#pragma unroll
-        for (int b = 0; b <= PF; ++b) {
-          const int i = i0 + b;
-          if (i < n) {
-            if (i + PF < n)
-              load_stage<false>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
-            const double z = stage_scores(ring[b]);  // lane j: row j
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-              const double zj = lane_f64(z, j);
-              if (lane == i) zk[j] = zj;
-            }
-            mtop = fmax(mtop, z);
-            // Rescale a row only when its score passes the reference by more than
-            // kLazyRescale (always on its first source, whose reference is -inf).
-            const bool grow = !(z <= mref + kLazyRescale);
-            if (__builtin_amdgcn_ballot_w64(grow && lane < R) != 0) {
-              const double sc = grow ? exp(mref - z) : 1.0;
-              mref = grow ? z : mref;
-              lsum *= sc;
-              const float scf = static_cast<float>(sc);
-#pragma unroll
-              for (int j = 0; j < R; ++j) {
-                const float sj = lane_f32(scf, j);
-#pragma unroll
-                for (int k = 0; k < NU; ++k)
-#pragma unroll
-                  for (int e = 0; e < VEC; ++e) acc[j][k][e] *= sj;
-              }
-            }
-            const double ez = exp(z - mref);
-            lsum += ez;
-            const float ef = static_cast<float>(ez);
-#pragma unroll
-            for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(ef, j), ring[b].t.u[j]);
-          }
-        }
-      }
-    }
-
-    // normalise, write h (and the weights / merged statistics)
-    const float inv = static_cast<float>(1.0 / lsum);  // lane j: row j (online and merge)
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (j >= nrow) continue;
-      const int64_t row = r0 + j;
-      float scale = 1.f;
-      if constexpr (MODE != kTileTwoPass) scale = lane_f32(inv, j);
-      IO* orow = static_cast<IO*>(p.out) + row * p.out_ld;
-#pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = g.unit(k);
-        if (u < g.nur) {
-          float y[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) y[e] = acc[j][k][e] * scale;
-          store_unit<IO, VEC>(orow + u * VEC, y);
-        }
-      }
-      if (p.alpha != nullptr && g.w == 0) {
-        double a = zk[j];
-        if constexpr (MODE != kTileTwoPass) a = exp(zk[j] - lane_f64(mref, j)) / lane_f64(lsum, j);
-        if (lane < n) p.alpha[row * p.alpha_ld + lane] = static_cast<float>(a);
-      }
-    }
-    if constexpr (MODE == kTileMerge) {
-      if (lane < nrow && g.w == 0) {
-        const float mf = static_cast<float>(mtop);
-        if (p.m_out) p.m_out[r0 + lane] = mf;
-        if (p.l_out) p.l_out[r0 + lane] = static_cast<float>(lsum * exp(mref - static_cast<double>(mf)));
-      }
-    }
-  }
-}
-
-// ---- launchers -----------------------------------------------------------------------------------
-
-namespace {
-
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
-// Rows per tile and prefetch depth for NU units per lane: the tile's accumulators and its
-// PF + 1 stages must leave room for several waves per SIMD, and the loads in flight
-// (waves x PF tiles) must cover the HBM latency.
-#ifndef LRAR_TILE_R
-constexpr int tile_rows(int nu) { return nu <= 1 ? 4 : (nu <= 2 ? 2 : 1); }
-#else
-constexpr int tile_rows(int nu) { return nu <= 4 ? LRAR_TILE_R : 1; }
-#endif
-#ifndef LRAR_TILE_PF
-constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
-#else
-constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
-#endif
-
-template <typename IO, int VEC, int NU, int TU, int KS, int WPR, int MODE, typename ACC>
-hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
-  constexpr int R = tile_rows(NU);
-  constexpr int PF = tile_prefetch(NU);
-  auto kern = k_read_tile<IO, VEC, NU, TU, KS, R, PF, WPR, MODE, ACC>;
-  const int ub = (p.d - p.r) / VEC;
-  const size_t lds = KS > 0 ? 0 : static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
-  // Workgroups per CU for this instantiation and LDS size (cached: the query is not free).
-  static thread_local size_t cached_lds = ~size_t(0);
-  static thread_local int cached_per_cu = 0;
-  if (cached_lds != lds) {
-    int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kBlock, lds) != hipSuccess ||
-        per < 1)
-      per = 1;
-    cached_per_cu = per;
-    cached_lds = lds;
-  }
-  const int per_cu = cached_per_cu;
-  // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
-  // the grid runs in one round and the groups' tile counts differ by at most one.
-  const int64_t resident = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock / WPR;
-  const int64_t tiles = (p.T + R - 1) / R;
-  const int64_t per_group = (tiles + resident - 1) / resident;
-  const int64_t groups = (tiles + per_group - 1) / per_group;
-  constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
-  const int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p);
-  return hipGetLastError();
-}
-
-// Key path: spread pieces of KS elements when the key is short and its start is KS-aligned;
-// otherwise the row units, with TU = 1 when every key chunk lands in a wave's last slot.
-template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
-hipError_t launch_tile_key(const ReadParams& p, hipStream_t s) {
-  const int c0 = p.d - p.r;
-  if constexpr (VEC > 1) {
-    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, WPR, MODE, ACC>(p, s);
-    if (p.r <= 2 * kWave && c0 % 2 == 0)
-      return launch_tile_t<IO, VEC, NU, 1, 2, WPR, MODE, ACC>(p, s);
-    if (p.r <= 4 * kWave && c0 % 4 == 0)
-      return launch_tile_t<IO, VEC, NU, 1, 4, WPR, MODE, ACC>(p, s);
-  }
-  const int first_key_chunk = (c0 / VEC) / kWave;
-  if constexpr (NU > 1) {
-    if (first_key_chunk / WPR >= NU - 1)
-      return launch_tile_t<IO, VEC, NU, 1, 0, WPR, MODE, ACC>(p, s);
-  }
-  return launch_tile_t<IO, VEC, NU, NU, 0, WPR, MODE, ACC>(p, s);
-}
-
-// Rows of up to 4 chunks of 64 units are held by one wave; wider rows by the 4 waves of a
-// workgroup, each taking every fourth chunk.
-template <typename IO, int VEC, int MODE, typename ACC>
-hipError_t launch_tile_nu(const ReadParams& p, hipStream_t s) {
-  const int nur = (p.d + VEC - 1) / VEC;
-  const int chunks = (nur + kWave - 1) / kWave;
-  if (chunks <= 1) return launch_tile_key<IO, VEC, 1, 1, MODE, ACC>(p, s);
-  if (chunks <= 2) return launch_tile_key<IO, VEC, 2, 1, MODE, ACC>(p, s);
-  if (chunks <= 4) return launch_tile_key<IO, VEC, 4, 1, MODE, ACC>(p, s);
-  if (chunks <= 8) return launch_tile_key<IO, VEC, 2, 4, MODE, ACC>(p, s);
-  if (chunks <= 16) return launch_tile_key<IO, VEC, 4, 4, MODE, ACC>(p, s);
-  if (chunks <= 32) return launch_tile_key<IO, VEC, 8, 4, MODE, ACC>(p, s);
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
+hipError_t launch_tile_online(const ReadParams& p, int io_bf16, int vec, hipStream_t s);
+hipError_t launch_tile_twopass(const ReadParams& p, int io_bf16, int vec, hipStream_t s);
+hipError_t launch_tile_merge(const ReadParams& p, int io_bf16, int vec, int acc_bf16,
+                             hipStream_t s);
 
 int tile_max_chunks() { return 32; }
 
 hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s) {
-  if (kind == ReadKind::kMerge) {
-    if (io_bf16) {
-      if (acc_bf16) return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileMerge, bf16_bits>(p, s)
-                                   : launch_tile_nu<bf16_bits, 1, kTileMerge, bf16_bits>(p, s);
-      return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileMerge, float>(p, s)
-                     : launch_tile_nu<bf16_bits, 1, kTileMerge, float>(p, s);
-    }
-    if (acc_bf16) return vec > 1 ? launch_tile_nu<float, 4, kTileMerge, bf16_bits>(p, s)
-                                 : launch_tile_nu<float, 1, kTileMerge, bf16_bits>(p, s);
-    return vec > 1 ? launch_tile_nu<float, 4, kTileMerge, float>(p, s)
-                   : launch_tile_nu<float, 1, kTileMerge, float>(p, s);
-  }
-  if (kind == ReadKind::kOnline) {
-    if (io_bf16) return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileOnline, float>(p, s)
-                                : launch_tile_nu<bf16_bits, 1, kTileOnline, float>(p, s);
-    return vec > 1 ? launch_tile_nu<float, 4, kTileOnline, float>(p, s)
-                   : launch_tile_nu<float, 1, kTileOnline, float>(p, s);
-  }
-  if (io_bf16) return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileTwoPass, float>(p, s)
-                              : launch_tile_nu<bf16_bits, 1, kTileTwoPass, float>(p, s);
-  return vec > 1 ? launch_tile_nu<float, 4, kTileTwoPass, float>(p, s)
-                 : launch_tile_nu<float, 1, kTileTwoPass, float>(p, s);
+  if (kind == ReadKind::kMerge) return launch_tile_merge(p, io_bf16, vec, acc_bf16, s);
+  if (kind == ReadKind::kOnline) return launch_tile_online(p, io_bf16, vec, s);
+  return launch_tile_twopass(p, io_bf16, vec, s);
 }
 
 }  // namespace lrar

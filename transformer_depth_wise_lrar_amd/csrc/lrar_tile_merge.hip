@@ -1,0 +1,20 @@
+// Instantiation of the register-tile read, merge mode (Phase 2; see lrar_tile_impl.h).
+#include "lrar_tile_impl.h"
+
+namespace lrar {
+
+hipError_t launch_tile_merge(const ReadParams& p, int io_bf16, int vec, int acc_bf16,
+                             hipStream_t s) {
+  if (io_bf16) {
+    if (acc_bf16) return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileMerge, bf16_bits>(p, s)
+                                 : launch_tile_nu<bf16_bits, 1, kTileMerge, bf16_bits>(p, s);
+    return vec > 1 ? launch_tile_nu<bf16_bits, 8, kTileMerge, float>(p, s)
+                   : launch_tile_nu<bf16_bits, 1, kTileMerge, float>(p, s);
+  }
+  if (acc_bf16) return vec > 1 ? launch_tile_nu<float, 4, kTileMerge, bf16_bits>(p, s)
+                               : launch_tile_nu<float, 1, kTileMerge, bf16_bits>(p, s);
+  return vec > 1 ? launch_tile_nu<float, 4, kTileMerge, float>(p, s)
+                 : launch_tile_nu<float, 1, kTileMerge, float>(p, s);
+}
+
+}  // namespace lrar
