@@ -3,6 +3,8 @@
 // ring, and the float64 key partial sums. See lrar_tile.hip for the layout they serve.
 #pragma once
 
+#include <type_traits>
+
 #include "lrar_device.h"
 
 namespace lrar {
@@ -108,6 +110,40 @@ struct KeyPiece<float, 4> {
   }
 };
 
+// 8 or 16 consecutive key elements: one or more 16-byte units.
+template <typename IO, int KS>
+struct KeyPieceUnits {
+  static constexpr int kPer = 16 / sizeof(IO);  // elements per 16-byte unit
+  static constexpr int kUnits = KS / kPer;
+  Unit<IO, 16 / sizeof(IO)> u[kUnits];
+  __device__ __forceinline__ void load(const IO* p) {
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) u[k].load_cached(p + k * kPer);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) u[k].zero();
+  }
+  __device__ __forceinline__ void get(float (&x)[KS]) const {
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+      float y[kPer];
+      u[k].get(y);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) x[k * kPer + e] = y[e];
+    }
+  }
+};
+
+template <>
+struct KeyPiece<bf16_bits, 8> : KeyPieceUnits<bf16_bits, 8> {};
+template <>
+struct KeyPiece<bf16_bits, 16> : KeyPieceUnits<bf16_bits, 16> {};
+template <>
+struct KeyPiece<float, 8> : KeyPieceUnits<float, 8> {};
+template <>
+struct KeyPiece<float, 16> : KeyPieceUnits<float, 16> {};
+
 // One source's tile in flight: the rows and, with KS > 0, the spread key pieces of each row.
 template <typename IO, int VEC, int NU, int R, int KS>
 struct Stage {
@@ -179,9 +215,9 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
 
 // The same from this lane's spread key piece (KS > 0); qs holds the matching query values
 // (0 beyond the key).
-template <typename IO, int KS>
+template <typename IO, int KS, typename QT>
 __device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
-                                                   const double (&qs)[KS], double& dot,
+                                                   const QT (&qs)[KS], double& dot,
                                                    double& ss) {
   float x[KS];
   kp.get(x);
@@ -190,7 +226,7 @@ __device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
 #pragma unroll
   for (int e = 0; e < KS; ++e) {
     const double kv = static_cast<double>(x[e]);
-    dot = fma(qs[e], kv, dot);
+    dot = fma(static_cast<double>(qs[e]), kv, dot);
     ss = fma(kv, kv, ss);
   }
 }
@@ -230,6 +266,51 @@ __device__ __forceinline__ double exp_weight(double x) {
   return ldexp(p, static_cast<int>(k));
 }
 
+// Lane i ^ 16 within each half-wave (ds_swizzle in bit-mask mode: and 0x1f, xor 0x10).
+__device__ __forceinline__ double swizzle_xor16_f64(double v) {
+  constexpr int kXor16 = 0x1f | (0x10 << 10);
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_ds_swizzle(static_cast<int>(b), kXor16);
+  const int hi = __builtin_amdgcn_ds_swizzle(static_cast<int>(b >> 32), kXor16);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// Row-local sums for R = 1 or 2 tile rows when the spread key sits in lanes 0..31: the 2R
+// values (q . k, k . k per row) are reduced by a transposed butterfly. Partners that differ in
+// lane bit 0, then bit 1, swap halves of their value set, so after two steps each lane carries
+// one value summed over its quad; rotations of each DPP row by 4 and 8 lanes add the row's
+// four quads, and a lane-xor-16 swizzle adds the second row. Lane j (< R) returns row j's
+// score.
+template <int R>
+__device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
+                                                      double eps) {
+  static_assert(R == 1 || R == 2, "two or four values");
+  constexpr int kRor4 = 0x124, kRor8 = 0x128;
+  const bool b0 = (lane & 1) != 0;
+  double x;
+  if constexpr (R == 2) {
+    // values 0..3 = dot0, ss0, dot1, ss1; after the xor-1 step lanes with bit 0 clear carry
+    // {dot0, ss0}, the others {dot1, ss1}; after the xor-2 step lane (b1 b0) carries value
+    // 2 b0 + b1: lane 0 dot0, lane 1 dot1, lane 2 ss0, lane 3 ss1.
+    const double keep0 = b0 ? red[2] : red[0], send0 = b0 ? red[0] : red[2];
+    const double keep1 = b0 ? red[3] : red[1], send1 = b0 ? red[1] : red[3];
+    const double w0 = keep0 + dpp_f64<kDppXor1>(send0, 0.0);
+    const double w1 = keep1 + dpp_f64<kDppXor1>(send1, 0.0);
+    const bool b1 = (lane & 2) != 0;
+    x = (b1 ? w1 : w0) + dpp_f64<kDppXor2>(b1 ? w0 : w1, 0.0);
+  } else {
+    // values 0, 1 = dot, ss; lane 0 ends with dot, lane 1 with ss
+    x = (b0 ? red[1] : red[0]) + dpp_f64<kDppXor1>(b0 ? red[0] : red[1], 0.0);
+    x += dpp_f64<kDppXor2>(x, 0.0);
+  }
+  x += dpp_f64<kRor4>(x, 0.0);
+  x += dpp_f64<kRor8>(x, 0.0);
+  x += swizzle_xor16_f64(x);
+  // ss of row j sits R lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1)
+  const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
+  return score_from_sums(x, ss, r, eps);
+}
+
 // Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
 // lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
 // division run once for all rows.
@@ -260,5 +341,10 @@ __device__ __forceinline__ void fma_row(float (&acc)[NU][VEC], float w,
 }
 
 constexpr int ks_slots(int ks) { return ks > 0 ? ks : 1; }
+
+// The spread query values a lane keeps: float64 for pieces of up to 4 elements, float32 (and
+// widened on use) for larger pieces, which would otherwise take 16 or 32 registers.
+template <int KS>
+using SpreadQ = typename std::conditional<(KS > 4), float, double>::type;
 
 }  // namespace lrar

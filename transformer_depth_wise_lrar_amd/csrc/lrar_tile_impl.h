@@ -40,8 +40,8 @@
 namespace lrar {
 
 
-template <typename IO, int VEC, int NU, int TU, int KS, int R, int PF, int WPR, int MODE,
-          typename ACC>
+template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int R, int PF, int WPR,
+          int MODE, typename ACC>
 __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   extern __shared__ float q_lds[];
@@ -61,15 +61,15 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
   g.r = p.r;
   // The query: spread over the lanes (KS > 0), or staged in LDS from the first key unit's
   // column (KS = 0; the columns of that unit that precede the key hold zero).
-  double qs[ks_slots(KS)];
+  SpreadQ<KS> qs[ks_slots(KS)];
 #pragma unroll
-  for (int e = 0; e < ks_slots(KS); ++e) qs[e] = 0.0;
+  for (int e = 0; e < ks_slots(KS); ++e) qs[e] = 0;
   if constexpr (KS > 0) {
     if (n > 0) {
 #pragma unroll
       for (int e = 0; e < KS; ++e) {
         const int idx = lane * KS + e;
-        if (idx < p.r) qs[e] = static_cast<double>(p.q[idx]);
+        if (idx < p.r) qs[e] = static_cast<SpreadQ<KS>>(p.q[idx]);
       }
     }
   } else {
@@ -188,7 +188,10 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
       else
         key_partial_units<TU>(st.t.u[j], q_lds, t, red[2 * j], red[2 * j + 1]);
     }
-    if constexpr (KS > 0) {
+    if constexpr (KS > 0 && ROWRED && R <= 2) {
+      // the spread key sits in lanes 0..31 of every wave of the row
+      return row_scores_rowlocal<R>(red, lane, p.r, p.eps);
+    } else if constexpr (KS > 0) {
       lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
     } else {
       wave_sums_dpp(red);
@@ -365,11 +368,12 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
 constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
 #endif
 
-template <typename IO, int VEC, int NU, int TU, int KS, int WPR, int MODE, typename ACC>
+template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, int MODE,
+          typename ACC>
 hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
   constexpr int R = tile_rows(NU);
   constexpr int PF = tile_prefetch(NU);
-  auto kern = k_read_tile<IO, VEC, NU, TU, KS, R, PF, WPR, MODE, ACC>;
+  auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC>;
   const int ub = (p.d - p.r) / VEC;
   const size_t lds = KS > 0 ? 0 : static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
   // Workgroups per CU for this instantiation and LDS size (cached: the query is not free).
@@ -396,24 +400,29 @@ hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Key path: spread pieces of KS elements when the key is short and its start is KS-aligned;
-// otherwise the row units, with TU = 1 when every key chunk lands in a wave's last slot.
+// Key path. Spread pieces of KS elements when the key is short: preferably KS = r / 32 rounded
+// up to a power of two, so the key fits lanes 0..31 (row-local sums), else 1 or 2 elements over
+// up to 64 lanes; a piece size must divide r and keep the loads aligned. Otherwise the row
+// units, with TU = 1 when every key chunk lands in a wave's last slot.
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, hipStream_t s) {
   const int c0 = p.d - p.r;
   if constexpr (VEC > 1) {
-    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, WPR, MODE, ACC>(p, s);
-    if (p.r <= 2 * kWave && c0 % 2 == 0)
-      return launch_tile_t<IO, VEC, NU, 1, 2, WPR, MODE, ACC>(p, s);
-    if (p.r <= 4 * kWave && c0 % 4 == 0)
-      return launch_tile_t<IO, VEC, NU, 1, 4, WPR, MODE, ACC>(p, s);
+    const auto fits = [&](int ks) { return p.r % ks == 0 && c0 % (ks < VEC ? ks : VEC) == 0; };
+    if (p.r <= 32 && fits(1)) return launch_tile_t<IO, VEC, NU, 1, 1, true, WPR, MODE, ACC>(p, s);
+    if (p.r <= 64 && fits(2)) return launch_tile_t<IO, VEC, NU, 1, 2, true, WPR, MODE, ACC>(p, s);
+    if (p.r <= 128 && fits(4)) return launch_tile_t<IO, VEC, NU, 1, 4, true, WPR, MODE, ACC>(p, s);
+    if (p.r <= 256 && fits(8)) return launch_tile_t<IO, VEC, NU, 1, 8, true, WPR, MODE, ACC>(p, s);
+    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, false, WPR, MODE, ACC>(p, s);
+    if (p.r <= 2 * kWave && fits(2))
+      return launch_tile_t<IO, VEC, NU, 1, 2, false, WPR, MODE, ACC>(p, s);
   }
   const int first_key_chunk = (c0 / VEC) / kWave;
   if constexpr (NU > 1) {
     if (first_key_chunk / WPR >= NU - 1)
-      return launch_tile_t<IO, VEC, NU, 1, 0, WPR, MODE, ACC>(p, s);
+      return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, s);
   }
-  return launch_tile_t<IO, VEC, NU, NU, 0, WPR, MODE, ACC>(p, s);
+  return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, s);
 }
 
 // Rows of up to 4 chunks of 64 units are held by one wave; wider rows by the 4 waves of a
