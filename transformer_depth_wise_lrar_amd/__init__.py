@@ -90,6 +90,26 @@ def exported_symbols() -> list[str]:
             "lrar_last_error", "lrar_version"]
 
 
+class Prepared:
+    """A library call with its arguments already marshalled: calling it runs only the C entry
+    point (so a timed region holds the launch and nothing of the Python marshalling). It keeps
+    the tensors it was built from alive; their contents may change between calls."""
+
+    def __init__(self, fn, args, result, keep):
+        self._fn, self._args, self.result, self._keep = fn, args, result, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.result
+
+
+def _run(fn, args, result, keep, prepare):
+    if prepare:
+        return Prepared(fn, args, result, keep)
+    _check(fn(*args))
+    return result
+
+
 def _check(status: int):
     if status != LRAR_OK:
         L = lib()
@@ -173,7 +193,7 @@ def _src_table(srcs: Sequence, io: int | None):
 
 
 def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=None,
-                 variant: str = "auto", stream=None):
+                 variant: str = "auto", stream=None, prepare: bool = False):
     """h = sum_i softmax_i(q . RMSNorm(tail_r(o_i))) o_i for every row.
 
     srcs: n tensors [T, d] (bf16 or fp32, unit column stride); q: fp32 [r].
@@ -193,13 +213,13 @@ def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=N
     if alpha is not None:
         _need(alpha, (T, len(srcs)), torch.float32, "alpha")
     ap, ald = _rows(alpha, "alpha") if alpha is not None else (None, 0)
-    _check(lib().lrar_forward(T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op,
-                              old, ap, ald, VARIANTS[variant], _stream(stream)))
-    return out, alpha
+    args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op, old, ap, ald,
+            VARIANTS[variant], _stream(stream))
+    return _run(lib().lrar_forward, args, (out, alpha), (srcs, q, out, alpha), prepare)
 
 
 def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=None,
-                       m=None, l=None, acc=None, stream=None):
+                       m=None, l=None, acc=None, stream=None, prepare: bool = False):
     """Phase-1 statistics of queries qs [nq, r] against the sources.
 
     Returns (m [nq, T], l [nq, T], acc [nq, T, d]); acc is unnormalised, fp32 by default."""
@@ -222,15 +242,14 @@ def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=
     _need(acc, (nq, T, d), None, "acc")
     if acc.stride(2) != 1 or m.stride(1) != 1 or l.stride(1) != 1 or m.stride(0) != l.stride(0):
         raise ValueError("m, l, acc need unit inner stride and m, l one row stride")
-    _check(lib().lrar_forward_stats(T, d, r, float(eps), io, len(srcs), ptrs, lds, nq,
-                                    qs.data_ptr(), qs.stride(0), m.data_ptr(), l.data_ptr(),
-                                    m.stride(0), acc.data_ptr(), _dtype_code(acc),
-                                    acc.stride(1), acc.stride(0), _stream(stream)))
-    return m, l, acc
+    args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, nq, qs.data_ptr(), qs.stride(0),
+            m.data_ptr(), l.data_ptr(), m.stride(0), acc.data_ptr(), _dtype_code(acc),
+            acc.stride(1), acc.stride(0), _stream(stream))
+    return _run(lib().lrar_forward_stats, args, (m, l, acc), (srcs, qs, m, l, acc), prepare)
 
 
 def lrar_merge(m, l, acc, srcs: Sequence, q, r: int, eps: float = 1e-6, out=None,
-               stats_out: bool = False, io_dtype=None, stream=None):
+               stats_out: bool = False, io_dtype=None, stream=None, prepare: bool = False):
     """Phase-2 merge of one site's statistics (m [T], l [T], acc [T, d]) with extra sources.
 
     Returns out, or (out, m', l') with stats_out=True."""
@@ -259,12 +278,12 @@ def lrar_merge(m, l, acc, srcs: Sequence, q, r: int, eps: float = 1e-6, out=None
     if stats_out:
         m_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
         l_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
-    _check(lib().lrar_merge(T, d, r, float(eps), io, m.data_ptr(), l.data_ptr(), accp,
-                            _dtype_code(acc), accld, len(srcs), ptrs, lds,
-                            q.data_ptr() if q is not None else None, op, old,
-                            m_out.data_ptr() if m_out is not None else None,
-                            l_out.data_ptr() if l_out is not None else None, _stream(stream)))
-    return (out, m_out, l_out) if stats_out else out
+    args = (T, d, r, float(eps), io, m.data_ptr(), l.data_ptr(), accp, _dtype_code(acc), accld,
+            len(srcs), ptrs, lds, q.data_ptr() if q is not None else None, op, old,
+            m_out.data_ptr() if m_out is not None else None,
+            l_out.data_ptr() if l_out is not None else None, _stream(stream))
+    result = (out, m_out, l_out) if stats_out else out
+    return _run(lib().lrar_merge, args, result, (m, l, acc, srcs, q, out, m_out, l_out), prepare)
 
 
 def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
@@ -273,7 +292,8 @@ def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
 
 
 def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
-                  accumulate: bool = False, dq=None, workspace=None, stream=None):
+                  accumulate: bool = False, dq=None, workspace=None, stream=None,
+                  prepare: bool = False):
     """Source and query gradients of one read for upstream gradient dout (fp32 [T, d]).
 
     Returns (dsrc list of fp32 [T, d], dq fp32 [r])."""
@@ -300,20 +320,20 @@ def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
     if workspace is None:
         workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
     gp, gld = _rows(dout, "dout")
-    _check(lib().lrar_backward(T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr(), gp, gld,
-                               dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               _stream(stream)))
-    return dsrc, dq
+    args = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr(), gp, gld, dptrs, dlds,
+            int(bool(accumulate)), dq.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return _run(lib().lrar_backward, args, (dsrc, dq), (srcs, q, dout, dsrc, dq, workspace),
+                prepare)
 
 
-def lrar_copy(dst, src, stream=None):
+def lrar_copy(dst, src, stream=None, prepare: bool = False):
     """Plain streaming copy of src into dst (same byte size, 16-byte multiples)."""
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("dst and src must have the same byte size")
-    _check(lib().lrar_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
-    return dst
+    args = (dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream))
+    return _run(lib().lrar_copy, args, dst, (dst, src), prepare)
 
 
 def version() -> str:
