@@ -76,7 +76,9 @@ typedef enum lrar_variant {
  *   out, out_ld  : device [T, out_ld] of type io; receives h. Must not be one of src.
  *   alpha, alpha_ld : optional device float32 [T, alpha_ld >= n]; receives the weights.
  *   variant      : lrar_variant. LRAR_ERR_UNSUPPORTED if ONLINE is asked for a d it does
- *                  not cover (d > 8192 bf16 / 4096 f32 on the vector path).
+ *                  not cover: d > 16384 (bf16) / 8192 (f32) on the vector path, taken when
+ *                  d is a multiple of 8 (bf16) / 4 (f32) and every row of the sources and
+ *                  of out starts 16-byte aligned; d > 2048 on the element path otherwise.
  * With n = 1 the output equals src[0] exactly (the embedding-only read is the identity). */
 lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                          int32_t n, const void* const* src, const int64_t* src_ld,
@@ -127,8 +129,9 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
  *                   order, so results are bitwise reproducible.
  *   workspace     : device scratch of at least lrar_backward_workspace_size(T, d, r, n)
  *                   bytes, 8-byte aligned; its contents are not needed after the call.
- * Supported on the vector path for d <= 8192 (bf16) / 4096 (f32), on the scalar path for
- * d <= 2048; LRAR_ERR_UNSUPPORTED otherwise. */
+ * Supported on the vector path (d a multiple of 8 (bf16) / 4 (f32), every row of the
+ * sources, dout and dsrc 16-byte aligned) for d <= 16384 (bf16) / 8192 (f32), on the element path for d <= 2048;
+ * LRAR_ERR_UNSUPPORTED otherwise. */
 lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                           int32_t n, const void* const* src, const int64_t* src_ld,
                           const float* q, const float* dout, int64_t dout_ld,

@@ -71,7 +71,8 @@ def test_forward_empty_is_ok_without_device(L):
 
 
 def test_online_too_wide_is_unsupported(L):
-    assert fwd(L, d=8192 * 2, r=16, ld=8192 * 2, out_ld=8192 * 2, variant=2) == \
+    # 2049 units of 8 bf16 are 33 chunks of 64 lanes, one more than a register tile holds
+    assert fwd(L, d=16392, r=16, ld=16392, out_ld=16392, variant=2) == \
         lrar.LRAR_ERR_UNSUPPORTED
 
 
