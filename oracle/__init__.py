@@ -93,6 +93,8 @@ class Oracle:
         lib.orc_attnres_standard.argtypes = [i64, i32, dbl, i32, _pp, _i64p, _dp, _dp, i64,
                                              _dp]
         lib.orc_forward_fullrms.argtypes = lib.orc_forward.argtypes
+        lib.orc_forward_keys.argtypes = [i64, i32, i32, dbl, i32, _pp, _i64p, _pp, _i64p, _dp,
+                                         _dp, i64, _dp]
         lib.orc_stats.argtypes = [i64, i32, i32, dbl, i32, _pp, _i64p, i32, _dp, _dp, _dp, _dp]
         lib.orc_merge.argtypes = [i64, i32, i32, dbl, _dp, _dp, _dp, i32, _pp, _i64p, _dp, _dp,
                                   i64, _dp, _dp]
@@ -100,7 +102,7 @@ class Oracle:
                                      _dp]
         lib.orc_backward_fullrms.argtypes = lib.orc_backward.argtypes
         for fn in ("orc_scores", "orc_forward", "orc_attnres_standard", "orc_forward_fullrms",
-                   "orc_stats", "orc_merge", "orc_backward", "orc_backward_fullrms"):
+                   "orc_forward_keys", "orc_stats", "orc_merge", "orc_backward", "orc_backward_fullrms"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -132,6 +134,30 @@ class Oracle:
     def forward_fullrms(self, srcs, q, r, eps):
         """(h, alpha) of the full-width-RMS control read."""
         return self._fwd(self.lib.orc_forward_fullrms, srcs, q, r, eps, "forward_fullrms")
+
+    def forward_keys(self, srcs, keys, q, r, eps):
+        """(h, alpha) of the separate-key read: keys is a list of n [T, >= r] arrays whose
+        first r columns are the sources' keys."""
+        arrs, ptrs, lds, T, d = _src_arrays(srcs)
+        karrs = []
+        for k in keys:
+            k = _f64(k)
+            if k.ndim != 2 or k.shape[0] != T or k.shape[1] < r:
+                raise ValueError("each key must be [T, >= r]")
+            if k.strides[1] != 8 or k.strides[0] % 8:
+                k = np.ascontiguousarray(k)
+            karrs.append(k)
+        if len(karrs) != len(arrs):
+            raise ValueError("one key per source")
+        n = len(arrs)
+        kptrs = (ctypes.c_void_p * n)(*[k.ctypes.data for k in karrs])
+        klds = (ctypes.c_int64 * n)(*[k.strides[0] // 8 for k in karrs])
+        q = np.ascontiguousarray(_f64(q))
+        out = np.empty((T, d))
+        alpha = np.empty((T, n))
+        _check(self.lib.orc_forward_keys(T, d, r, eps, n, ptrs, lds, kptrs, klds, _dptr(q),
+                                         _dptr(out), d, _dptr(alpha)), "forward_keys")
+        return out, alpha
 
     def attnres_standard(self, srcs, q, eps):
         """(h, alpha) of standard AttnRes: full-width key, q of length d."""
@@ -221,6 +247,10 @@ def forward(*a, **k):
 
 def forward_fullrms(*a, **k):
     return default().forward_fullrms(*a, **k)
+
+
+def forward_keys(*a, **k):
+    return default().forward_keys(*a, **k)
 
 
 def attnres_standard(*a, **k):

@@ -183,6 +183,43 @@ int orc_forward_fullrms(int64_t T, int d, int r, double eps, int n, const double
   return 0;
 }
 
+// Separate-key read, the read side of Projected LR-AttnRes ([Paper] App. C.1: each source
+// has its own r-wide key, RMS-normalised; App. C.2: a source then carries d + r elements).
+// Source i supplies a value row o_i (d wide, from src) and a key row k_i (r wide, from key);
+// for every token t,
+//   alpha_i = softmax_i(q . k_i / sqrt(||k_i||^2 / r + eps)),   h = sum_i alpha_i o_i.
+// key[i] is a [T, key_ld[i]] array of which the first r columns are the key.
+int orc_forward_keys(int64_t T, int d, int r, double eps, int n, const double* const* src,
+                     const int64_t* ld, const double* const* key, const int64_t* key_ld,
+                     const double* q, double* out, int64_t out_ld, double* alpha) {
+  if (bad_common(T, d, r, eps, n, 1) || !src || !ld || !key || !key_ld || !q || !out ||
+      out_ld < d)
+    return -1;
+  for (int i = 0; i < n; ++i)
+    if (!key[i] || key_ld[i] < r) return -1;
+  std::vector<double> z(n), a(n);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int i = 0; i < n; ++i) {
+      const double* k = row_of(key[i], key_ld[i], t);
+      double sum_sq = 0.0;
+      for (int j = 0; j < r; ++j) sum_sq += k[j] * k[j];
+      const double rho = std::sqrt(sum_sq / r + eps);
+      double zi = 0.0;
+      for (int j = 0; j < r; ++j) zi += q[j] * (k[j] / rho);
+      z[i] = zi;
+    }
+    softmax(z, a);
+    for (int j = 0; j < d; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < n; ++i) s += a[i] * row_of(src[i], ld[i], t)[j];
+      out[t * out_ld + j] = s;
+    }
+    if (alpha)
+      for (int i = 0; i < n; ++i) alpha[t * n + i] = a[i];
+  }
+  return 0;
+}
+
 // Phase 1 of the two-phase block schedule ([AttnRes-TR] Method, "two-phase inference":
 // the block's static queries are batched against the cached block representations;
 // [Paper] §3.4: the inter- and intra-block results merge by an online-softmax update).

@@ -366,6 +366,85 @@ def pin_fullrms_at_r_equals_d(orc):
                                                                      atol=1e-14)
 
 
+def pin_fullrms_closed_form(orc):
+    """[Paper] §4.4 Eq. 13 (control): the key is P_r o / sqrt(||o||^2 / d + eps), so the head
+    coordinates enter through the denominator. At eps = 0, o_A = (1, 1, 1, 1) has full RMS 1
+    and normalised key (1, 1); o_B = (2, 0, 0, 0) has full RMS 1 and key (0, 0). With
+    q = (ln 3, 0) the scores are ln 3 and 0: weights (3/4, 1/4), h = (5/4, 3/4, 3/4, 3/4).
+    Moving o_A's head to (3, 1) makes its full RMS sqrt 3, so its score is ln 3 / sqrt 3."""
+    q = np.array([math.log(3.0), 0.0])
+    oA = np.array([[1.0, 1.0, 1.0, 1.0]])
+    oB = np.array([[2.0, 0.0, 0.0, 0.0]])
+    h, al = orc.forward_fullrms([oA, oB], q, 2, 0.0)
+    assert np.allclose(al[0], [0.75, 0.25], rtol=0, atol=1e-15), al
+    assert np.allclose(h[0], [1.25, 0.75, 0.75, 0.75], rtol=0, atol=1e-15), h
+    oA2 = np.array([[3.0, 1.0, 1.0, 1.0]])
+    _, al2 = orc.forward_fullrms([oA2, oB], q, 2, 0.0)
+    e = math.exp(math.log(3.0) / math.sqrt(3.0))
+    assert np.allclose(al2[0], [e / (e + 1.0), 1.0 / (e + 1.0)], rtol=0, atol=1e-15), al2
+    # eps is added to the mean of squares: eps = 3 makes o_A's RMS 2 and its score ln 3 / 2
+    _, al3 = orc.forward_fullrms([oA, oB], q, 2, 3.0)
+    zB = 0.0
+    zA = math.log(3.0) / 2.0
+    wA = math.exp(zA) / (math.exp(zA) + math.exp(zB))
+    assert abs(al3[0, 0] - wA) < 1e-15, al3
+
+
+def _worked_keys():
+    """The worked example's keys (1, 0) and (0, 1) as separate key rows."""
+    return np.array([[1.0, 0.0]]), np.array([[0.0, 1.0]])
+
+
+def pin_keys_worked_example(orc):
+    """Separate-key read ([Paper] App. C.1: each source's key is its own r-wide vector,
+    RMS-normalised). With the worked example's keys (1, 0) and (0, 1) held apart from the
+    values and q = (ln 3 / sqrt 2, 0), the weights are (3/4, 1/4) whatever the values hold,
+    their last coordinates included, and h = 3/4 o_A + 1/4 o_B."""
+    q = np.array([math.log(3.0) / math.sqrt(2.0), 0.0])
+    kA, kB = _worked_keys()
+    oA = np.array([[4.0, -1.0, 7.0, -2.0, 0.5]])
+    oB = np.array([[0.0, 3.0, 5.0, 3.0, -8.0]])
+    h, al = orc.forward_keys([oA, oB], [kA, kB], q, 2, 0.0)
+    assert np.allclose(al[0], [0.75, 0.25], rtol=0, atol=1e-15), al
+    assert np.allclose(h[0], 0.75 * oA[0] + 0.25 * oB[0], rtol=0, atol=1e-14), h
+
+
+def pin_keys_equal_tail_is_slice_read(orc):
+    """When each source's key is a copy of its own last r coordinates the separate-key read is
+    the sliced read ([Paper] §3.3 vs App. C.1). The keys sit in wider arrays (row stride > r),
+    so the key stride is exercised too."""
+    rng = _rng(18)
+    T, d, r, n = 5, 12, 4, 3
+    srcs = _rand_sources(rng, n, T, d)
+    keys = []
+    for s in srcs:
+        k = rng.standard_normal((T, r + 3))
+        k[:, :r] = s[:, d - r:]
+        keys.append(k)
+    q = rng.standard_normal(r)
+    h, al = orc.forward_keys(srcs, keys, q, r, 1e-6)
+    h2, al2 = orc.forward(srcs, q, r, 1e-6)
+    assert np.allclose(al, al2, rtol=0, atol=1e-15) and np.allclose(h, h2, rtol=1e-14,
+                                                                     atol=1e-14)
+
+
+def pin_keys_values_do_not_route(orc):
+    """With separate keys the values only carry content: changing every value leaves the
+    weights unchanged, and h is linear in the values."""
+    rng = _rng(19)
+    T, d, r, n = 4, 6, 3, 4
+    srcs = _rand_sources(rng, n, T, d)
+    other = _rand_sources(rng, n, T, d)
+    keys = _rand_sources(rng, n, T, r)
+    q = rng.standard_normal(r)
+    h1, al1 = orc.forward_keys(srcs, keys, q, r, 1e-6)
+    h2, al2 = orc.forward_keys(other, keys, q, r, 1e-6)
+    assert np.array_equal(al1, al2)
+    both = [a + b for a, b in zip(srcs, other)]
+    h3, _ = orc.forward_keys(both, keys, q, r, 1e-6)
+    assert np.allclose(h3, h1 + h2, rtol=1e-13, atol=1e-13)
+
+
 def pin_nan_on_zero_slice(orc):
     """[Explainer]: eps > 0 prevents division by zero. At eps = 0 an all-zero slice gives 0/0,
     and the read returns NaN for that token rather than a made-up value."""

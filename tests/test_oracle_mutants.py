@@ -45,6 +45,16 @@ MUTANTS = {
                           "for (int j = 0; j < d; ++j) g_dot_diff += g[j] * (o[j]);\n      const double dz = a[i]"),
     "bwd_dq_unnormalised": ("dq[j] += dz * (k / rho[i]);", "dq[j] += dz * k;"),
     "bwd_dq_transposed_slot": ("gi[d - r + j] += dz", "gi[d - 1 - j] += dz"),
+    "fullrms_mean_over_r": ("const double rho_d = std::sqrt(sum_sq / d + eps);",
+                            "const double rho_d = std::sqrt(sum_sq / r + eps);"),
+    "fullrms_eps_outside": ("const double rho_d = std::sqrt(sum_sq / d + eps);",
+                            "const double rho_d = std::sqrt(sum_sq / d) + eps;"),
+    "keys_from_value_tail": ("const double* k = row_of(key[i], key_ld[i], t);",
+                             "const double* k = row_of(src[i], ld[i], t) + d - r;"),
+    "keys_first_row_only": ("const double* k = row_of(key[i], key_ld[i], t);",
+                            "const double* k = row_of(key[i], key_ld[i], 0);"),
+    "keys_rms_over_d": ("const double rho = std::sqrt(sum_sq / r + eps);\n      double zi",
+                        "const double rho = std::sqrt(sum_sq / d + eps);\n      double zi"),
 }
 
 
