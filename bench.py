@@ -252,6 +252,32 @@ def rows_backward(torch, lrar, ev, reps):
     return res
 
 
+def rows_read_variants(torch, lrar, ev, reps):
+    """The full-width-RMS control read and the separate-key read on the full-routing shape
+    (T = 16384, d = 1024, bf16), at the widest site (n = 49) and a middle one (n = 13): the
+    control at r = 64, the separate keys at r = 32 (the pages' projected rank) and r = 64.
+    The separate-key read also reads n keys of r elements per token."""
+    T, d, r = 8 * 2048, 1024, 64
+    srcs = gen_sources(torch, 49, T, d, (0.5, 2.0), seed=5000, dtype=torch.bfloat16)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    q = gen_queries(torch, 1, r, seed=5001)[0]
+    for n in (13, 49):
+        ms = time_calls(torch, ev, lrar.lrar_forward_fullrms(
+            srcs[:n], q, r, 1e-6, out=out, prepare=True), reps)
+        res[f"fullrms_r{r}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2))
+    for rk in (32, 64):
+        keys = gen_sources(torch, 49, T, rk, (0.5, 2.0), seed=5100 + rk, dtype=torch.bfloat16)
+        qk = gen_queries(torch, 1, rk, seed=5002 + rk)[0]
+        for n in (13, 49):
+            ms = time_calls(torch, ev, lrar.lrar_forward_keys(
+                srcs[:n], keys[:n], qk, rk, 1e-6, out=out, prepare=True), reps)
+            res[f"keys_r{rk}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2) + 2 * n * rk * T)
+        del keys
+    del srcs, out
+    return res
+
+
 # ---- the CPU baseline: the oracle on a bounded sample -------------------------------------------
 
 def cpu_baseline(torch, budget_s=12.0):
@@ -357,7 +383,8 @@ def main():
     if not args.no_rows:
         for name, fn in (("block_routing_d2048", rows_block_routing),
                          ("production_d7168", rows_production),
-                         ("backward_d4096", rows_backward)):
+                         ("backward_d4096", rows_backward),
+                         ("read_variants_d1024", rows_read_variants)):
             log(f"bench: row {name}")
             rows[name] = fn(torch, lrar, ev, args.reps)
             torch.cuda.empty_cache()

@@ -85,6 +85,32 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
                          const float* q, void* out, int64_t out_ld, float* alpha,
                          int64_t alpha_ld, int32_t variant, void* stream);
 
+/* The full-width-RMS control read (LR-AttnRes paper §4.4, Eq. 13 "control"; App. B.1): the
+ * key of source i is its last r coordinates divided by the RMS of the whole row,
+ *     kbar_i = tail_r(o_i) / sqrt(||o_i||^2 / d + eps),   z_i = q . kbar_i,
+ * and h = sum_i softmax_i(z) o_i as in lrar_forward. Arguments as for lrar_forward; always one
+ * pass over the sources. LRAR_ERR_UNSUPPORTED for rows wider than the online variant covers. */
+lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                 int32_t n, const void* const* src, const int64_t* src_ld,
+                                 const float* q, void* out, int64_t out_ld, float* alpha,
+                                 int64_t alpha_ld, void* stream);
+
+/* The separate-key read, the read side of Projected LR-AttnRes (LR-AttnRes paper App. C.1:
+ * each source has its own r-wide key, RMS-normalised; App. C.2: a source then carries d + r
+ * elements). Source i's value is src[i] (d wide) and its key the first r columns of key[i]:
+ *     z_i = q . k_i / sqrt(||k_i||^2 / r + eps),   h = sum_i softmax_i(z) o_i.
+ *   key, key_ld : host arrays of n device pointers [T, key_ld[i] >= r] of type io (1 <= r <= d).
+ * Other arguments as for lrar_forward; one pass over the sources and keys. Served for r <= 64
+ * with any key alignment, and for r <= 512 when r is a multiple of the per-lane key piece
+ * (r / 32 or r / 64 rounded up to a power of two) and the key rows are aligned to that piece
+ * (16 bytes at most); LRAR_ERR_UNSUPPORTED otherwise, or for rows wider than the online variant
+ * covers. */
+lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                              int32_t n, const void* const* src, const int64_t* src_ld,
+                              const void* const* key, const int64_t* key_ld, const float* q,
+                              void* out, int64_t out_ld, float* alpha, int64_t alpha_ld,
+                              void* stream);
+
 /* Phase 1 of the two-phase schedule (AttnRes technical-report summary, "Method"; LR-AttnRes
  * paper §3.4): nq site queries against the same n cached sources. For query s, token t:
  *     m[s][t]   = max_i z_si  rounded to float32,

@@ -70,6 +70,58 @@ def test_forward_empty_is_ok_without_device(L):
     assert fwd(L, T=0) == lrar.LRAR_OK
 
 
+def fwd_full(L, T=4, d=8, r=4, eps=1e-6, io=1, n=2, ld=8, q=FAKE, out=FAKE * 2, out_ld=8,
+             alpha=None, alpha_ld=0):
+    p, l = _src(n, ld)
+    return L.lrar_forward_fullrms(T, d, r, eps, io, n, p, l, q, out, out_ld, alpha, alpha_ld,
+                                  None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(r=0), dict(r=9), dict(eps=-1.0), dict(io=7), dict(n=0), dict(n=65),
+    dict(ld=7), dict(q=None), dict(out=None), dict(out_ld=7), dict(alpha=FAKE * 3, alpha_ld=1),
+    dict(out=FAKE),
+])
+def test_forward_fullrms_rejects(L, kw):
+    assert fwd_full(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_last_error().decode().startswith("lrar_forward_fullrms")
+
+
+def test_forward_fullrms_limits(L):
+    assert fwd_full(L, T=0) == lrar.LRAR_OK
+    assert fwd_full(L, T=0, d=16392, r=16, ld=16392, out_ld=16392) == lrar.LRAR_ERR_UNSUPPORTED
+
+
+def fwd_keys(L, T=4, d=8, r=4, io=1, n=2, ld=8, key=FAKE * 4, key_ld=8, keys=True, q=FAKE,
+             out=FAKE * 2, out_ld=8):
+    p, l = _src(n, ld)
+    k = max(n, 1)
+    kp = (ctypes.c_void_p * k)(*([key] * k)) if keys else None
+    kl = (ctypes.c_int64 * k)(*([key_ld] * k)) if keys else None
+    return L.lrar_forward_keys(T, d, r, 1e-6, io, n, p, l, kp, kl, q, out, out_ld, None, 0, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(keys=False), dict(key=None), dict(key_ld=3), dict(key=FAKE * 2),  # aliases out
+    dict(r=0), dict(r=9), dict(q=None), dict(n=0),
+])
+def test_forward_keys_rejects(L, kw):
+    assert fwd_keys(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_last_error().decode().startswith("lrar_forward_keys")
+
+
+def test_forward_keys_limits(L):
+    assert fwd_keys(L, T=0) == lrar.LRAR_OK
+    # r = 96 takes pieces of 4 (8-byte loads): served at 8-byte alignment, not at 2
+    big = dict(T=0, d=1024, r=96, ld=1024, out_ld=1024, key_ld=96)
+    assert fwd_keys(L, **big) == lrar.LRAR_OK
+    assert fwd_keys(L, key=FAKE * 4 + 2, **big) == lrar.LRAR_ERR_UNSUPPORTED
+    # r = 64 needs no alignment beyond the element's
+    assert fwd_keys(L, key=FAKE * 4 + 2, **dict(big, r=64, key_ld=64)) == lrar.LRAR_OK
+    # r = 1000 is wider than a spread key reaches
+    assert fwd_keys(L, **dict(big, r=1000, key_ld=1000)) == lrar.LRAR_ERR_UNSUPPORTED
+
+
 def test_online_too_wide_is_unsupported(L):
     # 2049 units of 8 bf16 are 33 chunks of 64 lanes, one more than a register tile holds
     assert fwd(L, d=16392, r=16, ld=16392, out_ld=16392, variant=2) == \

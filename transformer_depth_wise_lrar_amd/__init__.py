@@ -61,6 +61,10 @@ def lib():
                 raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
             L.lrar_forward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
                                        _vp, _i64, _vp, _i64, _i32, _vp]
+            L.lrar_forward_fullrms.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
+                                               _vp, _vp, _i64, _vp, _i64, _vp]
+            L.lrar_forward_keys.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
+                                            _vpp, _i64p, _vp, _vp, _i64, _vp, _i64, _vp]
             L.lrar_forward_stats.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
                                              _i32, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i64,
                                              _i64, _vp]
@@ -72,8 +76,8 @@ def lib():
             L.lrar_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
-            for fn in ("lrar_forward", "lrar_forward_stats", "lrar_merge", "lrar_backward",
-                       "lrar_copy"):
+            for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
+                       "lrar_forward_stats", "lrar_merge", "lrar_backward", "lrar_copy"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -85,7 +89,8 @@ def lib():
 
 def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
-    return ["lrar_forward", "lrar_forward_stats", "lrar_merge", "lrar_backward",
+    return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
+            "lrar_merge", "lrar_backward",
             "lrar_backward_workspace_size", "lrar_copy", "lrar_status_string",
             "lrar_last_error", "lrar_version"]
 
@@ -216,6 +221,57 @@ def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=N
     args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op, old, ap, ald,
             VARIANTS[variant], _stream(stream))
     return _run(lib().lrar_forward, args, (out, alpha), (srcs, q, out, alpha), prepare)
+
+
+def _read_outputs(srcs, T, d, out, alpha):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, d), dtype=srcs[0].dtype, device=srcs[0].device)
+    _need(out, (T, d), srcs[0].dtype, "out")
+    if alpha is True:
+        alpha = torch.empty((T, len(srcs)), dtype=torch.float32, device=srcs[0].device)
+    if alpha is False:
+        alpha = None
+    if alpha is not None:
+        _need(alpha, (T, len(srcs)), torch.float32, "alpha")
+    return out, alpha
+
+
+def lrar_forward_fullrms(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=None,
+                         stream=None, prepare: bool = False):
+    """The full-width-RMS control read: the key tail_r(o_i) is divided by the RMS of the whole
+    row o_i. Arguments and result as for lrar_forward (one pass, no variant)."""
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    _query(q, r)
+    out, alpha = _read_outputs(srcs, T, d, out, alpha)
+    op, old = _rows(out, "out")
+    ap, ald = _rows(alpha, "alpha") if alpha is not None else (None, 0)
+    args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op, old, ap, ald,
+            _stream(stream))
+    return _run(lib().lrar_forward_fullrms, args, (out, alpha), (srcs, q, out, alpha), prepare)
+
+
+def lrar_forward_keys(srcs: Sequence, keys: Sequence, q, r: int, eps: float = 1e-6, out=None,
+                      alpha=None, stream=None, prepare: bool = False):
+    """The separate-key read: source i routes by the RMS-normalised first r columns of keys[i]
+    ([T, >= r], the sources' dtype) and contributes its full row srcs[i] to h. Arguments and
+    result otherwise as for lrar_forward (one pass, no variant)."""
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    if len(keys) != len(srcs):
+        raise ValueError("one key tensor per source")
+    kptrs = (ctypes.c_void_p * max(len(keys), 1))()
+    klds = (ctypes.c_int64 * max(len(keys), 1))()
+    for i, k in enumerate(keys):
+        _need(k, (T, r), srcs[0].dtype, f"keys[{i}]")
+        kptrs[i], klds[i] = _rows(k, f"keys[{i}]")
+    _query(q, r)
+    out, alpha = _read_outputs(srcs, T, d, out, alpha)
+    op, old = _rows(out, "out")
+    ap, ald = _rows(alpha, "alpha") if alpha is not None else (None, 0)
+    args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, kptrs, klds, q.data_ptr(), op, old,
+            ap, ald, _stream(stream))
+    return _run(lib().lrar_forward_keys, args, (out, alpha), (srcs, keys, q, out, alpha),
+                prepare)
 
 
 def lrar_forward_stats(srcs: Sequence, qs, r: int, eps: float = 1e-6, acc_dtype=None,

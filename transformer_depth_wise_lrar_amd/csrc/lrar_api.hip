@@ -83,18 +83,14 @@ bool overlaps_source(const void* p, const lrar::SrcList& S, int n) {
   return false;
 }
 
-}  // namespace
-
-extern "C" {
-
-lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
-                         const void* const* src, const int64_t* src_ld, const float* q, void* out,
-                         int64_t out_ld, float* alpha, int64_t alpha_ld, int32_t variant,
-                         void* stream) {
-  const char* fn = "lrar_forward";
+// Checks the arguments every forward read shares and fills the parameter block; use_vec is
+// the unit width the sources and out allow (16-byte units, or single elements).
+lrar_status check_read(const char* fn, int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                       int32_t n, const void* const* src, const int64_t* src_ld, const float* q,
+                       void* out, int64_t out_ld, float* alpha, int64_t alpha_ld,
+                       lrar::ReadParams& p, int& use_vec) {
   lrar_status st = check_shape(fn, T, d, r, eps, io);
   if (st != LRAR_OK) return st;
-  lrar::ReadParams p;
   std::memset(&p, 0, sizeof(p));
   bool vec_ok = true;
   st = check_sources(fn, T, d, io, n, 1, src, src_ld, p.src, vec_ok);
@@ -106,14 +102,45 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
     return fail(LRAR_ERR_INVALID, "%s: out aliases a source", fn);
   if (alpha != nullptr && alpha_ld < n)
     return fail(LRAR_ERR_INVALID, "%s: alpha_ld = %lld < n = %d", fn, (long long)alpha_ld, n);
-  if (variant < LRAR_VARIANT_AUTO || variant > LRAR_VARIANT_ONLINE)
-    return fail(LRAR_ERR_INVALID, "%s: unknown variant %d", fn, variant);
   const int vec = vec_of(io);
   if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
-  const int use_vec = vec_ok ? vec : 1;
+  use_vec = vec_ok ? vec : 1;
+  p.n = n;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.q = q;
+  p.out = out;
+  p.out_ld = out_ld;
+  p.alpha = alpha;
+  p.alpha_ld = alpha_ld;
+  return LRAR_OK;
+}
+
+// A row fits a register tile when it has at most tile_max_chunks() chunks of 64 units.
+bool row_fits_tile(int32_t d, int use_vec) {
   const int nur = (d + use_vec - 1) / use_vec;
-  // A row fits a register tile when it has at most tile_max_chunks() chunks of 64 units.
-  const bool tile_fits = (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_chunks();
+  return (nur + lrar::kWave - 1) / lrar::kWave <= lrar::tile_max_chunks();
+}
+
+}  // namespace
+
+extern "C" {
+
+lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
+                         const void* const* src, const int64_t* src_ld, const float* q, void* out,
+                         int64_t out_ld, float* alpha, int64_t alpha_ld, int32_t variant,
+                         void* stream) {
+  const char* fn = "lrar_forward";
+  lrar::ReadParams p;
+  int use_vec = 1;
+  lrar_status st = check_read(fn, T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
+                              alpha_ld, p, use_vec);
+  if (st != LRAR_OK) return st;
+  if (variant < LRAR_VARIANT_AUTO || variant > LRAR_VARIANT_ONLINE)
+    return fail(LRAR_ERR_INVALID, "%s: unknown variant %d", fn, variant);
+  const bool tile_fits = row_fits_tile(d, use_vec);
   lrar::ReadKind kind;
   if (variant == LRAR_VARIANT_ONLINE) {
     if (!tile_fits)
@@ -127,20 +154,73 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
     kind = tile_fits ? lrar::ReadKind::kOnline : lrar::ReadKind::kTwoPass;
   }
   if (T == 0) return LRAR_OK;
-  p.n = n;
-  p.d = d;
-  p.r = r;
-  p.T = T;
-  p.eps = eps;
-  p.q = q;
-  p.out = out;
-  p.out_ld = out_ld;
-  p.alpha = alpha;
-  p.alpha_ld = alpha_ld;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = tile_fits ? lrar::launch_tile(p, kind, io == LRAR_BF16, use_vec, 0, hs)
                                  : lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0, hs);
   return device_status(e, fn);
+}
+
+lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                 int32_t n, const void* const* src, const int64_t* src_ld,
+                                 const float* q, void* out, int64_t out_ld, float* alpha,
+                                 int64_t alpha_ld, void* stream) {
+  const char* fn = "lrar_forward_fullrms";
+  lrar::ReadParams p;
+  int use_vec = 1;
+  lrar_status st = check_read(fn, T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
+                              alpha_ld, p, use_vec);
+  if (st != LRAR_OK) return st;
+  if (!row_fits_tile(d, use_vec))
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: the control read holds a whole row in registers; "
+                "d = %d is too wide on this path", fn, d);
+  if (T == 0) return LRAR_OK;
+  return device_status(lrar::launch_tile_fullrms(p, io == LRAR_BF16, use_vec,
+                                                 static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                              int32_t n, const void* const* src, const int64_t* src_ld,
+                              const void* const* key, const int64_t* key_ld, const float* q,
+                              void* out, int64_t out_ld, float* alpha, int64_t alpha_ld,
+                              void* stream) {
+  const char* fn = "lrar_forward_keys";
+  lrar::ReadParams p;
+  int use_vec = 1;
+  lrar_status st = check_read(fn, T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
+                              alpha_ld, p, use_vec);
+  if (st != LRAR_OK) return st;
+  if (key == nullptr || key_ld == nullptr) return fail(LRAR_ERR_INVALID, "%s: null key table", fn);
+  lrar::SrcList keys;
+  std::memset(&keys, 0, sizeof(keys));
+  // Largest power of two (up to 16 bytes) that every key row start is a multiple of.
+  uintptr_t align = 16;
+  for (int i = 0; i < n; ++i) {
+    if (key[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: key[%d] is null", fn, i);
+    if (key_ld[i] < r)
+      return fail(LRAR_ERR_INVALID, "%s: key_ld[%d] = %lld < r = %d", fn, i,
+                  (long long)key_ld[i], r);
+    if (key[i] == out && out != nullptr)
+      return fail(LRAR_ERR_INVALID, "%s: out aliases key[%d]", fn, i);
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(key[i]) |
+                           static_cast<uintptr_t>(key_ld[i]) * esize(io);
+    while (align > 1 && (bits & (align - 1)) != 0) align >>= 1;
+    keys.ptr[i] = key[i];
+    keys.ld[i] = key_ld[i];
+  }
+  if (!row_fits_tile(d, use_vec))
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: the read holds a whole row in registers; d = %d is "
+                "too wide on this path", fn, d);
+  p.key_piece = lrar::tile_keys_piece(r, static_cast<int>(align), static_cast<int>(esize(io)),
+                                      use_vec);
+  if (p.key_piece == 0)
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: r = %d is not served with keys aligned to %d bytes "
+                "on the %s path (r <= 64, or r <= 512 divisible by its piece with aligned rows)",
+                fn, r, static_cast<int>(align), use_vec > 1 ? "vector" : "element");
+  if (T == 0) return LRAR_OK;
+  return device_status(lrar::launch_tile_keys(p, keys, io == LRAR_BF16, use_vec,
+                                              static_cast<hipStream_t>(stream)),
+                       fn);
 }
 
 lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,

@@ -29,7 +29,12 @@ struct ReadParams {
   int64_t acc_ld;
   float* m_out;  // nullable
   float* l_out;  // nullable
+  // separate-key read only: the spread key piece chosen by tile_keys_piece
+  int key_piece;
 };
+
+// A spread key piece of ks elements per lane, reduced row-locally (rowred) or over the lanes.
+constexpr int key_piece_code(int ks, bool rowred) { return 2 * ks + (rowred ? 1 : 0); }
 
 enum class ReadKind { kTwoPass, kOnline, kMerge };
 
@@ -75,6 +80,13 @@ hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec,
 hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
                        hipStream_t s);
 int tile_max_chunks();
+// The full-width-RMS control read and the separate-key read on register tiles (one pass).
+hipError_t launch_tile_fullrms(const ReadParams& p, int io_bf16, int vec, hipStream_t s);
+hipError_t launch_tile_keys(const ReadParams& p, const SrcList& keys, int io_bf16, int vec,
+                            hipStream_t s);
+// Spread key piece for a separate key of r elements whose rows all start at multiples of
+// align_bytes (a power of two), with esize-byte elements; 0 if none serves this key.
+int tile_keys_piece(int r, int align_bytes, int esize, int vec);
 
 hipError_t launch_stats(const StatsParams& p, int io_bf16, int vec, int acc_bf16, hipStream_t s);
 

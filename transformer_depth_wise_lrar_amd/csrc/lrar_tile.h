@@ -9,7 +9,18 @@
 
 namespace lrar {
 
-enum TileMode : int { kTileOnline = 0, kTileTwoPass = 1, kTileMerge = 2 };
+enum TileMode : int {
+  kTileOnline = 0,   // the read, one pass
+  kTileTwoPass = 1,  // the read, key slices first
+  kTileMerge = 2,    // Phase 2: the online pass started from Phase-1 statistics
+  kTileFullRms = 3,  // the full-width-RMS control read, one pass
+  kTileKeys = 4      // the separate-key read, one pass
+};
+
+// Per-source key table: only the separate-key read has one (an empty argument otherwise).
+struct NoKeyTable {};
+template <int MODE>
+using KeyTable = typename std::conditional<MODE == kTileKeys, SrcList, NoKeyTable>::type;
 
 constexpr double kLazyRescale = 8.0;
 
@@ -162,16 +173,19 @@ struct TileGeom {
 };
 
 // Loads one source's tile. KEYS_ONLY: only the key (the spread pieces, or the key units when
-// KS = 0). ROWS: whether the row units are loaded at all.
-template <bool KEYS_ONLY, typename IO, int VEC, int NU, int R, int KS>
+// KS = 0). SEP: the spread key pieces come from the source's own key rows (kbase, row stride
+// kld) instead of the value row's last r columns.
+template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
 __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
                                            const IO* __restrict__ base, int64_t ld,
-                                           const TileGeom& g) {
+                                           const TileGeom& g, const IO* kbase = nullptr,
+                                           int64_t kld = 0) {
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const IO* rowp = base + (g.r0 + j) * ld;  // wave-uniform: lane offsets stay 32-bit
     if constexpr (KS > 0) {
-      if (j < g.nrow && g.lane * KS < g.r) st.kp[j].load(rowp + g.c0 + g.lane * KS);
+      const IO* keyp = SEP ? kbase + (g.r0 + j) * kld : rowp + g.c0;
+      if (j < g.nrow && g.lane * KS < g.r) st.kp[j].load(keyp + g.lane * KS);
       else st.kp[j].zero();
     }
     if constexpr (!(KEYS_ONLY && KS > 0)) {
@@ -213,8 +227,40 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
   }
 }
 
-// The same from this lane's spread key piece (KS > 0); qs holds the matching query values
-// (0 beyond the key).
+// This lane's share of q . k over the key columns and of o . o over the whole row, for the
+// full-width-RMS control: every unit slot of the row counts toward the square sum.
+template <typename IO, int VEC, int NU>
+__device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
+                                                 const float* __restrict__ q_lds,
+                                                 const TileGeom& g, double& dot, double& ss) {
+  dot = 0.0;
+  ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int u = g.unit(k);
+    if (u < g.nur) {
+      float x[VEC];
+      row[k].get(x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const double v = static_cast<double>(x[e]);
+        ss = fma(v, v, ss);
+      }
+      if (u >= g.ub) {
+        const float* qv = q_lds + (u - g.ub) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int col = u * VEC + e;
+          const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
+          dot = fma(static_cast<double>(qv[e]), kv, dot);
+        }
+      }
+    }
+  }
+}
+
+// This lane's share of q . k and k . k from its spread key piece (KS > 0); qs holds the
+// matching query values (0 beyond the key).
 template <typename IO, int KS, typename QT>
 __device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
                                                    const QT (&qs)[KS], double& dot,

@@ -19,6 +19,12 @@
 //                 per row in float64; pass 2 streams the full rows with the fixed float32
 //                 weights. The key bytes are read twice (normally from L2 the second time).
 //   kTileMerge    kTileOnline started from Phase-1 statistics (m, l, acc): lrar_merge.
+//   kTileFullRms  kTileOnline with the full-width-RMS control score (LR-AttnRes paper §4.4,
+//                 Eq. 13): the key columns are divided by the RMS of the whole row, which is
+//                 summed from the row units already in registers.
+//   kTileKeys     kTileOnline with a separate r-wide key per source (the read side of the
+//                 paper's Projected LR-AttnRes, App. C.1-C.2): the spread key pieces are
+//                 loaded from the key rows, the values from the source rows.
 //
 // Key arithmetic (float64: bf16/fp32 x fp32 products are exact in float64).
 //   KS = 0   the key is taken from the row units in registers: only the last TU unit slots of
@@ -42,7 +48,7 @@ namespace lrar {
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int R, int PF, int WPR,
           int MODE, typename ACC>
-__global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
+__global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MODE> keys) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   extern __shared__ float q_lds[];
   // Partial key sums of the waves that share a row (two slots, alternating by source).
@@ -95,6 +101,17 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
   const int64_t ntiles = (p.T + R - 1) / R;
   int parity = 0;
   const auto src_base = [&](int i) { return static_cast<const IO*>(p.src.ptr[i]); };
+  constexpr bool kSep = MODE == kTileKeys;
+  const auto key_base = [&](int i) -> const IO* {
+    if constexpr (kSep) return static_cast<const IO*>(keys.ptr[i]);
+    else return nullptr;
+  };
+  const auto key_ld = [&](int i) -> int64_t {
+    if constexpr (kSep) return keys.ld[i];
+    else return 0;
+  };
+  // Width of the mean of squares in the key's RMS: the key, or the whole row for the control.
+  const int nrm = MODE == kTileFullRms ? p.d : p.r;
   const auto set_tile = [&](TileGeom& t, int64_t tile) {
     t = g;
     t.r0 = tile * R;
@@ -185,12 +202,14 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
     for (int j = 0; j < R; ++j) {
       if constexpr (KS > 0)
         key_partial_spread<IO, KS>(st.kp[j], qs, red[2 * j], red[2 * j + 1]);
+      else if constexpr (MODE == kTileFullRms)
+        row_partial_full(st.t.u[j], q_lds, t, red[2 * j], red[2 * j + 1]);
       else
         key_partial_units<TU>(st.t.u[j], q_lds, t, red[2 * j], red[2 * j + 1]);
     }
     if constexpr (KS > 0 && ROWRED && R <= 2) {
       // the spread key sits in lanes 0..31 of every wave of the row
-      return row_scores_rowlocal<R>(red, lane, p.r, p.eps);
+      return row_scores_rowlocal<R>(red, lane, nrm, p.eps);
     } else if constexpr (KS > 0) {
       lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
     } else {
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
         parity ^= 1;
       }
     }
-    return row_scores_to_lanes<R>(red, lane, p.r, p.eps);
+    return row_scores_to_lanes<R>(red, lane, nrm, p.eps);
   };
 
   // Ring of PF + 1 stages: the item PF ahead is loading while the current one is folded in.
@@ -292,14 +311,16 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p) {
       begin_tile(t);
 #pragma unroll
       for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<false>(ring[b], src_base(b), p.src.ld[b], t);
+        if (b < n)
+          load_stage<false, kSep>(ring[b], src_base(b), p.src.ld[b], t, key_base(b), key_ld(b));
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
           if (i < n) {
             if (i + PF < n)
-              load_stage<false>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], t);
+              load_stage<false, kSep>(ring[(b + PF) % (PF + 1)], src_base(i + PF),
+                                      p.src.ld[i + PF], t, key_base(i + PF), key_ld(i + PF));
             const double z = stage_scores(ring[b], t);  // lane j: row j
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -370,7 +391,7 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, int MODE,
           typename ACC>
-hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
+hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
   constexpr int PF = tile_prefetch(NU);
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC>;
@@ -396,48 +417,89 @@ hipError_t launch_tile_t(const ReadParams& p, hipStream_t s) {
   const int64_t groups = (tiles + per_group - 1) / per_group;
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
   const int64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p, kt);
   return hipGetLastError();
 }
 
 // Key path. Spread pieces of KS elements when the key is short: preferably KS = r / 32 rounded
 // up to a power of two, so the key fits lanes 0..31 (row-local sums), else 1 or 2 elements over
 // up to 64 lanes; a piece size must divide r and keep the loads aligned. Otherwise the row
-// units, with TU = 1 when every key chunk lands in a wave's last slot.
+// units, with TU = 1 when every key chunk lands in a wave's last slot. The full-width-RMS
+// control always sums the row units (TU = NU); the separate-key read takes the piece the host
+// chose (p.key_piece, see tile_keys_piece).
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
-hipError_t launch_tile_key(const ReadParams& p, hipStream_t s) {
-  const int c0 = p.d - p.r;
-  if constexpr (VEC > 1) {
-    const auto fits = [&](int ks) { return p.r % ks == 0 && c0 % (ks < VEC ? ks : VEC) == 0; };
-    if (p.r <= 32 && fits(1)) return launch_tile_t<IO, VEC, NU, 1, 1, true, WPR, MODE, ACC>(p, s);
-    if (p.r <= 64 && fits(2)) return launch_tile_t<IO, VEC, NU, 1, 2, true, WPR, MODE, ACC>(p, s);
-    if (p.r <= 128 && fits(4)) return launch_tile_t<IO, VEC, NU, 1, 4, true, WPR, MODE, ACC>(p, s);
-    if (p.r <= 256 && fits(8)) return launch_tile_t<IO, VEC, NU, 1, 8, true, WPR, MODE, ACC>(p, s);
-    if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, false, WPR, MODE, ACC>(p, s);
-    if (p.r <= 2 * kWave && fits(2))
-      return launch_tile_t<IO, VEC, NU, 1, 2, false, WPR, MODE, ACC>(p, s);
+hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
+  if constexpr (MODE == kTileFullRms) {
+    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
+  } else if constexpr (MODE == kTileKeys) {
+    switch (p.key_piece) {
+      case key_piece_code(1, true):
+        return launch_tile_t<IO, VEC, NU, 1, 1, true, WPR, MODE, ACC>(p, kt, s);
+      case key_piece_code(1, false):
+        return launch_tile_t<IO, VEC, NU, 1, 1, false, WPR, MODE, ACC>(p, kt, s);
+      default: break;
+    }
+    if constexpr (VEC > 1) {
+      switch (p.key_piece) {
+        case key_piece_code(2, true):
+          return launch_tile_t<IO, VEC, NU, 1, 2, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(4, true):
+          return launch_tile_t<IO, VEC, NU, 1, 4, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(8, true):
+          return launch_tile_t<IO, VEC, NU, 1, 8, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(2, false):
+          return launch_tile_t<IO, VEC, NU, 1, 2, false, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(4, false):
+          return launch_tile_t<IO, VEC, NU, 1, 4, false, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(8, false):
+          return launch_tile_t<IO, VEC, NU, 1, 8, false, WPR, MODE, ACC>(p, kt, s);
+        default: break;
+      }
+    }
+    return hipErrorInvalidValue;
+  } else {
+    const int c0 = p.d - p.r;
+    if constexpr (VEC > 1) {
+      const auto fits = [&](int ks) { return p.r % ks == 0 && c0 % (ks < VEC ? ks : VEC) == 0; };
+      if (p.r <= 32 && fits(1))
+        return launch_tile_t<IO, VEC, NU, 1, 1, true, WPR, MODE, ACC>(p, kt, s);
+      if (p.r <= 64 && fits(2))
+        return launch_tile_t<IO, VEC, NU, 1, 2, true, WPR, MODE, ACC>(p, kt, s);
+      if (p.r <= 128 && fits(4))
+        return launch_tile_t<IO, VEC, NU, 1, 4, true, WPR, MODE, ACC>(p, kt, s);
+      if (p.r <= 256 && fits(8))
+        return launch_tile_t<IO, VEC, NU, 1, 8, true, WPR, MODE, ACC>(p, kt, s);
+      if (p.r <= kWave) return launch_tile_t<IO, VEC, NU, 1, 1, false, WPR, MODE, ACC>(p, kt, s);
+      if (p.r <= 2 * kWave && fits(2))
+        return launch_tile_t<IO, VEC, NU, 1, 2, false, WPR, MODE, ACC>(p, kt, s);
+    }
+    const int first_key_chunk = (c0 / VEC) / kWave;
+    if constexpr (NU > 1) {
+      if (first_key_chunk / WPR >= NU - 1)
+        return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, kt, s);
+    }
+    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
   }
-  const int first_key_chunk = (c0 / VEC) / kWave;
-  if constexpr (NU > 1) {
-    if (first_key_chunk / WPR >= NU - 1)
-      return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, s);
-  }
-  return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, s);
 }
 
 // Rows of up to 4 chunks of 64 units are held by one wave; wider rows by the 4 waves of a
 // workgroup, each taking every fourth chunk.
 template <typename IO, int VEC, int MODE, typename ACC>
-hipError_t launch_tile_nu(const ReadParams& p, hipStream_t s) {
+hipError_t launch_tile_nu(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   const int nur = (p.d + VEC - 1) / VEC;
   const int chunks = (nur + kWave - 1) / kWave;
-  if (chunks <= 1) return launch_tile_key<IO, VEC, 1, 1, MODE, ACC>(p, s);
-  if (chunks <= 2) return launch_tile_key<IO, VEC, 2, 1, MODE, ACC>(p, s);
-  if (chunks <= 4) return launch_tile_key<IO, VEC, 4, 1, MODE, ACC>(p, s);
-  if (chunks <= 8) return launch_tile_key<IO, VEC, 2, 4, MODE, ACC>(p, s);
-  if (chunks <= 16) return launch_tile_key<IO, VEC, 4, 4, MODE, ACC>(p, s);
-  if (chunks <= 32) return launch_tile_key<IO, VEC, 8, 4, MODE, ACC>(p, s);
+  if (chunks <= 1) return launch_tile_key<IO, VEC, 1, 1, MODE, ACC>(p, kt, s);
+  if (chunks <= 2) return launch_tile_key<IO, VEC, 2, 1, MODE, ACC>(p, kt, s);
+  if (chunks <= 4) return launch_tile_key<IO, VEC, 4, 1, MODE, ACC>(p, kt, s);
+  if (chunks <= 8) return launch_tile_key<IO, VEC, 2, 4, MODE, ACC>(p, kt, s);
+  if (chunks <= 16) return launch_tile_key<IO, VEC, 4, 4, MODE, ACC>(p, kt, s);
+  if (chunks <= 32) return launch_tile_key<IO, VEC, 8, 4, MODE, ACC>(p, kt, s);
   return hipErrorInvalidValue;
+}
+
+template <typename IO, int VEC, int MODE, typename ACC>
+hipError_t launch_tile_nu(const ReadParams& p, hipStream_t s) {
+  return launch_tile_nu<IO, VEC, MODE, ACC>(p, KeyTable<MODE>{}, s);
 }
 
 }  // namespace
