@@ -98,11 +98,15 @@ class Oracle:
         lib.orc_stats.argtypes = [i64, i32, i32, dbl, i32, _pp, _i64p, i32, _dp, _dp, _dp, _dp]
         lib.orc_merge.argtypes = [i64, i32, i32, dbl, _dp, _dp, _dp, i32, _pp, _i64p, _dp, _dp,
                                   i64, _dp, _dp]
+        lib.orc_merge_accumulate.argtypes = [i64, i32, i32, dbl, i32, _dp, _dp, _dp, _dp, i64,
+                                             _dp, i64, _dp, _dp, _dp, i64, _dp, _dp]
+        lib.orc_round_to_format.argtypes = [i64, _dp, i32, _dp]
         lib.orc_backward.argtypes = [i64, i32, i32, dbl, i32, _pp, _i64p, _dp, _dp, i64, _pp,
                                      _dp]
         lib.orc_backward_fullrms.argtypes = lib.orc_backward.argtypes
         for fn in ("orc_scores", "orc_forward", "orc_attnres_standard", "orc_forward_fullrms",
-                   "orc_forward_keys", "orc_stats", "orc_merge", "orc_backward", "orc_backward_fullrms"):
+                   "orc_forward_keys", "orc_merge_accumulate", "orc_round_to_format",
+                   "orc_stats", "orc_merge", "orc_backward", "orc_backward_fullrms"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -200,6 +204,35 @@ class Oracle:
                "merge")
         return out, m_out, l_out
 
+    def merge_accumulate(self, m, l, acc, b, o, q, r, eps, bits):
+        """Phase 2 with the partial-sum update fused in: b' = round(b + o) to a `bits`-bit
+        significand (b None: the block's first write), then the merge of (m [T], l [T],
+        acc [T, d]) with the single source b'. Returns (h, b', m', l')."""
+        m = np.ascontiguousarray(_f64(m))
+        l = np.ascontiguousarray(_f64(l))
+        acc = np.ascontiguousarray(_f64(acc))
+        T, d = acc.shape
+        o = np.ascontiguousarray(_f64(o))
+        if b is not None:
+            b = np.ascontiguousarray(_f64(b))
+        q = np.ascontiguousarray(_f64(q))
+        b_out = np.empty((T, d))
+        out = np.empty((T, d))
+        m_out = np.empty(T)
+        l_out = np.empty(T)
+        _check(self.lib.orc_merge_accumulate(
+            T, d, r, eps, bits, _dptr(m), _dptr(l), _dptr(acc), _dptr(b), d, _dptr(o), d,
+            _dptr(q), _dptr(b_out), _dptr(out), d, _dptr(m_out), _dptr(l_out)),
+            "merge_accumulate")
+        return out, b_out, m_out, l_out
+
+    def round_to_format(self, x, bits):
+        """x rounded to a `bits`-bit significand, ties to even (24: float32, 8: bfloat16)."""
+        x = np.ascontiguousarray(_f64(x))
+        y = np.empty_like(x)
+        _check(self.lib.orc_round_to_format(x.size, _dptr(x), bits, _dptr(y)), "round")
+        return y
+
     def _bwd(self, fn, srcs, q, dout, r, eps):
         arrs, ptrs, lds, T, d = _src_arrays(srcs)
         q = np.ascontiguousarray(_f64(q))
@@ -251,6 +284,14 @@ def forward_fullrms(*a, **k):
 
 def forward_keys(*a, **k):
     return default().forward_keys(*a, **k)
+
+
+def merge_accumulate(*a, **k):
+    return default().merge_accumulate(*a, **k)
+
+
+def round_to_format(*a, **k):
+    return default().round_to_format(*a, **k)
 
 
 def attnres_standard(*a, **k):

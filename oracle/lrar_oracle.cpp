@@ -290,6 +290,53 @@ int orc_merge(int64_t T, int d, int r, double eps, const double* m, const double
   return 0;
 }
 
+// Rounds x to the nearest number with a p-bit significand, ties to even, in a binary format
+// whose normal range starts at 2^-126 (below it the spacing stays 2^(-126 - p + 1), as for
+// subnormals): p = 24 is IEEE float32, p = 8 is bfloat16, p = 53 leaves a double of
+// magnitude >= 2^-126 unchanged.
+// Overflow is not modelled (the values here stay far below the formats' maxima).
+static double round_to_format(double x, int p) {
+  if (x == 0.0 || !std::isfinite(x)) return x;
+  int e = 0;
+  std::frexp(x, &e);  // x = f 2^e with 1/2 <= |f| < 1: the leading bit is worth 2^(e-1)
+  int lead = e - 1;
+  if (lead < -126) lead = -126;
+  const double spacing = std::ldexp(1.0, lead - (p - 1));
+  return std::nearbyint(x / spacing) * spacing;  // the default mode: nearest, ties to even
+}
+
+// Phase 2 with the partial-sum update fused in ([Paper] §3.3 "Partial-block routing": each
+// sub-layer output o updates the full-width partial sum, b <- b + o, and the key of the sum is
+// taken after the update; [AttnRes-TR] Method, Phase 2 merges the intra-block lookback). The
+// updated sum is stored in the sources' element type with a p-bit significand,
+//   b' = round_to_format(b + o, p)      (b null: the block's first write, b' = round(o)),
+// and the site merges its Phase-1 statistics with the single source b' as orc_merge does.
+// b, o are [T, *_ld]; b_out is [T, d] (row stride d) and receives b'.
+int orc_merge_accumulate(int64_t T, int d, int r, double eps, int p, const double* m,
+                         const double* l, const double* acc, const double* b, int64_t b_ld,
+                         const double* o, int64_t o_ld, const double* q, double* b_out,
+                         double* out, int64_t out_ld, double* m_out, double* l_out) {
+  if (bad_common(T, d, r, eps, 1, 1) || p < 2 || p > 53 || !o || o_ld < d || !b_out || !q)
+    return -1;
+  if (b && b_ld < d) return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < d; ++j) {
+      const double prev = b ? row_of(b, b_ld, t)[j] : 0.0;
+      b_out[t * d + j] = round_to_format(prev + row_of(o, o_ld, t)[j], p);
+    }
+  }
+  const double* srcs[1] = {b_out};
+  const int64_t lds[1] = {d};
+  return orc_merge(T, d, r, eps, m, l, acc, 1, srcs, lds, q, out, out_ld, m_out, l_out);
+}
+
+// Exposes round_to_format so tests can pin it against library conversions.
+int orc_round_to_format(int64_t count, const double* x, int p, double* y) {
+  if (count < 0 || p < 2 || p > 53 || (count > 0 && (!x || !y))) return -1;
+  for (int64_t k = 0; k < count; ++k) y[k] = round_to_format(x[k], p);
+  return 0;
+}
+
 // Backward of one read, treating every source slot as an independent input
 // ([Paper] App. B.3). With g = dL/dh for token t:
 //   Lemma 2 / §4.7:  dL/do_i = alpha_i g + alpha_i <g, o_i - h> grad_{o_i} z_i,

@@ -366,6 +366,65 @@ def pin_fullrms_at_r_equals_d(orc):
                                                                      atol=1e-14)
 
 
+def pin_round_to_format(orc):
+    """The storage rounding (IEEE round to nearest, ties to even) against library conversions:
+    numpy's float32 cast for 24 bits and torch's bfloat16 cast for 8 bits, on random values,
+    exact ties and values near 2^-126; plus hand-checked bfloat16 ties (1 + 2^-8 lies halfway
+    between 1 and 1 + 2^-7 and goes to the even 1; 1 + 3 * 2^-8 goes up to 1 + 2^-6)."""
+    import torch
+    rng = _rng(30)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                        1.0 + np.arange(-64, 64) * 2.0 ** -9, 1.0 + np.arange(-64, 64) * 2.0 ** -25,
+                        rng.standard_normal(200) * 2.0 ** -126, [0.0, -0.0, 2.0 ** -130]])
+    y24 = orc.round_to_format(x, 24)
+    assert np.array_equal(y24, x.astype(np.float32).astype(np.float64))
+    y8 = orc.round_to_format(x, 8)
+    ref8 = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(y8, ref8)
+    assert orc.round_to_format(np.array([1.0 + 2.0 ** -8]), 8)[0] == 1.0
+    assert orc.round_to_format(np.array([1.0 + 3 * 2.0 ** -8]), 8)[0] == 1.0 + 2.0 ** -6
+    normal = x[(np.abs(x) >= 2.0 ** -126) | (x == 0)]
+    assert np.array_equal(orc.round_to_format(normal, 53), normal)
+
+
+def pin_merge_accumulate_is_merge_of_updated_sum(orc):
+    """The fused Phase-2 update ([Paper] §3.3 'Partial-block routing'): the site merges its
+    statistics with b' = round(b + o), and with no earlier partial sum b' = o."""
+    rng = _rng(31)
+    T, d, r = 6, 16, 4
+    A = _rand_sources(rng, 3, T, d)
+    b = rng.standard_normal((T, d))
+    o = rng.standard_normal((T, d))
+    q = rng.standard_normal(r)
+    m, l, acc = orc.stats(A, q[None, :], r, 1e-6)
+    h, b2, m2, l2 = orc.merge_accumulate(m[0], l[0], acc[0], b, o, q, r, 1e-6, 8)
+    bref = orc.round_to_format(b + o, 8)
+    assert np.array_equal(b2, bref)
+    href, mref, lref = orc.merge(m[0], l[0], acc[0], [bref], q, r, 1e-6)
+    assert np.array_equal(h, href) and np.array_equal(m2, mref) and np.array_equal(l2, lref)
+    h0, b0, _, _ = orc.merge_accumulate(m[0], l[0], acc[0], None, o, q, r, 1e-6, 53)
+    assert np.array_equal(b0, o)
+    h0ref, _, _ = orc.merge(m[0], l[0], acc[0], [o], q, r, 1e-6)
+    assert np.array_equal(h0, h0ref)
+
+
+def pin_merge_accumulate_block_equals_forward(orc):
+    """A whole block by the two-phase schedule: Phase 1 over the completed sources A, then a
+    site after two writes o1, o2 of the current block (b = o1 + o2, unrounded at 53 bits)
+    reads exactly what one forward read over A and the sum o1 + o2 returns."""
+    rng = _rng(32)
+    T, d, r = 5, 12, 3
+    A = _rand_sources(rng, 4, T, d)
+    o1 = rng.standard_normal((T, d))
+    o2 = rng.standard_normal((T, d)) * 2.0
+    q = rng.standard_normal(r)
+    m, l, acc = orc.stats(A, q[None, :], r, 1e-6)
+    h, b, _, _ = orc.merge_accumulate(m[0], l[0], acc[0], o1, o2, q, r, 1e-6, 53)
+    href, _ = orc.forward(A + [o1 + o2], q, r, 1e-6)
+    assert np.allclose(h, href, rtol=1e-13, atol=1e-13)
+    assert np.allclose(b, o1 + o2, rtol=0, atol=0)
+
+
 def pin_fullrms_closed_form(orc):
     """[Paper] §4.4 Eq. 13 (control): the key is P_r o / sqrt(||o||^2 / d + eps), so the head
     coordinates enter through the denominator. At eps = 0, o_A = (1, 1, 1, 1) has full RMS 1

@@ -53,6 +53,15 @@ MUTANTS = {
                              "const double* k = row_of(src[i], ld[i], t) + d - r;"),
     "keys_first_row_only": ("const double* k = row_of(key[i], key_ld[i], t);",
                             "const double* k = row_of(key[i], key_ld[i], 0);"),
+    "round_truncates": ("return std::nearbyint(x / spacing) * spacing;",
+                        "return std::trunc(x / spacing) * spacing;"),
+    "round_no_subnormal_floor": ("if (lead < -126) lead = -126;", ""),
+    "mergeacc_drops_prev": ("const double prev = b ? row_of(b, b_ld, t)[j] : 0.0;",
+                            "const double prev = 0.0;"),
+    "mergeacc_routes_old_sum": ("const double* srcs[1] = {b_out};",
+                                "const double* srcs[1] = {b ? b : o};"),
+    "mergeacc_unrounded": ("b_out[t * d + j] = round_to_format(prev + row_of(o, o_ld, t)[j], p);",
+                           "b_out[t * d + j] = prev + row_of(o, o_ld, t)[j];"),
     "keys_rms_over_d": ("const double rho = std::sqrt(sum_sq / r + eps);\n      double zi",
                         "const double rho = std::sqrt(sum_sq / d + eps);\n      double zi"),
 }
