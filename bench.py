@@ -202,7 +202,8 @@ def rows_block_routing(torch, lrar, ev, reps):
 def rows_production(torch, lrar, ev, reps):
     """Production width d = 7168, T = 32768, 93 writes in 8 blocks (n <= 9): single-pass
     reads at r in {64, 1792, 7168}; the two-phase schedule of the largest block (Phase 1:
-    8 cached sources x 12 site queries; Phase 2: one merge per site with the partial sum)."""
+    8 cached sources x 12 site queries; Phase 2: one merge per site with the partial sum, and
+    the same merge with the partial-sum update b' = b + o fused in)."""
     T, d, nq = 32768, 7168, 12
     srcs = gen_sources(torch, 9, T, d, (0.5, 4.0), seed=3000, dtype=torch.bfloat16)
     out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
@@ -227,7 +228,14 @@ def rows_production(torch, lrar, ev, reps):
             m[0], l[0], acc[0], srcs[8:9], qs[0], r, 1e-6, out=out, prepare=True), reps)
         b2 = (ae * d + 8 + 2 * d + 2 * d) * T
         res[f"phase2_r{r}_acc{acc_name}"] = row_entry(ms2, b2)
-        del m, l, acc
+        # the same site with the partial-sum update fused in: b' = b + o is written and merged
+        bnew = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        ms3 = time_calls(torch, ev, lrar.lrar_merge_accumulate(
+            m[0], l[0], acc[0], srcs[8], srcs[7], qs[0], r, 1e-6, out=out, b_out=bnew,
+            prepare=True), reps)
+        b3 = (ae * d + 8 + 2 * d + 2 * d + 2 * d + 2 * d) * T
+        res[f"phase2_fused_update_r{r}_acc{acc_name}"] = row_entry(ms3, b3)
+        del m, l, acc, bnew
     del srcs, out
     return res
 

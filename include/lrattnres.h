@@ -142,6 +142,28 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
                        const int64_t* src_ld, const float* q, void* out, int64_t out_ld,
                        float* m_out, float* l_out, void* stream);
 
+/* Phase 2 with the partial-sum update fused in (LR-AttnRes paper §3.3 "Partial-block routing":
+ * each sub-layer output updates the full-width partial sum, b <- b + o, and the site routes
+ * over the updated sum; AttnRes technical-report summary, "Method", Phase 2). In one pass:
+ *     b_out = b + o                 (element type io, round to nearest even; b = 0 if NULL),
+ *     then lrar_merge of (m, l, acc) with the single extra source b_out.
+ * Reading b and o once and writing b_out replaces an update kernel plus a merge that reads
+ * b_out again.
+ *   b, b_ld       : device [T, b_ld] of type io, the block's partial sum so far, or NULL for
+ *                   the block's first write.
+ *   o, o_ld       : device [T, o_ld] of type io, the sub-layer output just written.
+ *   b_out, b_out_ld : device [T, b_out_ld] of type io; receives b + o. It may be b or o itself
+ *                   (same pointer and row stride: updated in place) but may not otherwise
+ *                   overlap them, acc or out.
+ *   Other arguments as for lrar_merge with n = 1. Rows wider than the online variant covers
+ *   return LRAR_ERR_UNSUPPORTED. */
+lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                  const float* m, const float* l, const void* acc,
+                                  lrar_dtype acc_dtype, int64_t acc_ld, const void* b,
+                                  int64_t b_ld, const void* o, int64_t o_ld, void* b_out,
+                                  int64_t b_out_ld, const float* q, void* out, int64_t out_ld,
+                                  float* m_out, float* l_out, void* stream);
+
 /* Backward of one read (LR-AttnRes paper App. B.3: Lemma 2 and Corollary 2.1), each source
  * slot treated as an independent input. With g = dout[t]:
  *     dz_i    = alpha_i <g, o_i - h>

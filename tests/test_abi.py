@@ -122,6 +122,38 @@ def test_forward_keys_limits(L):
     assert fwd_keys(L, **dict(big, r=1000, key_ld=1000)) == lrar.LRAR_ERR_UNSUPPORTED
 
 
+def merge_acc(L, T=4, d=8, r=4, io=1, acc_dtype=0, acc_ld=8, b=FAKE * 7, b_ld=8, o=FAKE * 8,
+              o_ld=8, b_out=FAKE * 9, b_out_ld=8, q=FAKE * 2, out=FAKE * 6, out_ld=8,
+              m_out=None, l_out=None):
+    return L.lrar_merge_accumulate(T, d, r, 1e-6, io, FAKE * 3, FAKE * 4, FAKE * 5, acc_dtype,
+                                   acc_ld, b, b_ld, o, o_ld, b_out, b_out_ld, q, out, out_ld,
+                                   m_out, l_out, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(r=0), dict(acc_dtype=5), dict(acc_ld=7), dict(o=None), dict(o_ld=7), dict(b_ld=7),
+    dict(b_out=None), dict(b_out_ld=7), dict(q=None), dict(out=None), dict(out_ld=7),
+    dict(m_out=FAKE * 10, l_out=FAKE * 10),
+    dict(b_out=FAKE * 8 + 16),           # partly overlaps o
+    dict(b_out=FAKE * 7, b_out_ld=16),   # starts at b with another row stride
+    dict(out=FAKE * 9),                  # out is b_out
+    dict(out=FAKE * 8 + 2),              # out overlaps o
+])
+def test_merge_accumulate_rejects(L, kw):
+    assert merge_acc(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_last_error().decode().startswith("lrar_merge_accumulate")
+
+
+def test_merge_accumulate_in_place_and_limits(L):
+    assert merge_acc(L, T=0) == lrar.LRAR_OK
+    assert merge_acc(L, T=0, b_out=FAKE * 7) == lrar.LRAR_OK   # in place over b
+    assert merge_acc(L, T=0, b_out=FAKE * 8) == lrar.LRAR_OK   # in place over o
+    assert merge_acc(L, T=0, b=None) == lrar.LRAR_OK           # the block's first write
+    wide = dict(T=0, d=16392, acc_ld=16392, b_ld=16392, o_ld=16392, b_out_ld=16392,
+                out_ld=16392)
+    assert merge_acc(L, **wide) == lrar.LRAR_ERR_UNSUPPORTED
+
+
 def test_online_too_wide_is_unsupported(L):
     # 2049 units of 8 bf16 are 33 chunks of 64 lanes, one more than a register tile holds
     assert fwd(L, d=16392, r=16, ld=16392, out_ld=16392, variant=2) == \

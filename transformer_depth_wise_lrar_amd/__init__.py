@@ -70,6 +70,9 @@ def lib():
                                              _i64, _vp]
             L.lrar_merge.argtypes = [_i64, _i32, _i32, _f64, _i32, _vp, _vp, _vp, _i32, _i64,
                                      _i32, _vpp, _i64p, _vp, _vp, _i64, _vp, _vp, _vp]
+            L.lrar_merge_accumulate.argtypes = [_i64, _i32, _i32, _f64, _i32, _vp, _vp, _vp,
+                                                _i32, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                                _vp, _vp, _i64, _vp, _vp, _vp]
             L.lrar_backward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
                                         _vp, _i64, _vpp, _i64p, _i32, _vp, _vp, ctypes.c_size_t,
                                         _vp]
@@ -77,7 +80,8 @@ def lib():
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
             for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
-                       "lrar_forward_stats", "lrar_merge", "lrar_backward", "lrar_copy"):
+                       "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
+                       "lrar_backward", "lrar_copy"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -90,7 +94,7 @@ def lib():
 def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
     return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
-            "lrar_merge", "lrar_backward",
+            "lrar_merge", "lrar_merge_accumulate", "lrar_backward",
             "lrar_backward_workspace_size", "lrar_copy", "lrar_status_string",
             "lrar_last_error", "lrar_version"]
 
@@ -340,6 +344,48 @@ def lrar_merge(m, l, acc, srcs: Sequence, q, r: int, eps: float = 1e-6, out=None
             l_out.data_ptr() if l_out is not None else None, _stream(stream))
     result = (out, m_out, l_out) if stats_out else out
     return _run(lib().lrar_merge, args, result, (m, l, acc, srcs, q, out, m_out, l_out), prepare)
+
+
+def lrar_merge_accumulate(m, l, acc, b, o, q, r: int, eps: float = 1e-6, out=None, b_out=None,
+                          stats_out: bool = False, stream=None, prepare: bool = False):
+    """Phase 2 with the partial-sum update fused in: b_out = b + o (b None: the block's first
+    write), then the merge of (m [T], l [T], acc [T, d]) with the single source b_out.
+
+    b_out may be b (or o) itself to update in place. Returns (out, b_out), or
+    (out, b_out, m', l') with stats_out=True."""
+    torch = _torch()
+    T, d = acc.shape
+    _need(acc, (T, d), None, "acc")
+    _need(m, (T,), torch.float32, "m")
+    _need(l, (T,), torch.float32, "l")
+    _need(o, (T, d), None, "o")
+    dt = o.dtype
+    io = _dtype_code(o)
+    if b is not None:
+        _need(b, (T, d), dt, "b")
+    _query(q, r)
+    if b_out is None:
+        b_out = torch.empty((T, d), dtype=dt, device=o.device)
+    _need(b_out, (T, d), dt, "b_out")
+    if out is None:
+        out = torch.empty((T, d), dtype=dt, device=o.device)
+    _need(out, (T, d), dt, "out")
+    op, old = _rows(out, "out")
+    accp, accld = _rows(acc, "acc")
+    bp, bld = _rows(b, "b") if b is not None else (None, 0)
+    obp, obld = _rows(o, "o")
+    bop, bold = _rows(b_out, "b_out")
+    m_out = l_out = None
+    if stats_out:
+        m_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
+        l_out = torch.empty((T,), dtype=torch.float32, device=acc.device)
+    args = (T, d, r, float(eps), io, m.data_ptr(), l.data_ptr(), accp, _dtype_code(acc), accld,
+            bp, bld, obp, obld, bop, bold, q.data_ptr(), op, old,
+            m_out.data_ptr() if m_out is not None else None,
+            l_out.data_ptr() if l_out is not None else None, _stream(stream))
+    result = (out, b_out, m_out, l_out) if stats_out else (out, b_out)
+    return _run(lib().lrar_merge_accumulate, args, result,
+                (m, l, acc, b, o, q, out, b_out, m_out, l_out), prepare)
 
 
 def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:

@@ -18,9 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblrattnres.so")
 SOURCES = ["lrar_api.hip", "lrar_read.hip", "lrar_tile.hip", "lrar_tile_online.hip",
-           "lrar_tile_twopass.hip", "lrar_tile_merge.hip", "lrar_stats.hip",
-           "lrar_tile_variants.hip", "lrar_stats_tile.hip", "lrar_backward.hip",
-           "lrar_backward_tile.hip"]
+           "lrar_tile_twopass.hip", "lrar_tile_merge.hip", "lrar_tile_merge_acc.hip",
+           "lrar_tile_variants.hip", "lrar_stats.hip", "lrar_stats_tile.hip",
+           "lrar_backward.hip", "lrar_backward_tile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

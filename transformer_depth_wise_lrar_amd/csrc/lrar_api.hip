@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 
 #include "../../include/lrattnres.h"
 #include "lrar_device.h"
@@ -116,6 +117,17 @@ lrar_status check_read(const char* fn, int64_t T, int32_t d, int32_t r, double e
   p.alpha = alpha;
   p.alpha_ld = alpha_ld;
   return LRAR_OK;
+}
+
+// Byte ranges of two [T, ld] row-major matrices (first d columns used; elements of es_a and
+// es_b bytes) intersect.
+bool rows_overlap(const void* a, int64_t a_ld, const void* b, int64_t b_ld, int64_t T, int32_t d,
+                  size_t es_a, size_t es_b) {
+  if (a == nullptr || b == nullptr || T == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = a0 + static_cast<uintptr_t>((T - 1) * a_ld + d) * es_a;
+  const uintptr_t b1 = b0 + static_cast<uintptr_t>((T - 1) * b_ld + d) * es_b;
+  return a0 < b1 && b0 < a1;
 }
 
 // A row fits a register tile when it has at most tile_max_chunks() chunks of 64 units.
@@ -337,6 +349,85 @@ size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n) 
   (void)n;
   if (T <= 0 || r < 1) return 0;
   return lrar::backward_workspace(T, r);
+}
+
+lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                  const float* m, const float* l, const void* acc,
+                                  lrar_dtype acc_dtype, int64_t acc_ld, const void* b,
+                                  int64_t b_ld, const void* o, int64_t o_ld, void* b_out,
+                                  int64_t b_out_ld, const float* q, void* out, int64_t out_ld,
+                                  float* m_out, float* l_out, void* stream) {
+  const char* fn = "lrar_merge_accumulate";
+  lrar_status st = check_shape(fn, T, d, r, eps, io);
+  if (st != LRAR_OK) return st;
+  if (!dtype_ok(acc_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown acc dtype", fn);
+  if (acc_ld < d) return fail(LRAR_ERR_INVALID, "%s: acc_ld = %lld < d", fn, (long long)acc_ld);
+  if (o_ld < d) return fail(LRAR_ERR_INVALID, "%s: o_ld = %lld < d", fn, (long long)o_ld);
+  if (b != nullptr && b_ld < d)
+    return fail(LRAR_ERR_INVALID, "%s: b_ld = %lld < d", fn, (long long)b_ld);
+  if (b_out_ld < d)
+    return fail(LRAR_ERR_INVALID, "%s: b_out_ld = %lld < d", fn, (long long)b_out_ld);
+  if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
+  if (T > 0 && (m == nullptr || l == nullptr || acc == nullptr || o == nullptr ||
+                b_out == nullptr || q == nullptr || out == nullptr))
+    return fail(LRAR_ERR_INVALID, "%s: null m, l, acc, o, b_out, q or out", fn);
+  if (m_out != nullptr && m_out == l_out)
+    return fail(LRAR_ERR_INVALID, "%s: m_out and l_out alias", fn);
+  const size_t es = esize(io);
+  // b_out may replace b or o in place (same start and row stride), but overlap nothing else;
+  // out overlaps none of the row buffers.
+  const auto same = [](const void* x, int64_t xl, const void* y, int64_t yl) {
+    return x == y && xl == yl;
+  };
+  if (rows_overlap(b_out, b_out_ld, o, o_ld, T, d, es, es) && !same(b_out, b_out_ld, o, o_ld))
+    return fail(LRAR_ERR_INVALID, "%s: b_out partly overlaps o", fn);
+  if (rows_overlap(b_out, b_out_ld, b, b_ld, T, d, es, es) && !same(b_out, b_out_ld, b, b_ld))
+    return fail(LRAR_ERR_INVALID, "%s: b_out partly overlaps b", fn);
+  if (rows_overlap(out, out_ld, o, o_ld, T, d, es, es) ||
+      rows_overlap(out, out_ld, b, b_ld, T, d, es, es) ||
+      rows_overlap(out, out_ld, b_out, b_out_ld, T, d, es, es))
+    return fail(LRAR_ERR_INVALID, "%s: out overlaps b, o or b_out", fn);
+  if (rows_overlap(acc, acc_ld, b_out, b_out_ld, T, d, esize(acc_dtype), es))
+    return fail(LRAR_ERR_INVALID, "%s: acc overlaps b_out", fn);
+  const int vec = vec_of(io);
+  bool vec_ok = d % vec == 0;
+  for (const auto& [ptr, ld] : {std::pair<const void*, int64_t>{o, o_ld}, {b, b_ld},
+                                {b_out, b_out_ld}, {out, out_ld}})
+    if (ptr != nullptr && (!aligned16(ptr) || ld % vec != 0)) vec_ok = false;
+  const int acc_elems_per_16 = acc_dtype == LRAR_BF16 ? 8 : 4;
+  if ((esize(acc_dtype) * vec) % 16 == 0 && (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0))
+    vec_ok = false;
+  const int use_vec = vec_ok ? vec : 1;
+  if (!row_fits_tile(d, use_vec))
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: the fused update holds a whole row in registers; "
+                "d = %d is too wide on this path", fn, d);
+  if (T == 0) return LRAR_OK;
+  lrar::ReadParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.src.ptr[0] = o;
+  p.src.ld[0] = o_ld;
+  p.n = 1;
+  p.d = d;
+  p.r = r;
+  p.T = T;
+  p.eps = eps;
+  p.q = q;
+  p.out = out;
+  p.out_ld = out_ld;
+  p.m_in = m;
+  p.l_in = l;
+  p.acc = acc;
+  p.acc_ld = acc_ld;
+  p.m_out = m_out;
+  p.l_out = l_out;
+  p.b_prev = b;
+  p.b_prev_ld = b_ld;
+  p.b_out = b_out;
+  p.b_out_ld = b_out_ld;
+  return device_status(lrar::launch_tile(p, lrar::ReadKind::kMergeAccumulate, io == LRAR_BF16,
+                                         use_vec, acc_dtype == LRAR_BF16,
+                                         static_cast<hipStream_t>(stream)),
+                       fn);
 }
 
 lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,

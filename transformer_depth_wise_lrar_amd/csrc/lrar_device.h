@@ -83,6 +83,16 @@ struct Unit<bf16_bits, 8> {
     raw = *reinterpret_cast<const u32x4*>(p);
   }
   __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
+  // Encodes 8 floats (round to nearest even) / writes the raw unit with a streaming store.
+  __device__ __forceinline__ void set(const float (&x)[8]) {
+    raw.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    raw.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    raw.z = static_cast<uint32_t>(f32_to_bf16(x[4])) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
+    raw.w = static_cast<uint32_t>(f32_to_bf16(x[6])) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+  }
+  __device__ __forceinline__ void store(bf16_bits* p) const {
+    __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
+  }
   __device__ __forceinline__ void get(float (&x)[8]) const {
     x[0] = __uint_as_float(raw.x << 16);
     x[1] = __uint_as_float(raw.x & 0xffff0000u);
@@ -105,6 +115,10 @@ struct Unit<float, 4> {
     raw = *reinterpret_cast<const f32x4*>(p);
   }
   __device__ __forceinline__ void zero() { raw = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void set(const float (&x)[4]) { raw = f32x4{x[0], x[1], x[2], x[3]}; }
+  __device__ __forceinline__ void store(float* p) const {
+    __builtin_nontemporal_store(raw, reinterpret_cast<f32x4*>(p));
+  }
   __device__ __forceinline__ void get(float (&x)[4]) const {
     x[0] = raw.x;
     x[1] = raw.y;
@@ -119,6 +133,8 @@ struct Unit<T, 1> {
   __device__ __forceinline__ void load(const T* p) { raw = *p; }
   __device__ __forceinline__ void load_cached(const T* p) { raw = *p; }
   __device__ __forceinline__ void zero() { raw = T(0); }
+  __device__ __forceinline__ void set(const float (&x)[1]) { raw = from_f32<T>(x[0]); }
+  __device__ __forceinline__ void store(T* p) const { *p = raw; }
   __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = to_f32<T>(raw); }
 };
 

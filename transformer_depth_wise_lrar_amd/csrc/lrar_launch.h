@@ -31,12 +31,17 @@ struct ReadParams {
   float* l_out;  // nullable
   // separate-key read only: the spread key piece chosen by tile_keys_piece
   int key_piece;
+  // merge with the partial-sum update fused in: b_out = b_prev + src[0] (b_prev nullable)
+  const void* b_prev;
+  int64_t b_prev_ld;
+  void* b_out;
+  int64_t b_out_ld;
 };
 
 // A spread key piece of ks elements per lane, reduced row-locally (rowred) or over the lanes.
 constexpr int key_piece_code(int ks, bool rowred) { return 2 * ks + (rowred ? 1 : 0); }
 
-enum class ReadKind { kTwoPass, kOnline, kMerge };
+enum class ReadKind { kTwoPass, kOnline, kMerge, kMergeAccumulate };
 
 // Phase-1 statistics (lrar_forward_stats).
 struct StatsParams {

@@ -14,7 +14,8 @@ enum TileMode : int {
   kTileTwoPass = 1,  // the read, key slices first
   kTileMerge = 2,    // Phase 2: the online pass started from Phase-1 statistics
   kTileFullRms = 3,  // the full-width-RMS control read, one pass
-  kTileKeys = 4      // the separate-key read, one pass
+  kTileKeys = 4,     // the separate-key read, one pass
+  kTileMergeAcc = 5  // Phase 2 with the partial-sum update b' = b + o fused in
 };
 
 // Per-source key table: only the separate-key read has one (an empty argument otherwise).

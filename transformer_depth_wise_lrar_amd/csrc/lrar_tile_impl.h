@@ -25,6 +25,10 @@
 //   kTileKeys     kTileOnline with a separate r-wide key per source (the read side of the
 //                 paper's Projected LR-AttnRes, App. C.1-C.2): the spread key pieces are
 //                 loaded from the key rows, the values from the source rows.
+//   kTileMergeAcc kTileMerge whose one extra source is the updated partial sum b' = b + o
+//                 (§3.3 "Partial-block routing"): the tiles of b and of the new output o are
+//                 added in registers, rounded to the element type, written out as b', and
+//                 scored and folded in from the registers (the key from the row units).
 //
 // Key arithmetic (float64: bf16/fp32 x fp32 products are exact in float64).
 //   KS = 0   the key is taken from the row units in registers: only the last TU unit slots of
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   };
   // Width of the mean of squares in the key's RMS: the key, or the whole row for the control.
   const int nrm = MODE == kTileFullRms ? p.d : p.r;
+  constexpr bool kMerge = MODE == kTileMerge || MODE == kTileMergeAcc;
   const auto set_tile = [&](TileGeom& t, int64_t tile) {
     t = g;
     t.r0 = tile * R;
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[j][k][e] = 0.f;
     }
-    if constexpr (MODE == kTileMerge) {
+    if constexpr (kMerge) {
       if (lane < t.nrow) {
         mref = static_cast<double>(p.m_in[t.r0 + lane]);
         mtop = mref;
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         }
       }
     }
-    if constexpr (MODE == kTileMerge) {
+    if constexpr (kMerge) {
       if (lane < t.nrow && t.w == 0) {
         const float mf = static_cast<float>(mtop);
         if (p.m_out) p.m_out[t.r0 + lane] = mf;
@@ -235,6 +240,39 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       }
     }
     return row_scores_to_lanes<R>(red, lane, nrm, p.eps);
+  };
+
+  // Scores source i's stage and folds its rows into the online-softmax accumulators.
+  const auto fold_source = [&](const Stage<IO, VEC, NU, R, KS>& st, const TileGeom& t, int i) {
+    const double z = stage_scores(st, t);  // lane j: row j
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const double zj = lane_f64(z, j);
+      if (lane == i) zk[j] = zj;
+    }
+    mtop = fmax(mtop, z);
+    // Rescale a row only when its score passes the reference by more than kLazyRescale
+    // (always on its first source, whose reference is -inf).
+    const bool grow = !(z <= mref + kLazyRescale);
+    if (__builtin_amdgcn_ballot_w64(grow && lane < R) != 0) {
+      const double sc = grow ? exp_weight(mref - z) : 1.0;
+      mref = grow ? z : mref;
+      lsum *= sc;
+      const float scf = static_cast<float>(sc);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float sj = lane_f32(scf, j);
+#pragma unroll
+        for (int k = 0; k < NU; ++k)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[j][k][e] *= sj;
+      }
+    }
+    const double ez = exp_weight(z - mref);
+    lsum += ez;
+    const float ef = static_cast<float>(ez);
+#pragma unroll
+    for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(ef, j), st.t.u[j]);
   };
 
   // Ring of PF + 1 stages: the item PF ahead is loading while the current one is folded in.
@@ -296,6 +334,52 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       }
       finish_tile(t);
     }
+  } else if constexpr (MODE == kTileMergeAcc) {
+    // one extra source, the updated partial sum b' = b + o, formed in registers
+    static_assert(KS == 0, "the key of b' is taken from the row units");
+    const IO* bprev = static_cast<const IO*>(p.b_prev);
+    IO* bout = static_cast<IO*>(p.b_out);
+    for (int64_t tile = group; tile < ntiles; tile += ngroups) {
+      TileGeom t;
+      set_tile(t, tile);
+      begin_tile(t);
+      Stage<IO, VEC, NU, R, KS>& st = ring[0];
+      load_stage<false>(st, src_base(0), p.src.ld[0], t);
+      if (bprev != nullptr) {
+        Tile<IO, VEC, NU, R> bt;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+#pragma unroll
+          for (int k = 0; k < NU; ++k) {
+            const int u = t.unit(k);
+            if (j < t.nrow && u < t.nur) bt.u[j][k].load(bprev + (t.r0 + j) * p.b_prev_ld + u * VEC);
+            else bt.u[j][k].zero();
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+#pragma unroll
+          for (int k = 0; k < NU; ++k) {
+            float x[VEC], y[VEC];
+            st.t.u[j][k].get(x);
+            bt.u[j][k].get(y);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) x[e] += y[e];
+            st.t.u[j][k].set(x);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+          const int u = t.unit(k);
+          if (j < t.nrow && u < t.nur) st.t.u[j][k].store(bout + (t.r0 + j) * p.b_out_ld + u * VEC);
+        }
+      }
+      fold_source(st, t, 0);
+      finish_tile(t);
+    }
   } else if (n == 0) {
     // a merge with no further sources: normalise the statistics
     for (int64_t tile = group; tile < ntiles; tile += ngroups) {
@@ -321,35 +405,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
             if (i + PF < n)
               load_stage<false, kSep>(ring[(b + PF) % (PF + 1)], src_base(i + PF),
                                       p.src.ld[i + PF], t, key_base(i + PF), key_ld(i + PF));
-            const double z = stage_scores(ring[b], t);  // lane j: row j
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-              const double zj = lane_f64(z, j);
-              if (lane == i) zk[j] = zj;
-            }
-            mtop = fmax(mtop, z);
-            // Rescale a row only when its score passes the reference by more than
-            // kLazyRescale (always on its first source, whose reference is -inf).
-            const bool grow = !(z <= mref + kLazyRescale);
-            if (__builtin_amdgcn_ballot_w64(grow && lane < R) != 0) {
-              const double sc = grow ? exp_weight(mref - z) : 1.0;
-              mref = grow ? z : mref;
-              lsum *= sc;
-              const float scf = static_cast<float>(sc);
-#pragma unroll
-              for (int j = 0; j < R; ++j) {
-                const float sj = lane_f32(scf, j);
-#pragma unroll
-                for (int k = 0; k < NU; ++k)
-#pragma unroll
-                  for (int e = 0; e < VEC; ++e) acc[j][k][e] *= sj;
-              }
-            }
-            const double ez = exp_weight(z - mref);
-            lsum += ez;
-            const float ef = static_cast<float>(ez);
-#pragma unroll
-            for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(ef, j), ring[b].t.u[j]);
+            fold_source(ring[b], t, i);
           }
         }
       }
@@ -430,6 +486,13 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr (MODE == kTileFullRms) {
+    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
+  } else if constexpr (MODE == kTileMergeAcc) {
+    const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
+    if constexpr (NU > 1) {
+      if (first_key_chunk / WPR >= NU - 1)
+        return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, kt, s);
+    }
     return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
   } else if constexpr (MODE == kTileKeys) {
     switch (p.key_piece) {
