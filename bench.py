@@ -241,7 +241,8 @@ def rows_production(torch, lrar, ev, reps):
 
 
 def rows_backward(torch, lrar, ev, reps):
-    """Backward of block routing: d = 4096, r = 1024, n = 10, T = 16384, fp32 gradients."""
+    """Backward of block routing: d = 4096, r = 1024, n = 10, T = 16384, with fp32 gradients
+    and with bf16 gradients."""
     T, d, r, n = 16384, 4096, 1024, 10
     srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=4000, dtype=torch.bfloat16)
     q = gen_queries(torch, 1, r, seed=4001)[0]
@@ -256,7 +257,15 @@ def rows_backward(torch, lrar, ev, reps):
         srcs, q, dout, r, 1e-6, dsrc=dsrc, dq=dq, workspace=ws, prepare=True), reps)
     nbytes = (2 * n * d + 4 * d + 4 * n * d) * T + 4 * r
     res = {f"backward_r{r}_n{n}": row_entry(ms, nbytes)}
-    del srcs, dsrc, dout
+    del dsrc
+    # bf16 gradients (dout and dsrc bf16), as the pages' own kernel writes them
+    dout16 = dout.to(torch.bfloat16)
+    dsrc16 = [torch.empty((T, d), dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+    ms16 = time_calls(torch, ev, lrar.lrar_backward_grad(
+        srcs, q, dout16, r, 1e-6, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True), reps)
+    res[f"backward_bf16_grads_r{r}_n{n}"] = row_entry(
+        ms16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r)
+    del srcs, dsrc16, dout, dout16
     return res
 
 

@@ -186,6 +186,20 @@ lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtyp
                           float* const* dsrc, const int64_t* dsrc_ld, int32_t accumulate,
                           float* dq, void* workspace, size_t workspace_bytes, void* stream);
 
+/* lrar_backward with the gradients in grad_dtype (the pages' own kernel writes bf16 source
+ * gradients: LR-AttnRes paper App. I). dout is a device [T, dout_ld] array of grad_dtype and
+ * dsrc a host array of n distinct device [T, dsrc_ld[i]] arrays of grad_dtype. Every value is
+ * computed in float32 / float64 as in lrar_backward; with LRAR_BF16 the source gradient (after
+ * the optional addition of the existing one) is rounded to nearest even once. dq stays float32.
+ * The vector path needs every dout and dsrc row 16-byte aligned. Other arguments, limits and
+ * the workspace as for lrar_backward (lrar_backward_grad with LRAR_F32 is lrar_backward). */
+lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                               int32_t n, const void* const* src, const int64_t* src_ld,
+                               const float* q, lrar_dtype grad_dtype, const void* dout,
+                               int64_t dout_ld, void* const* dsrc, const int64_t* dsrc_ld,
+                               int32_t accumulate, float* dq, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace lrar_backward needs for this shape (0 if T = 0). */
 size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n);
 

@@ -8,8 +8,8 @@ The bars (element by element):
     slack of a sum of n products (it only matters under cancellation).
   * Phase-1 statistics: m within one float32 rounding; l and acc within the float32
     accumulation bound after rescaling the oracle to the kernel's m.
-  * backward: dsrc_i within 1e-5 * max|dsrc_i ref| per source; dq within
-    1e-5 * sum_t sum_i |dz_ti| * max_j |kbar_tij|.
+  * backward: dsrc_i within 1e-5 * max|dsrc_i ref| per source (plus one bf16 ulp of the
+    value for bf16 gradients); dq within 1e-5 * sum_t sum_i |dz_ti| * max_j |kbar_tij|.
 """
 from __future__ import annotations
 
@@ -98,6 +98,13 @@ def assert_merge(y64, h_ref, w_prior, acc_norm, w_extra, extra64, io, where="mer
 
 def assert_dsrc(g64, g_ref, where="dsrc"):
     tol = np.full_like(g_ref, 1e-5 * max(float(np.abs(g_ref).max()), 1e-30))
+    _report(np.abs(g64 - g_ref), tol, where)
+
+
+def assert_dsrc_bf16(g64, g_ref, where="dsrc"):
+    """bf16 source gradients: the float32 bar of assert_dsrc plus one bf16 ulp of the value
+    (the kernel rounds its float32 result to nearest even once)."""
+    tol = ulp_bf16(g_ref) + 1e-5 * max(float(np.abs(g_ref).max()), 1e-30)
     _report(np.abs(g64 - g_ref), tol, where)
 
 

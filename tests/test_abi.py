@@ -211,6 +211,30 @@ def test_backward_rejects(L, kw):
     assert bwd(L, **kw) == lrar.LRAR_ERR_INVALID
 
 
+def bwd_grad(L, T=4, d=8, r=4, n=2, grad=1, dsrc=None, accumulate=0, dq=FAKE * 8,
+             dout=FAKE * 7):
+    p, ld = _src(n, 8)
+    dsrc = dsrc if dsrc is not None else [FAKE * (10 + i) for i in range(n)]
+    dp = (ctypes.c_void_p * n)(*dsrc)
+    dl = (ctypes.c_int64 * n)(*([8] * n))
+    return L.lrar_backward_grad(T, d, r, 1e-6, 1, n, p, ld, FAKE * 2, grad, dout, 8, dp, dl,
+                                accumulate, dq, FAKE * 9, 1 << 30, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(grad=7), dict(dsrc=[FAKE * 10, FAKE * 10]), dict(dsrc=[FAKE, FAKE * 11]),
+    dict(accumulate=2), dict(dq=None), dict(dout=FAKE * 10), dict(dout=None),
+])
+def test_backward_grad_rejects(L, kw):
+    assert bwd_grad(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_last_error().decode().startswith("lrar_backward_grad")
+
+
+def test_backward_grad_empty_is_ok(L):
+    for grad in (0, 1):
+        assert bwd_grad(L, T=0, grad=grad) == lrar.LRAR_OK
+
+
 def test_backward_workspace_size(L):
     assert L.lrar_backward_workspace_size(0, 8, 4, 2) == 0
     a = L.lrar_backward_workspace_size(16384, 4096, 1024, 10)

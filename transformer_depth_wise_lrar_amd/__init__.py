@@ -76,12 +76,15 @@ def lib():
             L.lrar_backward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
                                         _vp, _i64, _vpp, _i64p, _i32, _vp, _vp, ctypes.c_size_t,
                                         _vp]
+            L.lrar_backward_grad.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
+                                             _vp, _i32, _vp, _i64, _vpp, _i64p, _i32, _vp, _vp,
+                                             ctypes.c_size_t, _vp]
             L.lrar_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
             for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
                        "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
-                       "lrar_backward", "lrar_copy"):
+                       "lrar_backward", "lrar_backward_grad", "lrar_copy"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -94,7 +97,7 @@ def lib():
 def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
     return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
-            "lrar_merge", "lrar_merge_accumulate", "lrar_backward",
+            "lrar_merge", "lrar_merge_accumulate", "lrar_backward", "lrar_backward_grad",
             "lrar_backward_workspace_size", "lrar_copy", "lrar_status_string",
             "lrar_last_error", "lrar_version"]
 
@@ -393,27 +396,24 @@ def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
     return int(lib().lrar_backward_workspace_size(T, d, r, n))
 
 
-def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
-                  accumulate: bool = False, dq=None, workspace=None, stream=None,
-                  prepare: bool = False):
-    """Source and query gradients of one read for upstream gradient dout (fp32 [T, d]).
-
-    Returns (dsrc list of fp32 [T, d], dq fp32 [r])."""
+def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, workspace, stream,
+              prepare):
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, None)
     n = len(srcs)
     dev = srcs[0].device
+    gdt = dout.dtype
     if dsrc is None:
-        dsrc = [torch.zeros((T, d), dtype=torch.float32, device=dev) if accumulate
-                else torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(n)]
+        dsrc = [torch.zeros((T, d), dtype=gdt, device=dev) if accumulate
+                else torch.empty((T, d), dtype=gdt, device=dev) for _ in range(n)]
     if len(dsrc) != n:
         raise ValueError(f"dsrc needs {n} tensors, got {len(dsrc)}")
     _query(q, r)
-    _need(dout, (T, d), torch.float32, "dout")
+    _need(dout, (T, d), gdt, "dout")
     dptrs = (ctypes.c_void_p * max(n, 1))()
     dlds = (ctypes.c_int64 * max(n, 1))()
     for i, g in enumerate(dsrc):
-        _need(g, (T, d), torch.float32, f"dsrc[{i}]")
+        _need(g, (T, d), gdt, f"dsrc[{i}]")
         dptrs[i], dlds[i] = _rows(g, f"dsrc[{i}]")
     if dq is None:
         dq = torch.empty((r,), dtype=torch.float32, device=dev)
@@ -422,11 +422,34 @@ def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
     if workspace is None:
         workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
     gp, gld = _rows(dout, "dout")
-    args = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr(), gp, gld, dptrs, dlds,
-            int(bool(accumulate)), dq.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream(stream))
-    return _run(lib().lrar_backward, args, (dsrc, dq), (srcs, q, dout, dsrc, dq, workspace),
-                prepare)
+    head = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr())
+    if grad_code is not None:
+        head = head + (grad_code,)
+    args = head + (gp, gld, dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
+                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                   _stream(stream))
+    return _run(fn, args, (dsrc, dq), (srcs, q, dout, dsrc, dq, workspace), prepare)
+
+
+def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
+                  accumulate: bool = False, dq=None, workspace=None, stream=None,
+                  prepare: bool = False):
+    """Source and query gradients of one read for upstream gradient dout (fp32 [T, d]).
+
+    Returns (dsrc list of fp32 [T, d], dq fp32 [r])."""
+    if dout.dtype != _torch().float32:
+        raise TypeError("lrar_backward takes float32 gradients; use lrar_backward_grad")
+    return _backward(lib().lrar_backward, None, srcs, q, dout, r, eps, dsrc, accumulate, dq,
+                     workspace, stream, prepare)
+
+
+def lrar_backward_grad(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
+                       accumulate: bool = False, dq=None, workspace=None, stream=None,
+                       prepare: bool = False):
+    """lrar_backward with the gradients in dout's dtype (bf16 or fp32): dsrc are [T, d] of
+    that dtype (bf16 rounded once, after the optional accumulation); dq stays fp32 [r]."""
+    return _backward(lib().lrar_backward_grad, _dtype_code(dout), srcs, q, dout, r, eps, dsrc,
+                     accumulate, dq, workspace, stream, prepare)
 
 
 def lrar_copy(dst, src, stream=None, prepare: bool = False):

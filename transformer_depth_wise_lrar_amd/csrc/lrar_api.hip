@@ -430,14 +430,22 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
                        fn);
 }
 
-lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
-                          const void* const* src, const int64_t* src_ld, const float* q,
-                          const float* dout, int64_t dout_ld, float* const* dsrc,
+}  // extern "C"
+
+namespace {
+
+// The backward with gradients (dout, dsrc) of type grad; shared by both entry points.
+lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, double eps,
+                          lrar_dtype io, int32_t n, const void* const* src,
+                          const int64_t* src_ld, const float* q, lrar_dtype grad,
+                          const void* dout, int64_t dout_ld, void* const* dsrc,
                           const int64_t* dsrc_ld, int32_t accumulate, float* dq, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  const char* fn = "lrar_backward";
   lrar_status st = check_shape(fn, T, d, r, eps, io);
   if (st != LRAR_OK) return st;
+  if (!dtype_ok(grad)) return fail(LRAR_ERR_INVALID, "%s: unknown gradient dtype %d", fn, (int)grad);
+  // a gradient row's 16-byte units must start 16-byte aligned on the vector path
+  const int64_t grad_per_16 = 16 / static_cast<int64_t>(esize(grad));
   lrar::BwdParams p;
   std::memset(&p, 0, sizeof(p));
   bool vec_ok = true;
@@ -450,7 +458,7 @@ lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtyp
   if (T > 0 && (q == nullptr || dout == nullptr || dq == nullptr))
     return fail(LRAR_ERR_INVALID, "%s: null q, dout or dq", fn);
   const int vec = vec_of(io);
-  if (!aligned16(dout) || dout_ld % 4 != 0) vec_ok = false;
+  if (!aligned16(dout) || dout_ld % grad_per_16 != 0) vec_ok = false;
   for (int i = 0; i < n; ++i) {
     if (dsrc[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] is null", fn, i);
     if (dsrc_ld[i] < d)
@@ -460,7 +468,7 @@ lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtyp
     if (overlaps_source(dsrc[i], p.src, n))
       return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases a source", fn, i);
     if (dsrc[i] == dout) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases dout", fn, i);
-    if (!aligned16(dsrc[i]) || dsrc_ld[i] % 4 != 0) vec_ok = false;
+    if (!aligned16(dsrc[i]) || dsrc_ld[i] % grad_per_16 != 0) vec_ok = false;
     p.dsrc.ptr[i] = dsrc[i];
     p.dsrc.ld[i] = dsrc_ld[i];
   }
@@ -486,9 +494,34 @@ lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtyp
   p.accumulate = accumulate;
   p.dq = dq;
   p.workspace = workspace;
-  return device_status(lrar::launch_backward(p, io == LRAR_BF16, use_vec,
+  return device_status(lrar::launch_backward(p, io == LRAR_BF16, grad == LRAR_BF16, use_vec,
                                              static_cast<hipStream_t>(stream)),
                        fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
+                          const void* const* src, const int64_t* src_ld, const float* q,
+                          const float* dout, int64_t dout_ld, float* const* dsrc,
+                          const int64_t* dsrc_ld, int32_t accumulate, float* dq, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return backward_impl("lrar_backward", T, d, r, eps, io, n, src, src_ld, q, LRAR_F32, dout,
+                       dout_ld, reinterpret_cast<void* const*>(dsrc), dsrc_ld, accumulate, dq,
+                       workspace, workspace_bytes, stream);
+}
+
+lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                               int32_t n, const void* const* src, const int64_t* src_ld,
+                               const float* q, lrar_dtype grad_dtype, const void* dout,
+                               int64_t dout_ld, void* const* dsrc, const int64_t* dsrc_ld,
+                               int32_t accumulate, float* dq, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return backward_impl("lrar_backward_grad", T, d, r, eps, io, n, src, src_ld, q, grad_dtype,
+                       dout, dout_ld, dsrc, dsrc_ld, accumulate, dq, workspace, workspace_bytes,
+                       stream);
 }
 
 lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream) {

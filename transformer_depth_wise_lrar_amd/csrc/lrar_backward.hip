@@ -10,7 +10,8 @@
 //   3. s_i = <g, o_i> over all d (float64 sums of exact products); then
 //      dz_i = alpha_i (s_i - sum_j alpha_j s_j), which equals alpha_i <g, o_i - h>;
 //   4. dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns,
-//      optionally added to the existing gradient, written as float32;
+//      optionally added to the existing gradient, written in the gradient type (float32, or
+//      bf16 rounded to nearest even once after the optional addition);
 //   5. dz_i k_i / rho_i is accumulated into per-lane dq partials kept in registers across
 //      all rows of the wave.
 // At the end the four waves of a workgroup combine their dq partials through LDS in a fixed
@@ -29,7 +30,7 @@ constexpr int kReduceGroups = 32;
 
 // NU: units per lane that cover a row. TU: how many of the last unit slots may hold key
 // columns (the host checks that no key unit falls below slot NU - TU).
-template <typename IO, int VEC, int NU, int TU>
+template <typename IO, typename GIO, int VEC, int NU, int TU>
 __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __restrict__ block_dq) {
   constexpr int B = NU >= 4 ? 1 : (NU >= 2 ? 2 : 4);  // sources loaded together in the <g, o_i> pass
   constexpr int K0 = NU - TU;        // first unit slot that may hold key columns
@@ -58,12 +59,12 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
 
     // 2. upstream gradient row
     float gr[NU][VEC];
-    const float* grow = p.dout + row * p.dout_ld;
+    const GIO* grow = static_cast<const GIO*>(p.dout) + row * p.dout_ld;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
       const int u = lane + kWave * k;
       if (u < nur) {
-        load_f32<VEC>(grow + u * VEC, gr[k]);
+        load_grad<GIO, VEC>(grow + u * VEC, gr[k]);
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) gr[k][e] = 0.f;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
       const float c1 = lane_f32(c1f, i);
       const float c2 = lane_f32(c2f, i);
       const IO* orow = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
-      float* drow = p.dsrc.ptr[i] + row * p.dsrc.ld[i];
+      GIO* drow = static_cast<GIO*>(p.dsrc.ptr[i]) + row * p.dsrc.ld[i];
 #pragma unroll
       for (int k = 0; k < K0; ++k) {
         const int u = lane + kWave * k;
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
           for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];
           if (p.accumulate) {
             float old[VEC];
-            load_f32<VEC>(drow + u * VEC, old);
+            load_grad<GIO, VEC>(drow + u * VEC, old);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] += old[e];
           }
-          store_unit<float, VEC>(drow + u * VEC, v);
+          store_grad<GIO, VEC>(drow + u * VEC, v);
         }
       }
 #pragma unroll
@@ -162,11 +163,11 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
           }
           if (p.accumulate) {
             float old[VEC];
-            load_f32<VEC>(drow + u * VEC, old);
+            load_grad<GIO, VEC>(drow + u * VEC, old);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] += old[e];
           }
-          store_unit<float, VEC>(drow + u * VEC, v);
+          store_grad<GIO, VEC>(drow + u * VEC, v);
         }
       }
     }
@@ -248,32 +249,34 @@ int needed_tail_slots(int nu, int d, int r, int vec) {
   return nu - first_slot;
 }
 
-template <typename IO, int VEC, int NU>
+template <typename IO, typename GIO, int VEC, int NU>
 hipError_t launch_nu(const BwdParams& p, double* block_dq, int grid, int need, hipStream_t s) {
   const dim3 g(grid), b(kBlock);
   if (need <= 1 && NU >= 1) {
-    hipLaunchKernelGGL((k_backward<IO, VEC, NU, 1>), g, b, 0, s, p, block_dq);
+    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, 1>), g, b, 0, s, p, block_dq);
   } else if (need <= 2 && NU >= 2) {
-    hipLaunchKernelGGL((k_backward<IO, VEC, NU, (NU >= 2 ? 2 : NU)>), g, b, 0, s, p, block_dq);
+    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, (NU >= 2 ? 2 : NU)>), g, b, 0, s, p,
+                       block_dq);
   } else if (need <= 4 && NU >= 4) {
-    hipLaunchKernelGGL((k_backward<IO, VEC, NU, (NU >= 4 ? 4 : NU)>), g, b, 0, s, p, block_dq);
+    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, (NU >= 4 ? 4 : NU)>), g, b, 0, s, p,
+                       block_dq);
   } else {
-    hipLaunchKernelGGL((k_backward<IO, VEC, NU, NU>), g, b, 0, s, p, block_dq);
+    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, NU>), g, b, 0, s, p, block_dq);
   }
   return hipGetLastError();
 }
 
-template <typename IO, int VEC>
+template <typename IO, typename GIO, int VEC>
 hipError_t launch_bwd_t(const BwdParams& p, double* block_dq, int grid, hipStream_t s) {
   const int nu = units_per_lane<VEC>(p.d);
-  if (nu <= 1) return launch_nu<IO, VEC, 1>(p, block_dq, grid, needed_tail_slots(1, p.d, p.r, VEC), s);
-  if (nu <= 2) return launch_nu<IO, VEC, 2>(p, block_dq, grid, needed_tail_slots(2, p.d, p.r, VEC), s);
-  if (nu <= 4) return launch_nu<IO, VEC, 4>(p, block_dq, grid, needed_tail_slots(4, p.d, p.r, VEC), s);
-  if (nu <= 8) return launch_nu<IO, VEC, 8>(p, block_dq, grid, needed_tail_slots(8, p.d, p.r, VEC), s);
-  if (nu <= 16) return launch_nu<IO, VEC, 16>(p, block_dq, grid, needed_tail_slots(16, p.d, p.r, VEC), s);
+  const auto need = [&](int nu_b) { return needed_tail_slots(nu_b, p.d, p.r, VEC); };
+  if (nu <= 1) return launch_nu<IO, GIO, VEC, 1>(p, block_dq, grid, need(1), s);
+  if (nu <= 2) return launch_nu<IO, GIO, VEC, 2>(p, block_dq, grid, need(2), s);
+  if (nu <= 4) return launch_nu<IO, GIO, VEC, 4>(p, block_dq, grid, need(4), s);
+  if (nu <= 8) return launch_nu<IO, GIO, VEC, 8>(p, block_dq, grid, need(8), s);
+  if (nu <= 16) return launch_nu<IO, GIO, VEC, 16>(p, block_dq, grid, need(16), s);
   if constexpr (VEC == 1) {
-    if (nu <= 32)
-      return launch_nu<IO, VEC, 32>(p, block_dq, grid, needed_tail_slots(32, p.d, p.r, VEC), s);
+    if (nu <= 32) return launch_nu<IO, GIO, VEC, 32>(p, block_dq, grid, need(32), s);
   }
   return hipErrorInvalidValue;
 }
@@ -299,7 +302,8 @@ size_t backward_workspace(int64_t T, int r) {
   return (static_cast<size_t>(backward_grid(T)) + kReduceGroups) * static_cast<size_t>(r) * sizeof(double);
 }
 
-hipError_t launch_backward(const BwdParams& p, int io_bf16, int vec, hipStream_t s) {
+hipError_t launch_backward(const BwdParams& p, int io_bf16, int grad_bf16, int vec,
+                           hipStream_t s) {
   // The workspace holds backward_grid(T) workgroup rows; a launch may fill fewer of them.
   const int max_grid = backward_grid(p.T);
   int grid = max_grid;
@@ -308,10 +312,13 @@ hipError_t launch_backward(const BwdParams& p, int io_bf16, int vec, hipStream_t
   hipError_t e;
   if (vec > 1) {
     // the vector path runs on row tiles (lrar_backward_tile.hip)
-    e = launch_backward_tile(p, io_bf16, block_dq, max_grid, &grid, s);
+    e = launch_backward_tile(p, io_bf16, grad_bf16, block_dq, max_grid, &grid, s);
+  } else if (io_bf16) {
+    e = grad_bf16 ? launch_bwd_t<bf16_bits, bf16_bits, 1>(p, block_dq, grid, s)
+                  : launch_bwd_t<bf16_bits, float, 1>(p, block_dq, grid, s);
   } else {
-    e = io_bf16 ? launch_bwd_t<bf16_bits, 1>(p, block_dq, grid, s)
-                : launch_bwd_t<float, 1>(p, block_dq, grid, s);
+    e = grad_bf16 ? launch_bwd_t<float, bf16_bits, 1>(p, block_dq, grid, s)
+                  : launch_bwd_t<float, float, 1>(p, block_dq, grid, s);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dq_reduce1, dim3((p.r + kWave - 1) / kWave, kReduceGroups), dim3(kBlock), 0, s,

@@ -13,9 +13,10 @@
 //   then    alpha = softmax(z), sbar = sum_j alpha_j s_j, dz_i = alpha_i (s_i - sbar), which
 //           equals alpha_i <g, o_i - h>;
 //   pass B  dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns
-//           (the key units are read again, from L2), written as float32 (or added to the
-//           existing gradient); dz_i k_i / rho_i accumulates into per-lane dq partials kept in
-//           registers across the group's rows.
+//           (the key units are read again, from L2), written in the gradient type (float32,
+//           or bf16 rounded once; optionally added to the existing gradient first); dz_i k_i /
+//           rho_i accumulates into per-lane dq partials kept in registers across the group's
+//           rows.
 // The dq partials of a workgroup are combined in a fixed order and written as one float64 row
 // of the workspace; the reduction kernels of lrar_backward.hip then sum the workgroups' rows in
 // a fixed order, so dq is bitwise reproducible.
@@ -26,7 +27,7 @@
 
 namespace lrar {
 
-template <typename IO, int VEC, int NU, int TU, int WPR>
+template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR>
 __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* __restrict__ block_dq) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   constexpr int PF = 2;
@@ -65,12 +66,12 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
     g.nrow = 1;
     // upstream gradient of the row
     float gr[NU][VEC];
-    const float* grow = p.dout + row * p.dout_ld;
+    const GIO* grow = static_cast<const GIO*>(p.dout) + row * p.dout_ld;
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
       const int u = g.unit(k);
       if (u < g.nur) {
-        load_f32<VEC>(grow + u * VEC, gr[k]);
+        load_grad<GIO, VEC>(grow + u * VEC, gr[k]);
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) gr[k][e] = 0.f;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
       const float ai = lane_f32(af, i);
       const float c1 = lane_f32(c1f, i);
       const float c2 = lane_f32(c2f, i);
-      float* drow = p.dsrc.ptr[i] + row * p.dsrc.ld[i];
+      GIO* drow = static_cast<GIO*>(p.dsrc.ptr[i]) + row * p.dsrc.ld[i];
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
         const int u = g.unit(k);
@@ -172,11 +173,11 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
           }
           if (p.accumulate) {
             float old[VEC];
-            load_f32<VEC>(drow + u * VEC, old);
+            load_grad<GIO, VEC>(drow + u * VEC, old);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] += old[e];
           }
-          store_unit<float, VEC>(drow + u * VEC, v);
+          store_grad<GIO, VEC>(drow + u * VEC, v);
         }
       }
     };
@@ -253,10 +254,10 @@ int device_cus_bwd() {
   return cus;
 }
 
-template <typename IO, int VEC, int NU, int TU, int WPR>
+template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR>
 hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_blocks, int* grid_out,
                              hipStream_t s) {
-  auto kern = k_backward_tile<IO, VEC, NU, TU, WPR>;
+  auto kern = k_backward_tile<IO, GIO, VEC, NU, TU, WPR>;
   const int ub = (p.d - p.r) / VEC;
   const size_t lds = static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
   static thread_local size_t cached_lds = ~size_t(0);
@@ -280,28 +281,28 @@ hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_block
   return hipGetLastError();
 }
 
-template <typename IO, int VEC, int NU, int WPR>
+template <typename IO, typename GIO, int VEC, int NU, int WPR>
 hipError_t launch_bwd_tile_tu(const BwdParams& p, double* block_dq, int max_blocks, int* grid,
                               hipStream_t s) {
   const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
   if constexpr (NU > 1) {
     if (first_key_chunk / WPR >= NU - 1)
-      return launch_bwd_tile_t<IO, VEC, NU, 1, WPR>(p, block_dq, max_blocks, grid, s);
+      return launch_bwd_tile_t<IO, GIO, VEC, NU, 1, WPR>(p, block_dq, max_blocks, grid, s);
   }
-  return launch_bwd_tile_t<IO, VEC, NU, NU, WPR>(p, block_dq, max_blocks, grid, s);
+  return launch_bwd_tile_t<IO, GIO, VEC, NU, NU, WPR>(p, block_dq, max_blocks, grid, s);
 }
 
-template <typename IO, int VEC>
+template <typename IO, typename GIO, int VEC>
 hipError_t launch_bwd_tile_io(const BwdParams& p, double* block_dq, int max_blocks, int* grid,
                               hipStream_t s) {
   const int nur = (p.d + VEC - 1) / VEC;
   const int chunks = (nur + kWave - 1) / kWave;
-  if (chunks <= 1) return launch_bwd_tile_tu<IO, VEC, 1, 1>(p, block_dq, max_blocks, grid, s);
-  if (chunks <= 2) return launch_bwd_tile_tu<IO, VEC, 2, 1>(p, block_dq, max_blocks, grid, s);
-  if (chunks <= 4) return launch_bwd_tile_tu<IO, VEC, 4, 1>(p, block_dq, max_blocks, grid, s);
-  if (chunks <= 8) return launch_bwd_tile_tu<IO, VEC, 2, 4>(p, block_dq, max_blocks, grid, s);
-  if (chunks <= 16) return launch_bwd_tile_tu<IO, VEC, 4, 4>(p, block_dq, max_blocks, grid, s);
-  if (chunks <= 32) return launch_bwd_tile_tu<IO, VEC, 8, 4>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 1) return launch_bwd_tile_tu<IO, GIO, VEC, 1, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 2) return launch_bwd_tile_tu<IO, GIO, VEC, 2, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 4) return launch_bwd_tile_tu<IO, GIO, VEC, 4, 1>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 8) return launch_bwd_tile_tu<IO, GIO, VEC, 2, 4>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 16) return launch_bwd_tile_tu<IO, GIO, VEC, 4, 4>(p, block_dq, max_blocks, grid, s);
+  if (chunks <= 32) return launch_bwd_tile_tu<IO, GIO, VEC, 8, 4>(p, block_dq, max_blocks, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -309,10 +310,13 @@ hipError_t launch_bwd_tile_io(const BwdParams& p, double* block_dq, int max_bloc
 
 int backward_tile_max_chunks() { return 32; }
 
-hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, double* block_dq, int max_blocks,
-                                int* grid, hipStream_t s) {
-  return io_bf16 ? launch_bwd_tile_io<bf16_bits, 8>(p, block_dq, max_blocks, grid, s)
-                 : launch_bwd_tile_io<float, 4>(p, block_dq, max_blocks, grid, s);
+hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, int grad_bf16, double* block_dq,
+                                int max_blocks, int* grid, hipStream_t s) {
+  if (io_bf16)
+    return grad_bf16 ? launch_bwd_tile_io<bf16_bits, bf16_bits, 8>(p, block_dq, max_blocks, grid, s)
+                     : launch_bwd_tile_io<bf16_bits, float, 8>(p, block_dq, max_blocks, grid, s);
+  return grad_bf16 ? launch_bwd_tile_io<float, bf16_bits, 4>(p, block_dq, max_blocks, grid, s)
+                   : launch_bwd_tile_io<float, float, 4>(p, block_dq, max_blocks, grid, s);
 }
 
 }  // namespace lrar

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lrar {
 
 constexpr int kWave = 64;
@@ -28,8 +30,9 @@ struct SrcList {
   int64_t ld[kMaxSources];
 };
 
+// Gradient destinations (float32 or bf16 rows, by the entry point's gradient type).
 struct DstList {
-  float* ptr[kMaxSources];
+  void* ptr[kMaxSources];
   int64_t ld[kMaxSources];
 };
 
@@ -213,6 +216,48 @@ __device__ __forceinline__ void store_acc(A* p, const float (&x)[VEC]) {
   } else {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) p[v] = from_f32<A>(x[v]);
+  }
+}
+
+// VEC gradient values of type G (float32 or bf16) as floats, and back with round to nearest
+// even; on the vector path a row's units start at multiples of 4 * VEC (float32) or 2 * VEC
+// (bf16) bytes.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename G, int VEC>
+__device__ __forceinline__ void load_grad(const G* p, float (&x)[VEC]) {
+  if constexpr (std::is_same<G, float>::value) {
+    load_f32<VEC>(p, x);
+  } else if constexpr (VEC == 8) {
+    Unit<bf16_bits, 8> u;
+    u.load_cached(p);
+    u.get(x);
+  } else if constexpr (VEC == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xffff0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) x[e] = bf16_to_f32(p[e]);
+  }
+}
+
+template <typename G, int VEC>
+__device__ __forceinline__ void store_grad(G* p, const float (&x)[VEC]) {
+  if constexpr (std::is_same<G, float>::value) {
+    store_unit<float, VEC>(p, x);
+  } else if constexpr (VEC == 8) {
+    store_unit<bf16_bits, 8>(p, x);
+  } else if constexpr (VEC == 4) {
+    u32x2 v;
+    v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p[e] = f32_to_bf16(x[e]);
   }
 }
 

@@ -70,7 +70,7 @@ struct BwdParams {
   int64_t T;
   double eps;
   const float* q;
-  const float* dout;
+  const void* dout;  // float32 or bf16, the gradient type
   int64_t dout_ld;
   int accumulate;
   float* dq;
@@ -110,12 +110,13 @@ int backward_max_units();
 // Lanes' register window for dq partials must cover the key; false if this shape needs more.
 bool backward_supported(int d, int r, int vec);
 size_t backward_workspace(int64_t T, int r);
-hipError_t launch_backward(const BwdParams& p, int io_bf16, int vec, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, int io_bf16, int grad_bf16, int vec,
+                           hipStream_t s);
 // Row-tile backward for the vector path (lrar_backward_tile.hip): writes the dq partials of
 // *grid <= max_blocks workgroups into block_dq.
 int backward_tile_max_chunks();
-hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, double* block_dq, int max_blocks,
-                                int* grid, hipStream_t s);
+hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, int grad_bf16, double* block_dq,
+                                int max_blocks, int* grid, hipStream_t s);
 
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
