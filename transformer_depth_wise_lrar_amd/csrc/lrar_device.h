@@ -48,12 +48,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN (quietened).
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN. gfx950 converts in
+// hardware (v_cvt_pk_bf16_f32, two values per instruction).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_bits>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_bits>(u >> 16);
+  return __builtin_bit_cast(bf16_bits, static_cast<__bf16>(f));
+}
+
+// Two floats as two bfloat16 in one 32-bit word, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <typename T>
@@ -88,10 +94,10 @@ struct Unit<bf16_bits, 8> {
   __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
   // Encodes 8 floats (round to nearest even) / writes the raw unit with a streaming store.
   __device__ __forceinline__ void set(const float (&x)[8]) {
-    raw.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    raw.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-    raw.z = static_cast<uint32_t>(f32_to_bf16(x[4])) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
-    raw.w = static_cast<uint32_t>(f32_to_bf16(x[6])) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+    raw.x = pack_bf16x2(x[0], x[1]);
+    raw.y = pack_bf16x2(x[2], x[3]);
+    raw.z = pack_bf16x2(x[4], x[5]);
+    raw.w = pack_bf16x2(x[6], x[7]);
   }
   __device__ __forceinline__ void store(bf16_bits* p) const {
     __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
@@ -148,10 +154,10 @@ __device__ __forceinline__ void store_unit(T* p, const float (&x)[VEC]);
 template <>
 __device__ __forceinline__ void store_unit<bf16_bits, 8>(bf16_bits* p, const float (&x)[8]) {
   u32x4 v;
-  v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-  v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-  v.z = static_cast<uint32_t>(f32_to_bf16(x[4])) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
-  v.w = static_cast<uint32_t>(f32_to_bf16(x[6])) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+  v.x = pack_bf16x2(x[0], x[1]);
+  v.y = pack_bf16x2(x[2], x[3]);
+  v.z = pack_bf16x2(x[4], x[5]);
+  v.w = pack_bf16x2(x[6], x[7]);
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
@@ -252,8 +258,8 @@ __device__ __forceinline__ void store_grad(G* p, const float (&x)[VEC]) {
     store_unit<bf16_bits, 8>(p, x);
   } else if constexpr (VEC == 4) {
     u32x2 v;
-    v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-    v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    v.x = pack_bf16x2(x[0], x[1]);
+    v.y = pack_bf16x2(x[2], x[3]);
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
   } else {
 #pragma unroll
