@@ -76,6 +76,14 @@ __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float v) { return f32_to_bf16(v); }
 
+// Store of one output unit (16, 8 or 4 bytes), nontemporal: outputs are written once and not
+// read back by the kernel, and streaming them out keeps dirty lines from waiting in L2 and the
+// memory-side cache, whose later write-back would fall outside the kernel's own time.
+template <typename V>
+__device__ __forceinline__ void out_store(V v, V* p) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // ---- unit loads and stores ------------------------------------------------------------------
 
 // A unit of VEC elements of type T held in raw (undecoded) form.
@@ -100,7 +108,7 @@ struct Unit<bf16_bits, 8> {
     raw.w = pack_bf16x2(x[6], x[7]);
   }
   __device__ __forceinline__ void store(bf16_bits* p) const {
-    __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(p));
+    out_store(raw, reinterpret_cast<u32x4*>(p));
   }
   __device__ __forceinline__ void get(float (&x)[8]) const {
     x[0] = __uint_as_float(raw.x << 16);
@@ -126,7 +134,7 @@ struct Unit<float, 4> {
   __device__ __forceinline__ void zero() { raw = f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void set(const float (&x)[4]) { raw = f32x4{x[0], x[1], x[2], x[3]}; }
   __device__ __forceinline__ void store(float* p) const {
-    __builtin_nontemporal_store(raw, reinterpret_cast<f32x4*>(p));
+    out_store(raw, reinterpret_cast<f32x4*>(p));
   }
   __device__ __forceinline__ void get(float (&x)[4]) const {
     x[0] = raw.x;
@@ -158,18 +166,18 @@ __device__ __forceinline__ void store_unit<bf16_bits, 8>(bf16_bits* p, const flo
   v.y = pack_bf16x2(x[2], x[3]);
   v.z = pack_bf16x2(x[4], x[5]);
   v.w = pack_bf16x2(x[6], x[7]);
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  out_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 template <>
 __device__ __forceinline__ void store_unit<float, 4>(float* p, const float (&x)[4]) {
-  __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+  out_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
 }
 
 template <>
 __device__ __forceinline__ void store_unit<float, 8>(float* p, const float (&x)[8]) {
-  __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
-  __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p) + 1);
+  out_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+  out_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p) + 1);
 }
 
 template <>
@@ -260,7 +268,7 @@ __device__ __forceinline__ void store_grad(G* p, const float (&x)[VEC]) {
     u32x2 v;
     v.x = pack_bf16x2(x[0], x[1]);
     v.y = pack_bf16x2(x[2], x[3]);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+    out_store(v, reinterpret_cast<u32x2*>(p));
   } else {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) p[e] = f32_to_bf16(x[e]);
