@@ -14,9 +14,10 @@
 //   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
 //     l = sum_i e_si (float64 on the lanes), written once per row;
 //   * value pass: the row is walked in chunks of 64 units; each chunk of every source is loaded
-//     once and folded into two queries' accumulators at a time, which are written straight out
-//     (acc = sum_i e_si o_i, not normalised). The other waves of the CU keep HBM busy while a
-//     wave folds.
+//     once and folded into four queries' accumulators at a time, with the weights read from
+//     LDS; the accumulators are written straight out (acc = sum_i e_si o_i, not normalised),
+//     each store instruction covering 1 KiB of one accumulator row. The other waves of the CU
+//     keep HBM busy while a wave folds.
 // Each cached source row is read from HBM once per query group (its key again from L2), and
 // every accumulator element is written once.
 
@@ -29,14 +30,20 @@ namespace {
 
 constexpr int kStatsBlock = 768;
 constexpr int kStatsWaves = kStatsBlock / kWave;
+constexpr int kValQ = 4;  // queries folded per pass over a chunk's source units
+static_assert(kStatsMaxQ % kValQ == 0, "whole passes");
+// LDS a workgroup holds besides the staged queries (z_lds, w_lds)
+constexpr size_t kStatsStaticLds =
+    kStatsWaves * kStatsMaxQ * kStatsMaxSrc * (sizeof(double) + sizeof(float));
 
 }  // namespace
 
 template <typename IO, int VEC, typename ACC>
 __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nqg) {
   extern __shared__ float q_lds[];  // [nqg][rq]
-  // Scores of the wave's current row: z[s][i] for query s, source i.
+  // Scores of the wave's current row: z[s][i] for query s, source i; and their weights.
   __shared__ double z_lds[kStatsWaves][kStatsMaxQ][kStatsMaxSrc];
+  __shared__ __attribute__((aligned(16))) float w_lds[kStatsWaves][kStatsMaxSrc][kStatsMaxQ];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kStatsWaves + threadIdx.x / kWave;
@@ -125,58 +132,100 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
       }
     }
 
-    // ---- value pass: chunks of 64 units, every source's part of a chunk loaded together
-    Unit<IO, VEC> buf[kStatsMaxSrc];
-    const auto load_chunk = [&](Unit<IO, VEC> (&b)[kStatsMaxSrc], int c) {
-      const int u = lane + kWave * c;
+    // ---- value pass: chunks of 64 units, every source's part of a chunk loaded together. The
+    // weights go through LDS (w_lds[wave][source][query]): a few wide reads bring a source's
+    // weights for the queries of a pass to every lane, in place of one cross-lane read per
+    // weight. With bf16 sources and float32 accumulators a lane takes two runs of 4 columns
+    // (4 lane and 256 + 4 lane of the chunk) instead of one run of 8, so each 16-byte store of
+    // the accumulators lands next to its neighbour lanes' and a store covers 1 KiB.
 #pragma unroll
-      for (int i = 0; i < kStatsMaxSrc; ++i) {
-        if (i < n && u < nur)
-          b[i].load(static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i] + u * VEC);
-        else
-          b[i].zero();
+    for (int s = 0; s < kStatsMaxQ; ++s)
+      if (s < nqg && lane < n) w_lds[wv][lane][s] = ew[s];
+    __builtin_amdgcn_wave_barrier();
+    constexpr bool kSplit = std::is_same<IO, bf16_bits>::value && std::is_same<ACC, float>::value;
+    const int ccol = kWave * VEC;  // columns per chunk
+    Unit<IO, VEC> buf[kStatsMaxSrc];
+    const auto load_chunk = [&](int c) {
+      if constexpr (kSplit) {
+        const int col0 = c * ccol + 4 * lane;
+        const int col1 = col0 + ccol / 2;
+#pragma unroll
+        for (int i = 0; i < kStatsMaxSrc; ++i) {
+          const bf16_bits* rp = static_cast<const bf16_bits*>(p.src.ptr[i]) + row * p.src.ld[i];
+          u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+          if (i < n && col0 < p.d) lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col0));
+          if (i < n && col1 < p.d) hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col1));
+          buf[i].raw = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      } else {
+        const int u = lane + kWave * c;
+#pragma unroll
+        for (int i = 0; i < kStatsMaxSrc; ++i) {
+          if (i < n && u < nur)
+            buf[i].load(static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i] + u * VEC);
+          else
+            buf[i].zero();
+        }
       }
     };
-    const auto fold_chunk = [&](const Unit<IO, VEC> (&b)[kStatsMaxSrc], int c) {
+    const auto fold_chunk = [&](int c) {
       const int u = lane + kWave * c;
 #pragma unroll
-      for (int s = 0; s < kStatsMaxQ; s += 2) {
-        if (s < nqg) {
-          float a0[VEC], a1[VEC];
+      for (int s0 = 0; s0 < kStatsMaxQ; s0 += kValQ) {
+        if (s0 < nqg) {
+          float a[kValQ][VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) a0[e] = a1[e] = 0.f;
-          // The weights are broadcast from their lanes here, once per chunk: hoisting all
-          // (query, source) broadcasts out of the chunk loop would not fit in scalar registers.
-          float e0 = ew[s], e1 = ew[s + 1];
-          asm volatile("" : "+v"(e0), "+v"(e1));
+          for (int j = 0; j < kValQ; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) a[j][e] = 0.f;
 #pragma unroll
           for (int i = 0; i < kStatsMaxSrc; ++i) {
             if (i < n) {
-              const float w0 = lane_f32(e0, i);
-              const float w1 = lane_f32(e1, i);
-              float x[VEC];
-              b[i].get(x);
+              float w[kValQ];
+              const float* wp = &w_lds[wv][i][s0];
 #pragma unroll
-              for (int e = 0; e < VEC; ++e) {
-                a0[e] = fmaf(w0, x[e], a0[e]);
-                a1[e] = fmaf(w1, x[e], a1[e]);
-              }
+              for (int j = 0; j < kValQ; ++j) w[j] = wp[j];
+              float x[VEC];
+              buf[i].get(x);
+#pragma unroll
+              for (int j = 0; j < kValQ; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) a[j][e] = fmaf(w[j], x[e], a[j][e]);
             }
           }
-          if (u < nur) {
-            int64_t off = static_cast<int64_t>(q0 + s) * p.acc_qstride + row * p.acc_ld;
-            asm volatile("" : "+v"(off));
+          int64_t off = static_cast<int64_t>(q0 + s0) * p.acc_qstride + row * p.acc_ld;
+          asm volatile("" : "+v"(off));
+          if constexpr (kSplit) {
+            const int col0 = c * ccol + 4 * lane;
+            const int col1 = col0 + ccol / 2;
+            float* d0 = static_cast<float*>(p.acc) + off;
+#pragma unroll
+            for (int j = 0; j < kValQ; ++j) {
+              if (s0 + j < nqg) {
+                float* dj = d0 + j * p.acc_qstride;
+                if (col0 < p.d)
+                  out_store(f32x4{a[j][0], a[j][1], a[j][2], a[j][3]},
+                            reinterpret_cast<f32x4*>(dj + col0));
+                if (col1 < p.d)
+                  out_store(f32x4{a[j][4], a[j][5], a[j][6], a[j][7]},
+                            reinterpret_cast<f32x4*>(dj + col1));
+              }
+            }
+          } else if (u < nur) {
             ACC* d0 = static_cast<ACC*>(p.acc) + off + u * VEC;
-            store_acc<ACC, VEC>(d0, a0);
-            if (s + 1 < nqg) store_acc<ACC, VEC>(d0 + p.acc_qstride, a1);
+#pragma unroll
+            for (int j = 0; j < kValQ; ++j)
+              if (s0 + j < nqg) store_acc<ACC, VEC>(d0 + j * p.acc_qstride, a[j]);
           }
         }
       }
     };
     for (int c = 0; c < nslot; ++c) {
-      load_chunk(buf, c);
-      fold_chunk(buf, c);
+      load_chunk(c);
+      fold_chunk(c);
     }
+    // the next row's weights overwrite w_lds only after every lane has read this row's
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -239,7 +288,8 @@ hipError_t launch_stats_tile_t(const StatsParams& p, int qg, hipStream_t s) {
 int stats_tile_query_group(int d, int r, int vec) {
   const int ub = (d - r) / vec;
   const size_t per_q = static_cast<size_t>(d - ub * vec) * sizeof(float);
-  size_t fit = lds_limit() / per_q;
+  const size_t lim = lds_limit();
+  size_t fit = lim > kStatsStaticLds ? (lim - kStatsStaticLds) / per_q : 0;
   if (fit > static_cast<size_t>(kStatsMaxQ)) fit = kStatsMaxQ;
   return static_cast<int>(fit);
 }
