@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   constexpr int PF = 2;
   constexpr int K0 = NU - TU;  // first unit slot that may hold key columns
+  constexpr bool kRunStores = std::is_same<GIO, float>::value && VEC == 8;
   extern __shared__ float q_lds[];
   __shared__ double xch[2][kWavesPerBlock][3];
   const int lane = threadIdx.x & (kWave - 1);
@@ -155,22 +156,50 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
         const int u = g.unit(k);
-        if (u < g.nur) {
-          float v[VEC];
+        float v[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];
-          if (k >= K0 && u >= g.ub) {
-            float x[VEC];
-            st.t.u[0][k].get(x);
-            const float* qv = q_lds + (u - g.ub) * VEC;
+        for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];  // gr is 0 past the row
+        if (k >= K0 && u >= g.ub && u < g.nur) {
+          float x[VEC];
+          st.t.u[0][k].get(x);
+          const float* qv = q_lds + (u - g.ub) * VEC;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              if (u * VEC + e >= g.c0) {
-                v[e] += c1 * qv[e] - c2 * x[e];
-                dqa[k >= K0 ? k - K0 : 0][e] = fmaf(c1, x[e], dqa[k >= K0 ? k - K0 : 0][e]);
-              }
+          for (int e = 0; e < VEC; ++e) {
+            if (u * VEC + e >= g.c0) {
+              v[e] += c1 * qv[e] - c2 * x[e];
+              dqa[k >= K0 ? k - K0 : 0][e] = fmaf(c1, x[e], dqa[k >= K0 ? k - K0 : 0][e]);
             }
           }
+        }
+        if constexpr (kRunStores) {
+          // float32 gradients of 16-byte bf16 units: regroup the wave's 512 values so that
+          // every store covers 1 KiB (the chunk exists for all lanes or none)
+          const int cu = u - lane;  // the chunk's first unit
+          if (cu < g.nur) {
+            float lo[4], hi[4];
+            run_halves(v, lane, lo, hi);
+            float* cp = reinterpret_cast<float*>(drow) + static_cast<int64_t>(cu) * VEC;
+            const int l2 = lane >> 1;
+            if (cu + l2 < g.nur) {
+              if (p.accumulate) {
+                float old[4];
+                load_f32<4>(cp + 4 * lane, old);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lo[e] += old[e];
+              }
+              store_unit<float, 4>(cp + 4 * lane, lo);
+            }
+            if (cu + 32 + l2 < g.nur) {
+              if (p.accumulate) {
+                float old[4];
+                load_f32<4>(cp + 256 + 4 * lane, old);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hi[e] += old[e];
+              }
+              store_unit<float, 4>(cp + 256 + 4 * lane, hi);
+            }
+          }
+        } else if (u < g.nur) {
           if (p.accumulate) {
             float old[VEC];
             load_grad<GIO, VEC>(drow + u * VEC, old);

@@ -275,6 +275,26 @@ __device__ __forceinline__ void store_grad(G* p, const float (&x)[VEC]) {
   }
 }
 
+// Lane l holds floats 8l..8l+7 of a run of 512 (one 16-byte bf16 unit's worth of float32
+// values per lane). Returns in lo the floats 4l..4l+3 and in hi the floats 256+4l..256+4l+3 of
+// the run, so that a 16-byte store of lo, then of hi, by every lane writes 1 KiB contiguously
+// each time instead of two half-filled 2 KiB spans. Every lane of the wave must take part.
+__device__ __forceinline__ void run_halves(const float (&v)[8], int lane, float (&lo)[4],
+                                           float (&hi)[4]) {
+  const int a1 = (lane >> 1) << 2;         // byte address of the holder lane l / 2
+  const int a2 = ((lane >> 1) + 32) << 2;  // and of 32 + l / 2
+  const bool odd = (lane & 1) != 0;        // which half of the holder's 8 floats
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int x0 = __builtin_amdgcn_ds_bpermute(a1, __float_as_int(v[e]));
+    const int x1 = __builtin_amdgcn_ds_bpermute(a1, __float_as_int(v[4 + e]));
+    lo[e] = __int_as_float(odd ? x1 : x0);
+    const int y0 = __builtin_amdgcn_ds_bpermute(a2, __float_as_int(v[e]));
+    const int y1 = __builtin_amdgcn_ds_bpermute(a2, __float_as_int(v[4 + e]));
+    hi[e] = __int_as_float(odd ? y1 : y0);
+  }
+}
+
 // ---- cross-lane reductions -------------------------------------------------------------------
 // Butterfly (xor) reductions: every lane ends with the same, bitwise identical result because
 // each step adds the same two operands on both partners.
