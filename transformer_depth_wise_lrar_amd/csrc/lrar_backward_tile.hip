@@ -13,7 +13,8 @@
 //   then    alpha = softmax(z), sbar = sum_j alpha_j s_j, dz_i = alpha_i (s_i - sbar), which
 //           equals alpha_i <g, o_i - h>;
 //   pass B  dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns
-//           (the key units are read again, from L2), written in the gradient type (float32,
+//           (the key units were kept in LDS in pass A when n r elements fit 32 KiB per row
+//           group; otherwise they are read again), written in the gradient type (float32,
 //           or bf16 rounded once; optionally added to the existing gradient first); dz_i k_i /
 //           rho_i accumulates into per-lane dq partials kept in registers across the group's
 //           rows.
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   constexpr int PF = 2;
   constexpr int K0 = NU - TU;  // first unit slot that may hold key columns
   constexpr bool kRunStores = std::is_same<GIO, float>::value && VEC == 8;
-  extern __shared__ float q_lds[];
+  extern __shared__ __attribute__((aligned(16))) float q_lds[];
   __shared__ double xch[2][kWavesPerBlock][3];
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = threadIdx.x / kWave;
@@ -48,10 +49,18 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   g.c0 = p.d - p.r;
   g.ub = g.c0 / VEC;
   g.r = p.r;
-  for (int k = threadIdx.x; k < p.d - g.ub * VEC; k += kBlock) {
+  const int rq = p.d - g.ub * VEC;  // staged query columns
+  for (int k = threadIdx.x; k < rq; k += kBlock) {
     const int col = g.ub * VEC + k;
     q_lds[k] = col >= g.c0 ? p.q[col - g.c0] : 0.f;
   }
+  // Key stash (when the host sized it): the key units of every source of the row group's
+  // current row, written in pass A and read back in pass B by the lane that wrote them.
+  const int nkey = g.nur - g.ub;
+  Unit<IO, VEC>* stash = nullptr;
+  if (p.key_stash)
+    stash = reinterpret_cast<Unit<IO, VEC>*>(q_lds + ((rq + 3) & ~3)) +
+            static_cast<int64_t>(wib / WPR) * n * nkey;
   __syncthreads();
 
   float dqa[TU][VEC];
@@ -121,6 +130,13 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         rhoi = rho;
         si = red[2];
       }
+      if (stash != nullptr) {
+#pragma unroll
+        for (int k = K0; k < NU; ++k) {
+          const int u = g.unit(k);
+          if (u >= g.ub && u < g.nur) stash[i * nkey + (u - g.ub)] = st.t.u[0][k];
+        }
+      }
     };
 #pragma unroll
     for (int b = 0; b < PF; ++b)
@@ -147,8 +163,9 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
     const float c1f = static_cast<float>(dz / rhoi);                          // dz / rho
     const float c2f = static_cast<float>(dz * zi / (p.r * rhoi * rhoi));      // dz z / (r rho^2)
 
-    // ---- pass B: source gradients (the key units stream through the ring again)
-    const auto store_b = [&](const Stage<IO, VEC, NU, 1, 0>& st, int i) {
+    // ---- pass B: source gradients (the key units from the LDS stash, or streamed through the
+    // ring again when the stash would be too large)
+    const auto store_b = [&](const Unit<IO, VEC> (&ku)[NU], int i) {
       const float ai = lane_f32(af, i);
       const float c1 = lane_f32(c1f, i);
       const float c2 = lane_f32(c2f, i);
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];  // gr is 0 past the row
         if (k >= K0 && u >= g.ub && u < g.nur) {
           float x[VEC];
-          st.t.u[0][k].get(x);
+          ku[k].get(x);
           const float* qv = q_lds + (u - g.ub) * VEC;
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
@@ -210,17 +227,30 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         }
       }
     };
+    if (stash != nullptr) {
+      for (int i = 0; i < n; ++i) {
+        Unit<IO, VEC> ku[NU];
 #pragma unroll
-    for (int b = 0; b < PF; ++b)
-      if (b < n) load_stage<true>(ring[b], src_base(b), p.src.ld[b], g);
-    for (int i0 = 0; i0 < n; i0 += PF + 1) {
+        for (int k = 0; k < NU; ++k) {
+          const int u = g.unit(k);
+          if (k >= K0 && u >= g.ub && u < g.nur) ku[k] = stash[i * nkey + (u - g.ub)];
+          else ku[k].zero();
+        }
+        store_b(ku, i);
+      }
+    } else {
 #pragma unroll
-      for (int b = 0; b <= PF; ++b) {
-        const int i = i0 + b;
-        if (i < n) {
-          if (i + PF < n)
-            load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
-          store_b(ring[b], i);
+      for (int b = 0; b < PF; ++b)
+        if (b < n) load_stage<true>(ring[b], src_base(b), p.src.ld[b], g);
+      for (int i0 = 0; i0 < n; i0 += PF + 1) {
+#pragma unroll
+        for (int b = 0; b <= PF; ++b) {
+          const int i = i0 + b;
+          if (i < n) {
+            if (i + PF < n)
+              load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], g);
+            store_b(ring[b].t.u[0], i);
+          }
         }
       }
     }
@@ -283,12 +313,29 @@ int device_cus_bwd() {
   return cus;
 }
 
+// Largest key stash a workgroup takes (beyond it pass B reads the key units again from memory):
+// small enough that several workgroups still share a CU's LDS.
+constexpr size_t kStashMaxBytes = 32 * 1024;
+
+// Bytes of the key stash of one workgroup: the key units of every source for each of its
+// row groups.
+template <typename IO, int VEC>
+size_t stash_bytes(const BwdParams& p, int wpr) {
+  const int nur = (p.d + VEC - 1) / VEC;
+  const int nkey = nur - (p.d - p.r) / VEC;
+  return static_cast<size_t>(kWavesPerBlock / wpr) * p.n * nkey * sizeof(Unit<IO, VEC>);
+}
+
 template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR>
 hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_blocks, int* grid_out,
                              hipStream_t s) {
   auto kern = k_backward_tile<IO, GIO, VEC, NU, TU, WPR>;
+  BwdParams pk = p;
+  pk.key_stash = stash_bytes<IO, VEC>(p, WPR) <= kStashMaxBytes ? 1 : 0;
   const int ub = (p.d - p.r) / VEC;
-  const size_t lds = static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
+  const int rq = p.d - ub * VEC;
+  const size_t lds = static_cast<size_t>((rq + 3) & ~3) * sizeof(float) +
+                     (pk.key_stash ? stash_bytes<IO, VEC>(p, WPR) : 0);
   static thread_local size_t cached_lds = ~size_t(0);
   static thread_local int cached_per_cu = 0;
   if (cached_lds != lds) {
@@ -306,7 +353,7 @@ hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_block
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
   *grid_out = static_cast<int>(blocks);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, p, block_dq);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), lds, s, pk, block_dq);
   return hipGetLastError();
 }
 

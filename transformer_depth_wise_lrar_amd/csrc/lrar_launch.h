@@ -75,6 +75,7 @@ struct BwdParams {
   int accumulate;
   float* dq;
   void* workspace;  // [grid + reduce groups][r] float64 dq partials
+  int key_stash;    // set by the row-tile launcher: pass B reads the key units from LDS
 };
 
 // Column-chunked two-pass read (any width; also the merge when a row does not fit a tile).
