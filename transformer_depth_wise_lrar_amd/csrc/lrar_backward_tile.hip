@@ -50,10 +50,10 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   g.ub = g.c0 / VEC;
   g.r = p.r;
   const int rq = p.d - g.ub * VEC;  // staged query columns
-  for (int k = threadIdx.x; k < rq; k += kBlock) {
-    const int col = g.ub * VEC + k;
-    q_lds[k] = col >= g.c0 ? p.q[col - g.c0] : 0.f;
-  }
+  QStage qst;
+  qst.base = q_lds;
+  qst.nv = g.nur - g.ub;
+  qst.fill<VEC>(p.q, g.ub, g.c0, threadIdx.x, kBlock);
   // Key stash (when the host sized it): the key units of every source of the row group's
   // current row, written in pass A and read back in pass B by the lane that wrote them.
   const int nkey = g.nur - g.ub;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
     Stage<IO, VEC, NU, 1, 0> ring[PF + 1];
     const auto fold_a = [&](const Stage<IO, VEC, NU, 1, 0>& st, int i) {
       double red[3];
-      key_partial_units<TU>(st.t.u[0], q_lds, g, red[0], red[1]);
+      key_partial_units<TU>(st.t.u[0], qst, g, red[0], red[1]);
       double s = 0.0;
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
@@ -179,7 +179,8 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         if (k >= K0 && u >= g.ub && u < g.nur) {
           float x[VEC];
           ku[k].get(x);
-          const float* qv = q_lds + (u - g.ub) * VEC;
+          float qv[VEC];
+          qst.get<VEC>(u - g.ub, qv);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             if (u * VEC + e >= g.c0) {

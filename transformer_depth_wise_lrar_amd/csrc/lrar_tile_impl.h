@@ -54,7 +54,7 @@ template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int R, int 
           int MODE, typename ACC>
 __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MODE> keys) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
-  extern __shared__ float q_lds[];
+  extern __shared__ __attribute__((aligned(16))) float q_lds[];
   // Partial key sums of the waves that share a row (two slots, alternating by source).
   __shared__ double xch[2][kWavesPerBlock][2 * R];
   const int lane = threadIdx.x & (kWave - 1);
@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   g.r = p.r;
   // The query: spread over the lanes (KS > 0), or staged in LDS from the first key unit's
   // column (KS = 0; the columns of that unit that precede the key hold zero).
+  QStage qst;
+  qst.base = q_lds;
+  qst.nv = g.nur - g.ub;
   SpreadQ<KS> qs[ks_slots(KS)];
 #pragma unroll
   for (int e = 0; e < ks_slots(KS); ++e) qs[e] = 0;
@@ -83,12 +86,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       }
     }
   } else {
-    if (n > 0) {
-      for (int k = threadIdx.x; k < p.d - g.ub * VEC; k += kBlock) {
-        const int col = g.ub * VEC + k;
-        q_lds[k] = col >= g.c0 ? p.q[col - g.c0] : 0.f;
-      }
-    }
+    if (n > 0) qst.fill<VEC>(p.q, g.ub, g.c0, threadIdx.x, kBlock);
     __syncthreads();
   }
   // Spread key pieces sit in lanes [0, gp) (gp: a power of two).
@@ -208,9 +206,9 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       if constexpr (KS > 0)
         key_partial_spread<IO, KS>(st.kp[j], qs, red[2 * j], red[2 * j + 1]);
       else if constexpr (MODE == kTileFullRms)
-        row_partial_full(st.t.u[j], q_lds, t, red[2 * j], red[2 * j + 1]);
+        row_partial_full(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
       else
-        key_partial_units<TU>(st.t.u[j], q_lds, t, red[2 * j], red[2 * j + 1]);
+        key_partial_units<TU>(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
     }
     if constexpr (KS > 0 && ROWRED && R <= 2) {
       // the spread key sits in lanes 0..31 of every wave of the row
@@ -452,7 +450,8 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   constexpr int PF = tile_prefetch(NU);
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC>;
   const int ub = (p.d - p.r) / VEC;
-  const size_t lds = KS > 0 ? 0 : static_cast<size_t>(p.d - ub * VEC) * sizeof(float);
+  const int nur = (p.d + VEC - 1) / VEC;
+  const size_t lds = KS > 0 ? 0 : static_cast<size_t>(nur - ub) * VEC * sizeof(float);
   // Workgroups per CU for this instantiation and LDS size (cached: the query is not free).
   static thread_local size_t cached_lds = ~size_t(0);
   static thread_local int cached_per_cu = 0;
