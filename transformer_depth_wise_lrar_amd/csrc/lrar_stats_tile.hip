@@ -40,7 +40,7 @@ constexpr size_t kStatsStaticLds =
 
 template <typename IO, int VEC, typename ACC>
 __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nqg) {
-  extern __shared__ float q_lds[];  // [nqg][rq]
+  extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [nqg][rq]
   // Scores of the wave's current row: z[s][i] for query s, source i; and their weights.
   __shared__ double z_lds[kStatsWaves][kStatsMaxQ][kStatsMaxSrc];
   __shared__ __attribute__((aligned(16))) float w_lds[kStatsWaves][kStatsMaxSrc][kStatsMaxQ];
@@ -55,10 +55,11 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
   const int ub = c0 / VEC;
   const int rq = p.d - ub * VEC;  // staged query columns
   const int k_lo = ub / kWave;    // first slot that can hold key units
-  for (int idx = threadIdx.x; idx < nqg * rq; idx += kStatsBlock) {
-    const int s = idx / rq;
-    const int col = ub * VEC + (idx - s * rq);
-    q_lds[idx] = col >= c0 ? p.q[static_cast<int64_t>(q0 + s) * p.q_ld + (col - c0)] : 0.f;
+  // query s of the group staged at q_lds + s * rq, transposed (QStage)
+  const int nv = nur - ub;
+  for (int s = 0; s < nqg; ++s) {
+    QStage qs{q_lds + s * rq, nv};
+    qs.fill<VEC>(p.q + static_cast<int64_t>(q0 + s) * p.q_ld, ub, c0, threadIdx.x, kStatsBlock);
   }
   __syncthreads();
 
@@ -89,15 +90,17 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
               kv[e] = (u * VEC + e) >= c0 ? static_cast<double>(x[e]) : 0.0;
               red[kStatsMaxQ] = fma(kv[e], kv[e], red[kStatsMaxQ]);
             }
-            const float* qc = q_lds + (u - ub) * VEC;
             // One query at a time: the scheduling barrier keeps the query values of later
             // queries from being read ahead into registers.
 #pragma unroll
             for (int s = 0; s < kStatsMaxQ; ++s) {
               if (s < nqg) {
+                const QStage qs{q_lds + s * rq, nv};
+                float qv[VEC];
+                qs.get<VEC>(u - ub, qv);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                  red[s] = fma(static_cast<double>(qc[s * rq + e]), kv[e], red[s]);
+                  red[s] = fma(static_cast<double>(qv[e]), kv[e], red[s]);
               }
               __builtin_amdgcn_sched_barrier(0);
             }

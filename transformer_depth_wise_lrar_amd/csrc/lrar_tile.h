@@ -201,44 +201,6 @@ __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
   }
 }
 
-// The site query staged in LDS for the key units, in VEC-element units v = u - ub counted
-// from the first key unit (columns of that unit before the key hold zero). On the vector path
-// the units are stored "transposed": elements 4j..4j+3 of unit v are the float4 at index
-// j * nv + v, so the lanes of a wave, which hold consecutive units, read consecutive 16-byte
-// words (no bank conflicts); on the element path unit v is element v.
-struct QStage {
-  float* base;
-  int nv;  // staged units
-  // Stages the query (all threads of the workgroup; call __syncthreads afterwards).
-  template <int VEC>
-  __device__ __forceinline__ void fill(const float* __restrict__ q, int ub, int c0, int tid,
-                                       int nthreads) {
-    for (int idx = tid; idx < nv * VEC; idx += nthreads) {
-      const int col = ub * VEC + idx;
-      const float v = col >= c0 ? q[col - c0] : 0.f;
-      const int unit = idx / VEC, e = idx - unit * VEC;
-      if constexpr (VEC % 4 == 0) base[((e / 4) * nv + unit) * 4 + (e % 4)] = v;
-      else base[idx] = v;
-    }
-  }
-  template <int VEC>
-  __device__ __forceinline__ void get(int v, float (&q)[VEC]) const {
-    if constexpr (VEC % 4 == 0) {
-#pragma unroll
-      for (int j = 0; j < VEC / 4; ++j) {
-        const f32x4 t = reinterpret_cast<const f32x4*>(base)[j * nv + v];
-        q[4 * j + 0] = t.x;
-        q[4 * j + 1] = t.y;
-        q[4 * j + 2] = t.z;
-        q[4 * j + 3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) q[e] = base[v * VEC + e];
-    }
-  }
-};
-
 // This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the
 // last TU unit slots can hold key columns (the host picks TU so that the key starts in slot
 // NU - TU or later).
