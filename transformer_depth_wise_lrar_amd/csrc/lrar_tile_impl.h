@@ -386,6 +386,36 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       begin_tile(t);
       finish_tile(t);
     }
+  } else if (n == 1) {
+    // One source per tile (a merge with the partial sum, the embedding-only read): the tiles
+    // alternate between two stages, so the next tile's rows load while this tile is scored
+    // and folded in.
+    static_assert(PF >= 1, "two stages");
+    int64_t tile = group;
+    TileGeom t0, t1;
+    if (tile < ntiles) {
+      set_tile(t0, tile);
+      load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
+    }
+    for (; tile < ntiles; tile += 2 * ngroups) {
+      const bool more = tile + ngroups < ntiles;
+      if (more) {
+        set_tile(t1, tile + ngroups);
+        load_stage<false, kSep>(ring[1], src_base(0), p.src.ld[0], t1, key_base(0), key_ld(0));
+      }
+      begin_tile(t0);
+      fold_source(ring[0], t0, 0);
+      finish_tile(t0);
+      if (more) {
+        if (tile + 2 * ngroups < ntiles) {
+          set_tile(t0, tile + 2 * ngroups);
+          load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
+        }
+        begin_tile(t1);
+        fold_source(ring[1], t1, 0);
+        finish_tile(t1);
+      }
+    }
   } else {
     for (int64_t tile = group; tile < ntiles; tile += ngroups) {
       TileGeom t;
