@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   extern __shared__ __attribute__((aligned(16))) float q_lds[];
   __shared__ double xch[2][kWavesPerBlock][3];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wib = threadIdx.x / kWave;
+  const int wib = wave_in_block();
   const int64_t group = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wib) / WPR;
   const int64_t ngroups = static_cast<int64_t>(gridDim.x) * kWavesPerBlock / WPR;
   const int n = p.n;

@@ -24,6 +24,13 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kMaxSources = 64;
 constexpr int kMaxQueries = 64;
 
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar) value, so that
+// row indices and row pointers derived from it stay in scalar registers and global accesses
+// take the scalar-base + 32-bit lane-offset form instead of per-lane 64-bit address math.
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
+
 // Source pointer table, passed by value in the kernel arguments (1 KiB).
 struct SrcList {
   const void* ptr[kMaxSources];

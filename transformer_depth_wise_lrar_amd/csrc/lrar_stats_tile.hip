@@ -45,8 +45,8 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
   __shared__ double z_lds[kStatsWaves][kStatsMaxQ][kStatsMaxSrc];
   __shared__ __attribute__((aligned(16))) float w_lds[kStatsWaves][kStatsMaxSrc][kStatsMaxQ];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kStatsWaves + threadIdx.x / kWave;
+  const int wv = wave_in_block();
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kStatsWaves + wv;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kStatsWaves;
   const int n = p.n;
   const int nur = (p.d + VEC - 1) / VEC;
