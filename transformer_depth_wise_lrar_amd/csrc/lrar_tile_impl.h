@@ -243,12 +243,14 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   // Scores source i's stage and folds its rows into the online-softmax accumulators.
   const auto fold_source = [&](const Stage<IO, VEC, NU, R, KS>& st, const TileGeom& t, int i) {
     const double z = stage_scores(st, t);  // lane j: row j
+    if (p.alpha != nullptr) {  // the scores are kept only to write the weights
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const double zj = lane_f64(z, j);
-      if (lane == i) zk[j] = zj;
+      for (int j = 0; j < R; ++j) {
+        const double zj = lane_f64(z, j);
+        if (lane == i) zk[j] = zj;
+      }
     }
-    mtop = fmax(mtop, z);
+    if constexpr (kMerge) mtop = fmax(mtop, z);  // only the merge reports the maximum
     // Rescale a row only when its score passes the reference by more than kLazyRescale
     // (always on its first source, whose reference is -inf).
     const bool grow = !(z <= mref + kLazyRescale);
