@@ -288,8 +288,6 @@ int backward_grid(int64_t T) {
   return static_cast<int>(blocks < kBwdMaxBlocks ? (blocks > 0 ? blocks : 1) : kBwdMaxBlocks);
 }
 
-int backward_max_units() { return 16; }
-
 bool backward_supported(int d, int r, int vec) {
   const int nur = (d + vec - 1) / vec;
   const int nu = (nur + kWave - 1) / kWave;

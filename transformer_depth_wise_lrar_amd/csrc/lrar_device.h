@@ -1,12 +1,13 @@
 // Device-side building blocks of liblrattnres (internal; not installed).
 //
-// Layout conventions used by every kernel:
-//   * One 64-lane wavefront owns one token row at a time; a 256-thread workgroup holds four
-//     such rows. Rows are visited with a grid-stride loop.
+// Layout conventions shared by the kernels:
 //   * A row is cut into "units" of VEC consecutive elements, 16 bytes on the vector path
-//     (8 bf16 or 4 fp32) and one element on the scalar path. Lane l touches units
-//     l, l + 64, l + 128, ... so each load instruction of a wave covers one contiguous
-//     1 KiB stretch of the row.
+//     (8 bf16 or 4 fp32) and one element on the element path. Within a chunk of 64 units the
+//     lanes of a wave hold consecutive units, so each load instruction of a wave covers one
+//     contiguous 1 KiB stretch of the row.
+//   * Rows go to wavefronts either one row per wave at a time (the one-wave-per-row kernels)
+//     or as register tiles of a few rows, a row's chunks possibly shared by the four waves of
+//     a workgroup (the tile kernels; see lrar_tile_impl.h).
 //   * The key slice is the columns [d - r, d). Units that straddle d - r mask their leading
 //     elements out of the key.
 #pragma once
@@ -473,15 +474,6 @@ __device__ __forceinline__ double wave_max_dpp(double v) {
   const int64_t b = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
   const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
-  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
-}
-
-// A wave-uniform float64 moved into scalar registers (its value is the same in every lane;
-// this only frees the two vector registers that would otherwise hold it).
-__device__ __forceinline__ double uniform_f64(double v) {
-  const int64_t b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(b));
-  const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32));
   return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 

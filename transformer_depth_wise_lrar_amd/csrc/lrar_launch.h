@@ -107,7 +107,6 @@ hipError_t launch_stats_tile(const StatsParams& p, int io_bf16, int acc_bf16, in
 
 // Backward: grid size (workgroups) used for T rows, and the launcher.
 int backward_grid(int64_t T);
-int backward_max_units();
 // Lanes' register window for dq partials must cover the key; false if this shape needs more.
 bool backward_supported(int d, int r, int vec);
 size_t backward_workspace(int64_t T, int r);
