@@ -475,10 +475,11 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
 constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
 #endif
 
-// Spread-key reads of many sources keep one more source in flight: three sources ahead
-// measured 8 % (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two, at the
-// price of a third wave per SIMD. Reads of few sources, and keys taken from the row units
-// (whose float64 scoring already keeps the vector unit busy), keep the shallower ring.
+// Reads of many sources keep one more source in flight: three sources ahead measured 8 %
+// (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two for spread keys, in
+// both variants, and 9 % for the full-width-RMS control, at the price of a third wave per
+// SIMD. Reads of few sources, and slice keys taken from the row units (whose float64 scoring
+// already keeps the vector unit busy), keep the shallower ring.
 constexpr int kDeepPrefetch = 3;
 constexpr int kDeepMinSources = 8;
 
@@ -518,7 +519,8 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
 // A spread-key launch, with the deeper ring when it pays (see kDeepPrefetch).
 template <typename IO, int VEC, int NU, int KS, bool ROWRED, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_spread(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
-  if constexpr ((MODE == kTileOnline || MODE == kTileKeys) && NU >= 2 && NU <= 4) {
+  if constexpr ((MODE == kTileOnline || MODE == kTileKeys || MODE == kTileTwoPass) && NU >= 2 &&
+                NU <= 4) {
     if (p.n >= kDeepMinSources)
       return launch_tile_t<IO, VEC, NU, 1, KS, ROWRED, WPR, MODE, ACC, true>(p, kt, s);
   }
@@ -534,6 +536,10 @@ hipError_t launch_tile_spread(const ReadParams& p, const KeyTable<MODE>& kt, hip
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr (MODE == kTileFullRms) {
+    if constexpr (NU >= 2 && NU <= 4) {
+      if (p.n >= kDeepMinSources)
+        return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC, true>(p, kt, s);
+    }
     return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
   } else if constexpr (MODE == kTileMergeAcc) {
     const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
