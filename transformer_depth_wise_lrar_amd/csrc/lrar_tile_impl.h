@@ -127,8 +127,30 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   // e^{z - mref}, running maximum mtop. One vector exp then serves all R rows.
   double mref = -INFINITY, lsum = 0.0, mtop = -INFINITY;
 
-  // Starts a tile: clears the accumulators, or loads the Phase-1 statistics for a merge.
-  const auto begin_tile = [&](const TileGeom& t) {
+  // bf16 Phase-1 accumulators of a single-source merge are loaded a tile ahead, raw (16
+  // registers a row at four units per lane), and decoded when their tile starts.
+  constexpr bool kAccPre =
+      MODE == kTileMerge && std::is_same<ACC, bf16_bits>::value && VEC == 8;
+  Unit<bf16_bits, 8> apre[kAccPre ? R : 1][kAccPre ? NU : 1];
+  const auto load_acc_ahead = [&](const TileGeom& t) {
+    if constexpr (kAccPre) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const bf16_bits* prow =
+            static_cast<const bf16_bits*>(p.acc) + (t.r0 + j) * p.acc_ld;
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+          const int u = t.unit(k);
+          if (j < t.nrow && u < t.nur) apre[j][k].load(prow + u * VEC);
+          else apre[j][k].zero();
+        }
+      }
+    }
+  };
+
+  // Starts a tile: clears the accumulators, or loads the Phase-1 statistics for a merge
+  // (ahead: the accumulators were loaded by load_acc_ahead).
+  const auto begin_tile = [&](const TileGeom& t, bool ahead = false) {
     mref = -INFINITY;
     lsum = 0.0;
     mtop = -INFINITY;
@@ -146,14 +168,26 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         mtop = mref;
         lsum = static_cast<double>(p.l_in[t.r0 + lane]);
       }
+      bool decoded = false;
+      if constexpr (kAccPre) {
+        if (ahead) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if (j < t.nrow) {
-          const ACC* prow = static_cast<const ACC*>(p.acc) + (t.r0 + j) * p.acc_ld;
+          for (int j = 0; j < R; ++j)
 #pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            const int u = t.unit(k);
-            if (u < t.nur) load_acc<ACC, VEC>(prow + u * VEC, acc[j][k]);
+            for (int k = 0; k < NU; ++k) apre[j][k].get(acc[j][k]);
+          decoded = true;
+        }
+      }
+      if (!decoded) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          if (j < t.nrow) {
+            const ACC* prow = static_cast<const ACC*>(p.acc) + (t.r0 + j) * p.acc_ld;
+#pragma unroll
+            for (int k = 0; k < NU; ++k) {
+              const int u = t.unit(k);
+              if (u < t.nur) load_acc<ACC, VEC>(prow + u * VEC, acc[j][k]);
+            }
           }
         }
       }
@@ -398,6 +432,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     if (tile < ntiles) {
       set_tile(t0, tile);
       load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
+      load_acc_ahead(t0);
     }
     for (; tile < ntiles; tile += 2 * ngroups) {
       const bool more = tile + ngroups < ntiles;
@@ -405,15 +440,18 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         set_tile(t1, tile + ngroups);
         load_stage<false, kSep>(ring[1], src_base(0), p.src.ld[0], t1, key_base(0), key_ld(0));
       }
-      begin_tile(t0);
+      begin_tile(t0, true);
+      if (more) load_acc_ahead(t1);
       fold_source(ring[0], t0, 0);
       finish_tile(t0);
       if (more) {
-        if (tile + 2 * ngroups < ntiles) {
+        const bool next = tile + 2 * ngroups < ntiles;
+        if (next) {
           set_tile(t0, tile + 2 * ngroups);
           load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
         }
-        begin_tile(t1);
+        begin_tile(t1, true);
+        if (next) load_acc_ahead(t0);
         fold_source(ring[1], t1, 0);
         finish_tile(t1);
       }
