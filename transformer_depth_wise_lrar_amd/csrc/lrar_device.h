@@ -309,6 +309,7 @@ __device__ __forceinline__ void run_halves(const float (&v)[8], int lane, float 
 // j * nv + v, so the lanes of a wave, which hold consecutive units, read consecutive 16-byte
 // words (no bank conflicts); on the element path unit v is element v.
 struct QStage {
+  using value_type = float;
   float* base;
   int nv;  // staged units
   // Stages the query (all threads of the workgroup; call __syncthreads afterwards).
@@ -333,6 +334,40 @@ struct QStage {
         q[4 * j + 1] = t.y;
         q[4 * j + 2] = t.z;
         q[4 * j + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) q[e] = base[v * VEC + e];
+    }
+  }
+};
+
+// The same staging in float64 (two values per 16-byte word, transposed likewise), so the
+// scoring needs no per-element conversion of q.
+struct QStageD {
+  using value_type = double;
+  double* base;
+  int nv;
+  template <int VEC>
+  __device__ __forceinline__ void fill(const float* __restrict__ q, int ub, int c0, int tid,
+                                       int nthreads) {
+    for (int idx = tid; idx < nv * VEC; idx += nthreads) {
+      const int col = ub * VEC + idx;
+      const double v = col >= c0 ? static_cast<double>(q[col - c0]) : 0.0;
+      const int unit = idx / VEC, e = idx - unit * VEC;
+      if constexpr (VEC % 2 == 0) base[((e / 2) * nv + unit) * 2 + (e % 2)] = v;
+      else base[idx] = v;
+    }
+  }
+  template <int VEC>
+  __device__ __forceinline__ void get(int v, double (&q)[VEC]) const {
+    if constexpr (VEC % 2 == 0) {
+      typedef double f64x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int j = 0; j < VEC / 2; ++j) {
+        const f64x2 t = reinterpret_cast<const f64x2*>(base)[j * nv + v];
+        q[2 * j + 0] = t.x;
+        q[2 * j + 1] = t.y;
       }
     } else {
 #pragma unroll

@@ -204,9 +204,9 @@ __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
 // This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the
 // last TU unit slots can hold key columns (the host picks TU so that the key starts in slot
 // NU - TU or later).
-template <int TU, typename IO, int VEC, int NU>
+template <int TU, typename IO, int VEC, int NU, typename QS>
 __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU],
-                                                  const QStage& qs, const TileGeom& g,
+                                                  const QS& qs, const TileGeom& g,
                                                   double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
@@ -216,8 +216,8 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
     if (u >= g.ub && u < g.nur) {
       float x[VEC];
       row[k].get(x);
-      float qv[VEC];
-      qs.get<VEC>(u - g.ub, qv);
+      typename QS::value_type qv[VEC];
+      qs.template get<VEC>(u - g.ub, qv);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int col = u * VEC + e;
@@ -231,9 +231,9 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
 
 // This lane's share of q . k over the key columns and of o . o over the whole row, for the
 // full-width-RMS control: every unit slot of the row counts toward the square sum.
-template <typename IO, int VEC, int NU>
+template <typename IO, int VEC, int NU, typename QS>
 __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
-                                                 const QStage& qs, const TileGeom& g,
+                                                 const QS& qs, const TileGeom& g,
                                                  double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
@@ -249,8 +249,8 @@ __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
         ss = fma(v, v, ss);
       }
       if (u >= g.ub) {
-        float qv[VEC];
-        qs.get<VEC>(u - g.ub, qv);
+        typename QS::value_type qv[VEC];
+        qs.template get<VEC>(u - g.ub, qv);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const int col = u * VEC + e;

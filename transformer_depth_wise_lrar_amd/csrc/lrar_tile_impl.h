@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   g.r = p.r;
   // The query: spread over the lanes (KS > 0), or staged in LDS from the first key unit's
   // column (KS = 0; the columns of that unit that precede the key hold zero).
-  QStage qst;
-  qst.base = q_lds;
+  QStageD qst;
+  qst.base = reinterpret_cast<double*>(q_lds);
   qst.nv = g.nur - g.ub;
   SpreadQ<KS> qs[ks_slots(KS)];
 #pragma unroll
@@ -529,7 +529,7 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC>;
   const int ub = (p.d - p.r) / VEC;
   const int nur = (p.d + VEC - 1) / VEC;
-  const size_t lds = KS > 0 ? 0 : static_cast<size_t>(nur - ub) * VEC * sizeof(float);
+  const size_t lds = KS > 0 ? 0 : static_cast<size_t>(nur - ub) * VEC * sizeof(double);
   // Workgroups per CU for this instantiation and LDS size (cached: the query is not free).
   static thread_local size_t cached_lds = ~size_t(0);
   static thread_local int cached_per_cu = 0;
