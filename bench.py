@@ -154,17 +154,26 @@ def headline(torch, lrar, args, ev):
     site_ms = [sorted(v)[len(v) // 2] for v in per_site]          # median per site
     site_mean_ms = [sum(v) / len(v) for v in per_site]
     step_ms = sum(ms) / args.steps                                   # mean read time per step
+    steps_ms = [sum(ms[k * S:(k + 1) * S]) for k in range(args.steps)]
+    step_cv = (sum((x - step_ms) ** 2 for x in steps_ms) / args.steps) ** 0.5 / step_ms
     bytes_step = sum(fwd_bytes(T, d, n, 2) for n in range(1, S + 1))
     gbps = bytes_step / (step_ms * 1e-3) / 1e9
     sites = {str(n): dict(ms=round(site_ms[n - 1], 5),
                           GBps=round(fwd_bytes(T, d, n, 2) / (site_ms[n - 1] * 1e-3) / 1e9, 1))
              for n in (1, 2, 5, 9, 13, 25, 37, 49)}
     del srcs, calls
-    return dict(step_ms=step_ms, wall_ms=wall * 1e3 / args.steps, gbps=gbps, T=T, S=S,
+    return dict(step_ms=step_ms, step_cv=step_cv, wall_ms=wall * 1e3 / args.steps, gbps=gbps,
+                T=T, S=S,
                 bytes_step=bytes_step, launches=S, sites=sites, site_mean_ms=site_mean_ms)
 
 
 # ---- the other hot-path steps on their own workloads --------------------------------------------
+
+class Timing(float):
+    """A median launch time in ms that also carries the coefficient of variation of the
+    timed launches it was taken from."""
+    cv = None
+
 
 def time_calls(torch, ev, fn, reps, warm=2):
     tm = Timer(torch)
@@ -175,12 +184,18 @@ def time_calls(torch, ev, fn, reps, warm=2):
         ev()
         tm.run(fn)
     ms = sorted(tm.collect_ms())
-    return ms[len(ms) // 2]
+    t = Timing(ms[len(ms) // 2])
+    mean = sum(ms) / len(ms)
+    t.cv = (sum((x - mean) ** 2 for x in ms) / len(ms)) ** 0.5 / mean
+    return t
 
 
 def row_entry(ms, nbytes):
     g = nbytes / (ms * 1e-3) / 1e9
-    return dict(ms=round(ms, 5), GBps=round(g, 1), frac=round(g / HBM_PEAK_GBPS, 4))
+    e = dict(ms=round(float(ms), 5), GBps=round(g, 1), frac=round(g / HBM_PEAK_GBPS, 4))
+    if getattr(ms, "cv", None) is not None:
+        e["cv"] = round(ms.cv, 4)
+    return e
 
 
 def rows_block_routing(torch, lrar, ev, reps):
@@ -434,6 +449,7 @@ def main():
         "unit": "tokens/s per read site (mean over 49 sites)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(h["step_ms"], 4),
+        "step_cv": round(h["step_cv"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full routing d=1024 r=64, 49 sources / 49 read sites, "
