@@ -127,10 +127,11 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   // e^{z - mref}, running maximum mtop. One vector exp then serves all R rows.
   double mref = -INFINITY, lsum = 0.0, mtop = -INFINITY;
 
-  // bf16 Phase-1 accumulators of a single-source merge are loaded a tile ahead, raw (16
-  // registers a row at four units per lane), and decoded when their tile starts.
-  constexpr bool kAccPre =
-      MODE == kTileMerge && std::is_same<ACC, bf16_bits>::value && VEC == 8;
+  // bf16 Phase-1 accumulators of a single-source merge (with or without the fused update) are
+  // loaded a tile ahead, raw (16 registers a row at four units per lane), and decoded when
+  // their tile starts.
+  constexpr bool kAccPre = (MODE == kTileMerge || MODE == kTileMergeAcc) &&
+                           std::is_same<ACC, bf16_bits>::value && VEC == 8;
   Unit<bf16_bits, 8> apre[kAccPre ? R : 1][kAccPre ? NU : 1];
   const auto load_acc_ahead = [&](const TileGeom& t) {
     if constexpr (kAccPre) {
@@ -373,10 +374,20 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     static_assert(KS == 0, "the key of b' is taken from the row units");
     const IO* bprev = static_cast<const IO*>(p.b_prev);
     IO* bout = static_cast<IO*>(p.b_out);
+    if (group < ntiles) {
+      TileGeom t;
+      set_tile(t, group);
+      load_acc_ahead(t);
+    }
     for (int64_t tile = group; tile < ntiles; tile += ngroups) {
       TileGeom t;
       set_tile(t, tile);
-      begin_tile(t);
+      begin_tile(t, true);
+      if (tile + ngroups < ntiles) {
+        TileGeom tn;
+        set_tile(tn, tile + ngroups);
+        load_acc_ahead(tn);
+      }
       Stage<IO, VEC, NU, R, KS>& st = ring[0];
       load_stage<false>(st, src_base(0), p.src.ld[0], t);
       if (bprev != nullptr) {
