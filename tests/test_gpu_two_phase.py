@@ -45,6 +45,18 @@ def test_stats_shapes(d, r, io):
     check_stats(srcs, qs, r, 1e-6, torch.float32, f"d{d} r{r}")
 
 
+@pytest.mark.parametrize("n", [3, 8])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+def test_stats_full_group_ragged_width(n, io, acc_dtype):
+    """A full group of 12 queries (the kernel variant with no query-count branches) on a width
+    that ends in a partial chunk: the lanes past the row's end load and store the row's last
+    unit, which must leave every element equal to the oracle's."""
+    srcs = sources(n, 37, 1000, io, seed=106, scale=(0.5, 4.0))
+    qs = query(200, seed=107, nq=12)
+    check_stats(srcs, qs, 200, 1e-6, acc_dtype, f"full group n={n} d=1000")
+
+
 def test_stats_strided_queries():
     r = 64
     srcs = sources(3, 31, 1024, "bf16", seed=104)

@@ -8,16 +8,24 @@
 //     queries, laid out from the first key unit's column (columns of that unit before the key
 //     hold zero), so each key element is dotted with every query of the group from LDS;
 //   * each wave takes one token row at a time, rows dealt out in bands over all waves;
-//   * score pass: per source, the key units are loaded together, float64 partial sums of
-//     q_s . k for every query s and of k . k accumulate per lane, and the (queries + 1) sums
-//     are reduced by interleaved DPP chains; lane i keeps z_si;
+//   * score pass: per source, the key units are taken kStatsKeySlots slots at a time; float64
+//     partial sums of q_s . k for every query s and of k . k accumulate per lane, and the
+//     (queries + 1) sums are reduced by interleaved DPP chains; lane i keeps z_si. The next
+//     round's key units (the next source's first round after a source's last) are loaded while
+//     the current round is folded;
 //   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
 //     l = sum_i e_si (float64 on the lanes), written once per row;
 //   * value pass: the row is walked in chunks of 64 units; each chunk of every source is loaded
 //     once and folded into four queries' accumulators at a time, with the weights read from
 //     LDS; the accumulators are written straight out (acc = sum_i e_si o_i, not normalised),
-//     each store instruction covering 1 KiB of one accumulator row. The other waves of the CU
-//     keep HBM busy while a wave folds.
+//     each store instruction covering 1 KiB of one accumulator row. The last pass over a chunk
+//     loads the next chunk of each source as soon as it has taken that source's values, so the
+//     loads are in flight while the pass folds and stores.
+// Every load is issued by every lane whatever the source count and the row's width: a source
+// slot past n reads source 0 and a unit past the row (or before the key) reads the nearest unit
+// inside it, and those values are discarded. With loads under conditions the compiler cannot
+// count the loads in flight and waits for all of them, and for every earlier store, before it
+// uses any one.
 // Each cached source row is read from HBM once per query group (its key again from L2), and
 // every accumulator element is written once.
 
@@ -38,9 +46,13 @@ constexpr size_t kStatsStaticLds =
 
 }  // namespace
 
-template <typename IO, int VEC, typename ACC>
-__global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nqg) {
+// FULLQ: the group holds kStatsMaxQ queries, so no pass or store depends on the group's size
+// (with a smaller group, those branches leave the compiler unsure how many stores are in flight
+// and its waits for loads then also wait for stores).
+template <typename IO, int VEC, typename ACC, bool FULLQ>
+__global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nq_arg) {
   extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [nqg][rq]
+  const int nqg = FULLQ ? kStatsMaxQ : nq_arg;
   // Scores of the wave's current row: z[s][i] for query s, source i; and their weights.
   __shared__ double z_lds[kStatsWaves][kStatsMaxQ][kStatsMaxSrc];
   __shared__ __attribute__((aligned(16))) float w_lds[kStatsWaves][kStatsMaxSrc][kStatsMaxQ];
@@ -63,55 +75,89 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
   }
   __syncthreads();
 
+  // source slots past n stand in with source 0 (read, never used)
+  const IO* sp[kStatsMaxSrc];
+  int64_t sld[kStatsMaxSrc];
+#pragma unroll
+  for (int i = 0; i < kStatsMaxSrc; ++i) {
+    sp[i] = static_cast<const IO*>(i < n ? p.src.ptr[i] : p.src.ptr[0]);
+    sld[i] = i < n ? p.src.ld[i] : p.src.ld[0];
+  }
+  constexpr bool kSplit = std::is_same<IO, bf16_bits>::value && std::is_same<ACC, float>::value;
+  const int ccol = kWave * VEC;  // columns per chunk
+
   for (int64_t row = wave; row < p.T; row += nwaves) {
-    // ---- score pass: z_si of every (query, source) pair into z_lds
-    for (int i = 0; i < n; ++i) {
-      const IO* rowp = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
-      double red[kStatsMaxQ + 1];
+    // ---- score pass: z_si of every (query, source) pair into z_lds. Rounds of kStatsKeySlots
+    // slots run source by source; the next round's key units are loaded before this round's
+    // are folded.
+    const auto key_row = [&](int i) {
+      return static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
+    };
+    const auto load_keys = [&](const IO* rp, int kb, Unit<IO, VEC>(&dst)[kStatsKeySlots]) {
 #pragma unroll
-      for (int s = 0; s <= kStatsMaxQ; ++s) red[s] = 0.0;
-      for (int kb = k_lo; kb < nslot; kb += kStatsKeySlots) {
-        Unit<IO, VEC> ku[kStatsKeySlots];
+      for (int t = 0; t < kStatsKeySlots; ++t) {
+        int u = lane + kWave * (kb + t);
+        u = u < ub ? ub : (u < nur ? u : nur - 1);
+        dst[t].load_cached(rp + u * VEC);
+      }
+    };
+    Unit<IO, VEC> kn[kStatsKeySlots];
+    load_keys(key_row(0), k_lo, kn);
+    double red[kStatsMaxQ + 1];
 #pragma unroll
-        for (int t = 0; t < kStatsKeySlots; ++t) {
-          const int u = lane + kWave * (kb + t);
-          if (kb + t < nslot && u >= ub && u < nur) ku[t].load_cached(rowp + u * VEC);
-          else ku[t].zero();
-        }
+    for (int s = 0; s <= kStatsMaxQ; ++s) red[s] = 0.0;
+    for (int i = 0, kb = k_lo; i < n;) {
+      // this round's key values leave the load registers before the next round's loads
+      // reuse them, so no register copy has to wait for those loads
+      float x[kStatsKeySlots][VEC];
 #pragma unroll
-        for (int t = 0; t < kStatsKeySlots; ++t) {
-          const int u = lane + kWave * (kb + t);
-          if (kb + t < nslot && u >= ub && u < nur) {
-            float x[VEC];
-            ku[t].get(x);
-            double kv[VEC];
+      for (int t = 0; t < kStatsKeySlots; ++t) {
+        kn[t].get(x[t]);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              kv[e] = (u * VEC + e) >= c0 ? static_cast<double>(x[e]) : 0.0;
-              red[kStatsMaxQ] = fma(kv[e], kv[e], red[kStatsMaxQ]);
+        for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(x[t][e]));
+      }
+      const bool last = kb + kStatsKeySlots >= nslot;  // this round ends source i
+      const int i_next = last ? (i + 1 < n ? i + 1 : i) : i;
+      const int kb_next = last ? k_lo : kb + kStatsKeySlots;
+      load_keys(key_row(i_next), kb_next, kn);
+#pragma unroll
+      for (int t = 0; t < kStatsKeySlots; ++t) {
+        const int u = lane + kWave * (kb + t);
+        if (kb + t < nslot && u >= ub && u < nur) {
+          double kv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            kv[e] = (u * VEC + e) >= c0 ? static_cast<double>(x[t][e]) : 0.0;
+            red[kStatsMaxQ] = fma(kv[e], kv[e], red[kStatsMaxQ]);
+          }
+          // One query at a time: the scheduling barrier keeps the query values of later
+          // queries from being read ahead into registers.
+#pragma unroll
+          for (int s = 0; s < kStatsMaxQ; ++s) {
+            if (s < nqg) {
+              const QStage qs{q_lds + s * rq, nv};
+              float qv[VEC];
+              qs.get<VEC>(u - ub, qv);
+#pragma unroll
+              for (int e = 0; e < VEC; ++e)
+                red[s] = fma(static_cast<double>(qv[e]), kv[e], red[s]);
             }
-            // One query at a time: the scheduling barrier keeps the query values of later
-            // queries from being read ahead into registers.
-#pragma unroll
-            for (int s = 0; s < kStatsMaxQ; ++s) {
-              if (s < nqg) {
-                const QStage qs{q_lds + s * rq, nv};
-                float qv[VEC];
-                qs.get<VEC>(u - ub, qv);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                  red[s] = fma(static_cast<double>(qv[e]), kv[e], red[s]);
-              }
-              __builtin_amdgcn_sched_barrier(0);
-            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
-      wave_sums_dpp(red);
-      const double rho = sqrt(red[kStatsMaxQ] / p.r + p.eps);
+      if (last) {
+        wave_sums_dpp(red);
+        const double rho = sqrt(red[kStatsMaxQ] / p.r + p.eps);
 #pragma unroll
-      for (int s = 0; s < kStatsMaxQ; ++s)
-        if (lane == s && s < nqg) z_lds[wv][s][i] = red[s] / rho;
+        for (int s = 0; s < kStatsMaxQ; ++s) {
+          if (lane == s && s < nqg) z_lds[wv][s][i] = red[s] / rho;
+          red[s] = 0.0;
+        }
+        red[kStatsMaxQ] = 0.0;
+        ++i;
+      }
+      kb = kb_next;
     }
 
     // ---- statistics per query (lanes = sources)
@@ -145,37 +191,36 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
     for (int s = 0; s < kStatsMaxQ; ++s)
       if (s < nqg && lane < n) w_lds[wv][lane][s] = ew[s];
     __builtin_amdgcn_wave_barrier();
-    constexpr bool kSplit = std::is_same<IO, bf16_bits>::value && std::is_same<ACC, float>::value;
-    const int ccol = kWave * VEC;  // columns per chunk
-    Unit<IO, VEC> buf[kStatsMaxSrc];
-    const auto load_chunk = [&](int c) {
+    const auto load_src = [&](const IO* rp, int c, Unit<IO, VEC>& dst) {
       if constexpr (kSplit) {
-        const int col0 = c * ccol + 4 * lane;
-        const int col1 = col0 + ccol / 2;
-#pragma unroll
-        for (int i = 0; i < kStatsMaxSrc; ++i) {
-          const bf16_bits* rp = static_cast<const bf16_bits*>(p.src.ptr[i]) + row * p.src.ld[i];
-          u32x2 lo = {0u, 0u}, hi = {0u, 0u};
-          if (i < n && col0 < p.d) lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col0));
-          if (i < n && col1 < p.d) hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col1));
-          buf[i].raw = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+        int col0 = c * ccol + 4 * lane;
+        int col1 = col0 + ccol / 2;
+        col0 = col0 < p.d ? col0 : p.d - 4;
+        col1 = col1 < p.d ? col1 : p.d - 4;
+        const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col0));
+        const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col1));
+        dst.raw = u32x4{lo.x, lo.y, hi.x, hi.y};
       } else {
-        const int u = lane + kWave * c;
-#pragma unroll
-        for (int i = 0; i < kStatsMaxSrc; ++i) {
-          if (i < n && u < nur)
-            buf[i].load(static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i] + u * VEC);
-          else
-            buf[i].zero();
-        }
+        int u = lane + kWave * c;
+        u = u < nur ? u : nur - 1;
+        dst.load(rp + u * VEC);
       }
     };
-    const auto fold_chunk = [&](int c) {
-      const int u = lane + kWave * c;
+    Unit<IO, VEC> buf[kStatsMaxSrc];
+    // issued in source order, as the reloads below are, so a wait for one source's unit is
+    // a wait for it and the loads before it only
 #pragma unroll
-      for (int s0 = 0; s0 < kStatsMaxQ; s0 += kValQ) {
-        if (s0 < nqg) {
+    for (int i = 0; i < kStatsMaxSrc; ++i) {
+      load_src(sp[i] + row * sld[i], 0, buf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int c = 0; c < nslot; ++c) {
+      const int u = lane + kWave * c;
+      const int cn = c + 1 < nslot ? c + 1 : c;  // the last chunk reloads itself
+      // passes in reverse order, so the one that reloads (queries 0..3, always present) is last
+#pragma unroll
+      for (int s0 = kStatsMaxQ - kValQ; s0 >= 0; s0 -= kValQ) {
+        if (s0 == 0 || s0 < nqg) {
           float a[kValQ][VEC];
 #pragma unroll
           for (int j = 0; j < kValQ; ++j)
@@ -183,13 +228,13 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
             for (int e = 0; e < VEC; ++e) a[j][e] = 0.f;
 #pragma unroll
           for (int i = 0; i < kStatsMaxSrc; ++i) {
+            float x[VEC];
+            buf[i].get(x);
             if (i < n) {
               float w[kValQ];
               const float* wp = &w_lds[wv][i][s0];
 #pragma unroll
               for (int j = 0; j < kValQ; ++j) w[j] = wp[j];
-              float x[VEC];
-              buf[i].get(x);
 #pragma unroll
               for (int j = 0; j < kValQ; ++j)
 #pragma unroll
@@ -198,34 +243,43 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
           }
           int64_t off = static_cast<int64_t>(q0 + s0) * p.acc_qstride + row * p.acc_ld;
           asm volatile("" : "+v"(off));
+          // A lane past the row's end loaded the row's last unit in place of its own, so it
+          // holds that unit's sums bit for bit and stores them there too: every lane stores,
+          // with no branch, and the duplicate writes carry the same bytes.
           if constexpr (kSplit) {
-            const int col0 = c * ccol + 4 * lane;
-            const int col1 = col0 + ccol / 2;
+            int col0 = c * ccol + 4 * lane;
+            int col1 = col0 + ccol / 2;
+            col0 = col0 < p.d ? col0 : p.d - 4;
+            col1 = col1 < p.d ? col1 : p.d - 4;
             float* d0 = static_cast<float*>(p.acc) + off;
 #pragma unroll
             for (int j = 0; j < kValQ; ++j) {
               if (s0 + j < nqg) {
                 float* dj = d0 + j * p.acc_qstride;
-                if (col0 < p.d)
-                  out_store(f32x4{a[j][0], a[j][1], a[j][2], a[j][3]},
-                            reinterpret_cast<f32x4*>(dj + col0));
-                if (col1 < p.d)
-                  out_store(f32x4{a[j][4], a[j][5], a[j][6], a[j][7]},
-                            reinterpret_cast<f32x4*>(dj + col1));
+                out_store(f32x4{a[j][0], a[j][1], a[j][2], a[j][3]},
+                          reinterpret_cast<f32x4*>(dj + col0));
+                out_store(f32x4{a[j][4], a[j][5], a[j][6], a[j][7]},
+                          reinterpret_cast<f32x4*>(dj + col1));
               }
             }
-          } else if (u < nur) {
-            ACC* d0 = static_cast<ACC*>(p.acc) + off + u * VEC;
+          } else {
+            const int us = u < nur ? u : nur - 1;
+            ACC* d0 = static_cast<ACC*>(p.acc) + off + us * VEC;
 #pragma unroll
             for (int j = 0; j < kValQ; ++j)
               if (s0 + j < nqg) store_acc<ACC, VEC>(d0 + j * p.acc_qstride, a[j]);
           }
+          if (s0 == 0) {
+            // the next chunk, after this chunk's last stores: a wait for one source's unit is
+            // then a wait for it and the loads and stores issued before it
+#pragma unroll
+            for (int i = 0; i < kStatsMaxSrc; ++i) {
+              load_src(sp[i] + row * sld[i], cn, buf[i]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
       }
-    };
-    for (int c = 0; c < nslot; ++c) {
-      load_chunk(c);
-      fold_chunk(c);
     }
     // the next row's weights overwrite w_lds only after every lane has read this row's
     __builtin_amdgcn_wave_barrier();
@@ -264,11 +318,12 @@ size_t lds_limit() {
 
 template <typename IO, int VEC, typename ACC>
 hipError_t launch_stats_tile_t(const StatsParams& p, int qg, hipStream_t s) {
-  auto kern = k_stats_tile<IO, VEC, ACC>;
   const int ub = (p.d - p.r) / VEC;
   const int rq = p.d - ub * VEC;
   for (int q0 = 0; q0 < p.nq; q0 += qg) {
     const int nqg = (p.nq - q0) < qg ? (p.nq - q0) : qg;
+    auto kern = nqg == kStatsMaxQ ? k_stats_tile<IO, VEC, ACC, true>
+                                  : k_stats_tile<IO, VEC, ACC, false>;
     const size_t lds = static_cast<size_t>(nqg) * rq * sizeof(float);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStatsBlock, lds) !=
