@@ -55,6 +55,15 @@ lrar_status check_shape(const char* fn, int64_t T, int32_t d, int32_t r, double 
   return LRAR_OK;
 }
 
+// The read kernels address a tile's rows through 32-bit byte offsets from the tile's first
+// row, so a row stride must stay below 256 MiB.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 28;
+bool stride_ok(int64_t ld, size_t es) { return ld <= kMaxRowBytes / static_cast<int64_t>(es); }
+lrar_status stride_fail(const char* fn, const char* what, int64_t ld) {
+  return fail(LRAR_ERR_UNSUPPORTED, "%s: %s = %lld elements is a row stride of 256 MiB or more",
+              fn, what, (long long)ld);
+}
+
 // Fills the source table; also reports whether every row start is 16-byte aligned.
 lrar_status check_sources(const char* fn, int64_t T, int32_t d, lrar_dtype io, int32_t n,
                           int32_t n_min, const void* const* src, const int64_t* src_ld,
@@ -70,6 +79,7 @@ lrar_status check_sources(const char* fn, int64_t T, int32_t d, lrar_dtype io, i
     if (src[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: src[%d] is null", fn, i);
     if (src_ld[i] < d)
       return fail(LRAR_ERR_INVALID, "%s: src_ld[%d] = %lld < d = %d", fn, i, (long long)src_ld[i], d);
+    if (!stride_ok(src_ld[i], esize(io))) return stride_fail(fn, "src_ld", src_ld[i]);
     S.ptr[i] = src[i];
     S.ld[i] = src_ld[i];
     if (!aligned16(src[i]) || (src_ld[i] % vec) != 0) vec_ok = false;
@@ -212,6 +222,7 @@ lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_
     if (key_ld[i] < r)
       return fail(LRAR_ERR_INVALID, "%s: key_ld[%d] = %lld < r = %d", fn, i,
                   (long long)key_ld[i], r);
+    if (!stride_ok(key_ld[i], esize(io))) return stride_fail(fn, "key_ld", key_ld[i]);
     if (key[i] == out && out != nullptr)
       return fail(LRAR_ERR_INVALID, "%s: out aliases key[%d]", fn, i);
     const uintptr_t bits = reinterpret_cast<uintptr_t>(key[i]) |
@@ -305,6 +316,7 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
   if (st != LRAR_OK) return st;
   if (!dtype_ok(acc_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown acc dtype", fn);
   if (acc_ld < d) return fail(LRAR_ERR_INVALID, "%s: acc_ld = %lld < d", fn, (long long)acc_ld);
+  if (!stride_ok(acc_ld, esize(acc_dtype))) return stride_fail(fn, "acc_ld", acc_ld);
   if (T > 0 && (m == nullptr || l == nullptr || acc == nullptr || out == nullptr))
     return fail(LRAR_ERR_INVALID, "%s: null m, l, acc or out", fn);
   if (T > 0 && n > 0 && q == nullptr) return fail(LRAR_ERR_INVALID, "%s: q is null", fn);
@@ -367,6 +379,9 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
     return fail(LRAR_ERR_INVALID, "%s: b_ld = %lld < d", fn, (long long)b_ld);
   if (b_out_ld < d)
     return fail(LRAR_ERR_INVALID, "%s: b_out_ld = %lld < d", fn, (long long)b_out_ld);
+  if (!stride_ok(acc_ld, esize(acc_dtype))) return stride_fail(fn, "acc_ld", acc_ld);
+  if (!stride_ok(o_ld, esize(io))) return stride_fail(fn, "o_ld", o_ld);
+  if (b != nullptr && !stride_ok(b_ld, esize(io))) return stride_fail(fn, "b_ld", b_ld);
   if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
   if (T > 0 && (m == nullptr || l == nullptr || acc == nullptr || o == nullptr ||
                 b_out == nullptr || q == nullptr || out == nullptr))

@@ -49,6 +49,51 @@ using bf16_bits = uint16_t;
 // Native 16-byte vector types (accepted by the non-temporal load/store builtins).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- loads with a predicate and no branch ---------------------------------------------------
+// A raw buffer resource over [base, base + bytes) (CDNA resource word 3: 32-bit data format,
+// no stride). A load through it at a byte offset at or past `bytes` returns zero and reads no
+// memory: the hardware's range check. A lane with nothing to load passes kNoLoad, and a whole
+// load is switched off with an empty span; either way the instruction is still issued. Loads
+// taken under branches would leave the compiler unsure how many loads are in flight, and its
+// wait for one of them would then wait for all.
+constexpr uint32_t kNoLoad = 0x80000000u;  // past every span used here (each < 2^31 bytes)
+constexpr int kCachePolicyNT = 2;          // the nontemporal bit of the buffer load's policy
+// base and bytes must be the same in every lane of the wave: the resource lives in scalar
+// registers, and they are read from the first active lane (else the compiler, unable to prove
+// them uniform, would wrap each load in a loop over the distinct values).
+struct Span {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ Span(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(n), 0x00020000);
+  }
+  template <bool NT>
+  __device__ __forceinline__ u32x4 b128(uint32_t off) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rsrc, static_cast<int>(off), 0, NT ? kCachePolicyNT : 0));
+  }
+  template <bool NT>
+  __device__ __forceinline__ u32x2 b64(uint32_t off) const {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                         rsrc, static_cast<int>(off), 0, NT ? kCachePolicyNT : 0));
+  }
+  template <bool NT>
+  __device__ __forceinline__ uint32_t b32(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(off), 0,
+                                                NT ? kCachePolicyNT : 0);
+  }
+  template <bool NT>
+  __device__ __forceinline__ uint16_t b16(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b16(rsrc, static_cast<int>(off), 0,
+                                                NT ? kCachePolicyNT : 0);
+  }
+};
 
 // ---- scalar conversions ------------------------------------------------------------------
 
@@ -107,6 +152,10 @@ struct Unit<bf16_bits, 8> {
   __device__ __forceinline__ void load_cached(const bf16_bits* p) {
     raw = *reinterpret_cast<const u32x4*>(p);
   }
+  template <bool NT = true>
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    raw = s.b128<NT>(off);
+  }
   __device__ __forceinline__ void zero() { raw = u32x4{0u, 0u, 0u, 0u}; }
   // Encodes 8 floats (round to nearest even) / writes the raw unit with a streaming store.
   __device__ __forceinline__ void set(const float (&x)[8]) {
@@ -139,6 +188,10 @@ struct Unit<float, 4> {
   __device__ __forceinline__ void load_cached(const float* p) {
     raw = *reinterpret_cast<const f32x4*>(p);
   }
+  template <bool NT = true>
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    raw = __builtin_bit_cast(f32x4, s.b128<NT>(off));
+  }
   __device__ __forceinline__ void zero() { raw = f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void set(const float (&x)[4]) { raw = f32x4{x[0], x[1], x[2], x[3]}; }
   __device__ __forceinline__ void store(float* p) const {
@@ -157,6 +210,11 @@ struct Unit<T, 1> {
   T raw;
   __device__ __forceinline__ void load(const T* p) { raw = *p; }
   __device__ __forceinline__ void load_cached(const T* p) { raw = *p; }
+  template <bool NT = false>
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    if constexpr (sizeof(T) == 2) raw = __builtin_bit_cast(T, s.b16<NT>(off));
+    else raw = __builtin_bit_cast(T, s.b32<NT>(off));
+  }
   __device__ __forceinline__ void zero() { raw = T(0); }
   __device__ __forceinline__ void set(const float (&x)[1]) { raw = from_f32<T>(x[0]); }
   __device__ __forceinline__ void store(T* p) const { *p = raw; }
@@ -244,7 +302,6 @@ __device__ __forceinline__ void store_acc(A* p, const float (&x)[VEC]) {
 // VEC gradient values of type G (float32 or bf16) as floats, and back with round to nearest
 // even; on the vector path a row's units start at multiples of 4 * VEC (float32) or 2 * VEC
 // (bf16) bytes.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename G, int VEC>
 __device__ __forceinline__ void load_grad(const G* p, float (&x)[VEC]) {

@@ -37,6 +37,7 @@ struct KeyPiece;
 template <typename IO>
 struct KeyPiece<IO, 0> {
   __device__ __forceinline__ void load(const IO*) {}
+  __device__ __forceinline__ void load_span(const Span&, uint32_t) {}
   __device__ __forceinline__ void zero() {}
 };
 
@@ -44,6 +45,9 @@ template <>
 struct KeyPiece<bf16_bits, 1> {
   uint32_t raw;
   __device__ __forceinline__ void load(const bf16_bits* p) { raw = *p; }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    raw = s.b16<false>(off);
+  }
   __device__ __forceinline__ void zero() { raw = 0u; }
   __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = __uint_as_float(raw << 16); }
 };
@@ -53,6 +57,9 @@ struct KeyPiece<bf16_bits, 2> {
   uint32_t raw;
   __device__ __forceinline__ void load(const bf16_bits* p) {
     raw = *reinterpret_cast<const uint32_t*>(p);
+  }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    raw = s.b32<false>(off);
   }
   __device__ __forceinline__ void zero() { raw = 0u; }
   __device__ __forceinline__ void get(float (&x)[2]) const {
@@ -70,6 +77,11 @@ struct KeyPiece<bf16_bits, 4> {
     raw[0] = v.x;
     raw[1] = v.y;
   }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    const u32x2 v = s.b64<false>(off);
+    raw[0] = v.x;
+    raw[1] = v.y;
+  }
   __device__ __forceinline__ void zero() { raw[0] = raw[1] = 0u; }
   __device__ __forceinline__ void get(float (&x)[4]) const {
     x[0] = __uint_as_float(raw[0] << 16);
@@ -83,6 +95,9 @@ template <>
 struct KeyPiece<float, 1> {
   float raw;
   __device__ __forceinline__ void load(const float* p) { raw = *p; }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    raw = __uint_as_float(s.b32<false>(off));
+  }
   __device__ __forceinline__ void zero() { raw = 0.f; }
   __device__ __forceinline__ void get(float (&x)[1]) const { x[0] = raw; }
 };
@@ -95,6 +110,11 @@ struct KeyPiece<float, 2> {
     const f32x2 v = *reinterpret_cast<const f32x2*>(p);
     raw[0] = v.x;
     raw[1] = v.y;
+  }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    const u32x2 v = s.b64<false>(off);
+    raw[0] = __uint_as_float(v.x);
+    raw[1] = __uint_as_float(v.y);
   }
   __device__ __forceinline__ void zero() { raw[0] = raw[1] = 0.f; }
   __device__ __forceinline__ void get(float (&x)[2]) const {
@@ -112,6 +132,13 @@ struct KeyPiece<float, 4> {
     raw[1] = v.y;
     raw[2] = v.z;
     raw[3] = v.w;
+  }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+    const u32x4 v = s.b128<false>(off);
+    raw[0] = __uint_as_float(v.x);
+    raw[1] = __uint_as_float(v.y);
+    raw[2] = __uint_as_float(v.z);
+    raw[3] = __uint_as_float(v.w);
   }
   __device__ __forceinline__ void zero() { raw[0] = raw[1] = raw[2] = raw[3] = 0.f; }
   __device__ __forceinline__ void get(float (&x)[4]) const {
@@ -131,6 +158,10 @@ struct KeyPieceUnits {
   __device__ __forceinline__ void load(const IO* p) {
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) u[k].load_cached(p + k * kPer);
+  }
+  __device__ __forceinline__ void load_span(const Span& s, uint32_t off) {
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) u[k].template load_span<false>(s, off + 16u * k);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -175,12 +206,26 @@ struct TileGeom {
 
 // Loads one source's tile. KEYS_ONLY: only the key (the spread pieces, or the key units when
 // KS = 0). SEP: the spread key pieces come from the source's own key rows (kbase, row stride
-// kld) instead of the value row's last r columns.
+// kld) instead of the value row's last r columns. Slots outside the tile (a row past the
+// tile's last, a unit past the row's end or, KEYS_ONLY, before the key, a key piece past the
+// key) read as zero.
+//
+// Two ways to skip those slots. load_stage_branchy skips them under branches, and a stage that
+// is not needed (live false) is not loaded at all; the compiler then cannot count the loads in
+// flight and waits for all of them before it uses the oldest stage. load_stage_exact issues
+// every load in every lane through a Span: skipped slots take the offset kNoLoad and a stage
+// that is not needed loads over an empty span, reading no memory either way, so every item of
+// the ring leaves the same loads in flight and a wait for a stage is a wait for it alone.
+// Measured on MI355X, exact waits pay where each stage carries much vector work (the key read
+// from the row units, KS = 0: wide keys and the full-RMS control, up to a fifth faster), and
+// cost a few percent on the short-key streaming reads, where the other waves already hide the
+// latency; load_stage picks by KS.
 template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
-__device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
-                                           const IO* __restrict__ base, int64_t ld,
-                                           const TileGeom& g, const IO* kbase = nullptr,
-                                           int64_t kld = 0) {
+__device__ __forceinline__ void load_stage_branchy(Stage<IO, VEC, NU, R, KS>& st,
+                                                   const IO* __restrict__ base, int64_t ld,
+                                                   const TileGeom& g, const IO* kbase = nullptr,
+                                                   int64_t kld = 0, bool live = true) {
+  if (!live) return;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const IO* rowp = base + (g.r0 + j) * ld;  // wave-uniform: lane offsets stay 32-bit
@@ -199,6 +244,56 @@ __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
       }
     }
   }
+}
+
+template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
+__device__ __forceinline__ void load_stage_exact(Stage<IO, VEC, NU, R, KS>& st,
+                                                 const IO* __restrict__ base, int64_t ld,
+                                                 const TileGeom& g, const IO* kbase = nullptr,
+                                                 int64_t kld = 0, bool live = true) {
+  constexpr uint32_t es = sizeof(IO);
+  const uint32_t row_bytes = static_cast<uint32_t>(ld) * es;
+  const uint32_t span = live ? static_cast<uint32_t>((g.nrow - 1) * ld + g.nur * VEC) * es : 0u;
+  const Span rows(base + g.r0 * ld, span);
+  if constexpr (KS > 0) {
+    const bool lane_ok = g.lane * KS < g.r;
+    if constexpr (SEP) {
+      const uint32_t kspan = live ? static_cast<uint32_t>((g.nrow - 1) * kld + g.r) * es : 0u;
+      const Span keys(kbase + g.r0 * kld, kspan);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const uint32_t off = static_cast<uint32_t>(j * kld + g.lane * KS) * es;
+        st.kp[j].load_span(keys, j < g.nrow && lane_ok ? off : kNoLoad);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const uint32_t off = j * row_bytes + static_cast<uint32_t>(g.c0 + g.lane * KS) * es;
+        st.kp[j].load_span(rows, j < g.nrow && lane_ok ? off : kNoLoad);
+      }
+    }
+  }
+  if constexpr (!(KEYS_ONLY && KS > 0)) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = g.unit(k);
+        const bool want = j < g.nrow && u < g.nur && (!KEYS_ONLY || u >= g.ub);
+        const uint32_t off = j * row_bytes + static_cast<uint32_t>(u) * (VEC * es);
+        st.t.u[j][k].load_span(rows, want ? off : kNoLoad);
+      }
+    }
+  }
+}
+
+template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
+__device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
+                                           const IO* __restrict__ base, int64_t ld,
+                                           const TileGeom& g, const IO* kbase = nullptr,
+                                           int64_t kld = 0, bool live = true) {
+  if constexpr (KS == 0) load_stage_exact<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
+  else load_stage_branchy<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
 }
 
 // This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the

@@ -103,6 +103,11 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   const int64_t ntiles = (p.T + R - 1) / R;
   int parity = 0;
   const auto src_base = [&](int i) { return static_cast<const IO*>(p.src.ptr[i]); };
+  // The ring issues one stage load per item, also for the items past the last source: those
+  // load over an empty span (no memory read), so every item leaves the same loads in flight
+  // and a wait for a stage is a wait for that stage only.
+  const auto clamp_src = [&](int i) { return i < n ? i : n - 1; };
+  const IO* const kNoKeys = nullptr;  // the key base of a read whose keys are in its rows
   constexpr bool kSep = MODE == kTileKeys;
   const auto key_base = [&](int i) -> const IO* {
     if constexpr (kSep) return static_cast<const IO*>(keys.ptr[i]);
@@ -322,15 +327,19 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       begin_tile(t);
       // pass 1: scores from the key slices
 #pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<true>(ring[b], src_base(b), p.src.ld[b], t);
+      for (int b = 0; b < PF; ++b) {
+        const int ia = clamp_src(b);
+        load_stage<true>(ring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0, b < n);
+        if constexpr (KS == 0) __builtin_amdgcn_sched_barrier(0);  // stages issued in ring order
+      }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
+          const int ia = clamp_src(i + PF);
+          load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
+                           i + PF < n);
           if (i < n) {
-            if (i + PF < n)
-              load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], t);
             const double z = stage_scores(ring[b], t);
 #pragma unroll
             for (int j = 0; j < R; ++j) {
@@ -353,15 +362,19 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       // pass 2: the values (the row units only)
       Stage<IO, VEC, NU, R, 0> vring[PF + 1];
 #pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n) load_stage<false>(vring[b], src_base(b), p.src.ld[b], t);
+      for (int b = 0; b < PF; ++b) {
+        const int ia = clamp_src(b);
+        load_stage<false>(vring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0, b < n);
+        __builtin_amdgcn_sched_barrier(0);  // stages issued in ring order
+      }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
+          const int ia = clamp_src(i + PF);
+          load_stage<false>(vring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
+                            i + PF < n);
           if (i < n) {
-            if (i + PF < n)
-              load_stage<false>(vring[(b + PF) % (PF + 1)], src_base(i + PF), p.src.ld[i + PF], t);
 #pragma unroll
             for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(w[j], i), vring[b].t.u[j]);
           }
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         load_acc_ahead(tn);
       }
       Stage<IO, VEC, NU, R, KS>& st = ring[0];
-      load_stage<false>(st, src_base(0), p.src.ld[0], t);
+      load_stage_branchy<false>(st, src_base(0), p.src.ld[0], t);
       if (bprev != nullptr) {
         Tile<IO, VEC, NU, R> bt;
 #pragma unroll
@@ -442,14 +455,16 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     TileGeom t0, t1;
     if (tile < ntiles) {
       set_tile(t0, tile);
-      load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
+      load_stage_branchy<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0),
+                                      key_ld(0));
       load_acc_ahead(t0);
     }
     for (; tile < ntiles; tile += 2 * ngroups) {
       const bool more = tile + ngroups < ntiles;
       if (more) {
         set_tile(t1, tile + ngroups);
-        load_stage<false, kSep>(ring[1], src_base(0), p.src.ld[0], t1, key_base(0), key_ld(0));
+        load_stage_branchy<false, kSep>(ring[1], src_base(0), p.src.ld[0], t1, key_base(0),
+                                        key_ld(0));
       }
       begin_tile(t0, true);
       if (more) load_acc_ahead(t1);
@@ -459,7 +474,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         const bool next = tile + 2 * ngroups < ntiles;
         if (next) {
           set_tile(t0, tile + 2 * ngroups);
-          load_stage<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0), key_ld(0));
+          load_stage_branchy<false, kSep>(ring[0], src_base(0), p.src.ld[0], t0, key_base(0),
+                                          key_ld(0));
         }
         begin_tile(t1, true);
         if (next) load_acc_ahead(t0);
@@ -473,19 +489,21 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       set_tile(t, tile);
       begin_tile(t);
 #pragma unroll
-      for (int b = 0; b < PF; ++b)
-        if (b < n)
-          load_stage<false, kSep>(ring[b], src_base(b), p.src.ld[b], t, key_base(b), key_ld(b));
+      for (int b = 0; b < PF; ++b) {
+        const int ia = clamp_src(b);
+        load_stage<false, kSep>(ring[b], src_base(ia), p.src.ld[ia], t, key_base(ia), key_ld(ia),
+                                b < n);
+        // stages issued in ring order, so a wait for the oldest is a wait for it alone
+        if constexpr (KS == 0) __builtin_amdgcn_sched_barrier(0);
+      }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
-          if (i < n) {
-            if (i + PF < n)
-              load_stage<false, kSep>(ring[(b + PF) % (PF + 1)], src_base(i + PF),
-                                      p.src.ld[i + PF], t, key_base(i + PF), key_ld(i + PF));
-            fold_source(ring[b], t, i);
-          }
+          const int ia = clamp_src(i + PF);
+          load_stage<false, kSep>(ring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t,
+                                  key_base(ia), key_ld(ia), i + PF < n);
+          if (i < n) fold_source(ring[b], t, i);
         }
       }
       finish_tile(t);
