@@ -25,8 +25,8 @@
  *     allocates, frees or synchronises.
  *   - Matrices are row-major with an explicit row stride in ELEMENTS of their own type
  *     (ld >= d). A source is [T, d]; several sources may be the same buffer. The row stride
- *     of a source, key, accumulator or partial sum must stay below 256 MiB (LRAR_ERR_UNSUPPORTED
- *     otherwise): the kernels address a tile's rows by 32-bit byte offsets.
+ *     of a source, key, accumulator or partial sum may not exceed 256 MiB (else
+ *     LRAR_ERR_UNSUPPORTED): the kernels address a tile's rows by 32-bit byte offsets.
  *   - io selects the element type of sources and of out: LRAR_BF16 (raw bfloat16 bits) or
  *     LRAR_F32. q, m, l, alpha, dout, dsrc and dq are always float32.
  *   - Arithmetic: scores, RMS and softmax in float64 (bf16 x fp32 products are exact in

@@ -261,3 +261,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lrar, "_lib", None)
     with pytest.raises(lrar.LibraryNotBuilt):
         lrar.lib()
+
+
+def test_row_strides_of_256_mib_are_unsupported(L):
+    """The read kernels address a tile's rows by 32-bit byte offsets: a row stride above 256 MiB
+    is refused before any device work (T = 0 keeps the call host-only)."""
+    most = 1 << 27  # bf16 elements: 256 MiB, the largest stride taken
+    assert fwd(L, T=0, ld=most) == lrar.LRAR_OK
+    assert fwd(L, T=0, ld=most + 8) == lrar.LRAR_ERR_UNSUPPORTED
+    assert "row stride" in L.lrar_last_error().decode()
+    assert merge_acc(L, T=0, o_ld=most + 8) == lrar.LRAR_ERR_UNSUPPORTED
+    assert merge_acc(L, T=0, b_ld=most + 8) == lrar.LRAR_ERR_UNSUPPORTED
+    assert merge_acc(L, T=0, acc_ld=most // 2 + 8) == lrar.LRAR_ERR_UNSUPPORTED  # fp32 acc

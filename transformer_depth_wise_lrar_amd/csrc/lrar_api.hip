@@ -56,11 +56,11 @@ lrar_status check_shape(const char* fn, int64_t T, int32_t d, int32_t r, double 
 }
 
 // The read kernels address a tile's rows through 32-bit byte offsets from the tile's first
-// row, so a row stride must stay below 256 MiB.
+// row (at most 4 rows, under 2^31 bytes), so a row stride may not exceed 256 MiB.
 constexpr int64_t kMaxRowBytes = int64_t(1) << 28;
 bool stride_ok(int64_t ld, size_t es) { return ld <= kMaxRowBytes / static_cast<int64_t>(es); }
 lrar_status stride_fail(const char* fn, const char* what, int64_t ld) {
-  return fail(LRAR_ERR_UNSUPPORTED, "%s: %s = %lld elements is a row stride of 256 MiB or more",
+  return fail(LRAR_ERR_UNSUPPORTED, "%s: %s = %lld elements is a row stride above 256 MiB",
               fn, what, (long long)ld);
 }
 
