@@ -217,9 +217,11 @@ struct TileGeom {
 // that is not needed loads over an empty span, reading no memory either way, so every item of
 // the ring leaves the same loads in flight and a wait for a stage is a wait for it alone.
 // Measured on MI355X, exact waits pay where each stage carries much vector work (the key read
-// from the row units, KS = 0: wide keys and the full-RMS control, up to a fifth faster), and
-// cost a few percent on the short-key streaming reads, where the other waves already hide the
-// latency; load_stage picks by KS.
+// from the row units, KS = 0: wide keys and the full-RMS control, up to a fifth faster) and on
+// short-key reads of few sources (the two-deep ring: 5-11 % at 2 to 7 sources), and cost a few
+// percent on short-key reads of many sources through the three-deep ring, where the other
+// waves already hide the latency. The read kernel picks per instance (load_stage_as), the
+// backward by KS (load_stage).
 template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
 __device__ __forceinline__ void load_stage_branchy(Stage<IO, VEC, NU, R, KS>& st,
                                                    const IO* __restrict__ base, int64_t ld,
@@ -287,13 +289,22 @@ __device__ __forceinline__ void load_stage_exact(Stage<IO, VEC, NU, R, KS>& st,
   }
 }
 
+template <bool KEYS_ONLY, bool SEP, bool EXACT, typename IO, int VEC, int NU, int R, int KS>
+__device__ __forceinline__ void load_stage_as(Stage<IO, VEC, NU, R, KS>& st,
+                                              const IO* __restrict__ base, int64_t ld,
+                                              const TileGeom& g, const IO* kbase = nullptr,
+                                              int64_t kld = 0, bool live = true) {
+  if constexpr (EXACT) load_stage_exact<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
+  else load_stage_branchy<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
+}
+
+// Exact for keys read from the row units, branchy for spread keys.
 template <bool KEYS_ONLY, bool SEP = false, typename IO, int VEC, int NU, int R, int KS>
 __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
                                            const IO* __restrict__ base, int64_t ld,
                                            const TileGeom& g, const IO* kbase = nullptr,
                                            int64_t kld = 0, bool live = true) {
-  if constexpr (KS == 0) load_stage_exact<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
-  else load_stage_branchy<KEYS_ONLY, SEP>(st, base, ld, g, kbase, kld, live);
+  load_stage_as<KEYS_ONLY, SEP, KS == 0>(st, base, ld, g, kbase, kld, live);
 }
 
 // This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the

@@ -317,7 +317,10 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 
   // Ring of PF + 1 stages: the item PF ahead is loading while the current one is folded in.
   // Loops over the ring are unrolled by PF + 1 so that every stage index is a constant and no
-  // stage is copied (a copy would wait for its loads).
+  // stage is copied (a copy would wait for its loads). Exact loads (see load_stage_exact) for
+  // keys read from the row units and for the two-deep ring; spread keys through the three-deep
+  // ring keep the branchy loads.
+  constexpr bool kExact = KS == 0 || PF < 3;
   Stage<IO, VEC, NU, R, KS> ring[PF + 1];
 
   if constexpr (MODE == kTileTwoPass) {
@@ -329,16 +332,17 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 #pragma unroll
       for (int b = 0; b < PF; ++b) {
         const int ia = clamp_src(b);
-        load_stage<true>(ring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0, b < n);
-        if constexpr (KS == 0) __builtin_amdgcn_sched_barrier(0);  // stages issued in ring order
+        load_stage_as<true, false, kExact>(ring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
+                                           b < n);
+        if constexpr (kExact) __builtin_amdgcn_sched_barrier(0);  // stages issued in ring order
       }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
           const int ia = clamp_src(i + PF);
-          load_stage<true>(ring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
-                           i + PF < n);
+          load_stage_as<true, false, kExact>(ring[(b + PF) % (PF + 1)], src_base(ia),
+                                             p.src.ld[ia], t, kNoKeys, 0, i + PF < n);
           if (i < n) {
             const double z = stage_scores(ring[b], t);
 #pragma unroll
@@ -364,7 +368,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 #pragma unroll
       for (int b = 0; b < PF; ++b) {
         const int ia = clamp_src(b);
-        load_stage<false>(vring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0, b < n);
+        load_stage_as<false, false, true>(vring[b], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
+                                          b < n);
         __builtin_amdgcn_sched_barrier(0);  // stages issued in ring order
       }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
@@ -372,8 +377,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
           const int ia = clamp_src(i + PF);
-          load_stage<false>(vring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t, kNoKeys, 0,
-                            i + PF < n);
+          load_stage_as<false, false, true>(vring[(b + PF) % (PF + 1)], src_base(ia),
+                                            p.src.ld[ia], t, kNoKeys, 0, i + PF < n);
           if (i < n) {
 #pragma unroll
             for (int j = 0; j < R; ++j) fma_row(acc[j], lane_f32(w[j], i), vring[b].t.u[j]);
@@ -491,18 +496,19 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 #pragma unroll
       for (int b = 0; b < PF; ++b) {
         const int ia = clamp_src(b);
-        load_stage<false, kSep>(ring[b], src_base(ia), p.src.ld[ia], t, key_base(ia), key_ld(ia),
-                                b < n);
+        load_stage_as<false, kSep, kExact>(ring[b], src_base(ia), p.src.ld[ia], t, key_base(ia),
+                                           key_ld(ia), b < n);
         // stages issued in ring order, so a wait for the oldest is a wait for it alone
-        if constexpr (KS == 0) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kExact) __builtin_amdgcn_sched_barrier(0);
       }
       for (int i0 = 0; i0 < n; i0 += PF + 1) {
 #pragma unroll
         for (int b = 0; b <= PF; ++b) {
           const int i = i0 + b;
           const int ia = clamp_src(i + PF);
-          load_stage<false, kSep>(ring[(b + PF) % (PF + 1)], src_base(ia), p.src.ld[ia], t,
-                                  key_base(ia), key_ld(ia), i + PF < n);
+          load_stage_as<false, kSep, kExact>(ring[(b + PF) % (PF + 1)], src_base(ia),
+                                             p.src.ld[ia], t, key_base(ia), key_ld(ia),
+                                             i + PF < n);
           if (i < n) fold_source(ring[b], t, i);
         }
       }
