@@ -114,7 +114,7 @@ def gen_queries(torch, nq, r, seed, std=1.0):
 # ---- the headline workload ----------------------------------------------------------------------
 
 FULL = dict(T=8 * 2048, d=1024, r=64, eps=1e-6, n_sources=49, scale=(0.5, 2.0))
-DEEP_MIN_SOURCES = 8  # reads of this many sources or more take the deeper-ring instantiation
+DEEP_MIN_SOURCES = 20  # headline reads of this many sources or more take the deeper ring
 
 
 def fwd_bytes(T, d, n, e):
@@ -423,9 +423,9 @@ def main():
             rows[name] = fn(torch, lrar, ev, args.reps)
             torch.cuda.empty_cache()
     digest = source_digest()
-    # The dominant kernel: the library reads 8 or more sources with its deeper-ring tile
-    # instantiation (three sources in flight), which serves sites n = 8..49 and moves 97 % of
-    # the step's bytes; sites n = 1..7 run the two-deep instantiation.
+    # The dominant kernel: at d = 1024 the library reads 20 or more sources with its deeper-ring
+    # tile instantiation (three sources in flight), which serves sites n = 20..49 and moves 84 %
+    # of the step's bytes; sites n = 2..19 run the two-deep instantiation.
     deep = range(DEEP_MIN_SOURCES, h["S"] + 1)
     bytes_launch = sum(fwd_bytes(h["T"], FULL["d"], n, 2) for n in deep) / len(deep)
     avg_launch_s = sum(h["site_mean_ms"][n - 1] for n in deep) * 1e-3 / len(deep)
@@ -434,7 +434,7 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBPS, 4),
                     traffic=traffic_entry(digest, bytes_launch),
                     kernel="k_read_tile<bf16, 8, 2, 1, 2, true, 2, 3, 1, online> "
-                           "(d=1024, r=64; sites n=8..49)",
+                           "(d=1024, r=64; sites n=20..49)",
                     algorithmic_bytes_per_launch=round(bytes_launch),
                     avg_launch_us=round(avg_launch_s * 1e6, 3),
                     launches_per_step=len(deep))

@@ -555,6 +555,15 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
 // already keeps the vector unit busy), keep the shallower ring.
 constexpr int kDeepPrefetch = 3;
 constexpr int kDeepMinSources = 8;
+// Reads with the key in the row's last columns, spread over the lanes, and two units per lane
+// (d <= 1024 bf16) take the three-deep ring only from 20 sources: below that the two-deep ring
+// with exact waits measured 4-7 % faster (9 and 13 sources), above it 2-5 % slower (25 to 49).
+// The separate-key read keeps the lower threshold (its r = 64 keys measured 6 % slower at 13
+// sources with the two-deep ring).
+constexpr int kDeepMinSourcesNarrow = 20;
+constexpr int deep_min_sources(int nu, int mode) {
+  return nu <= 2 && mode != kTileKeys ? kDeepMinSourcesNarrow : kDeepMinSources;
+}
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, int MODE,
           typename ACC, bool DEEP = false>
@@ -594,7 +603,7 @@ template <typename IO, int VEC, int NU, int KS, bool ROWRED, int WPR, int MODE, 
 hipError_t launch_tile_spread(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr ((MODE == kTileOnline || MODE == kTileKeys || MODE == kTileTwoPass) && NU >= 2 &&
                 NU <= 4) {
-    if (p.n >= kDeepMinSources)
+    if (p.n >= deep_min_sources(NU, MODE))
       return launch_tile_t<IO, VEC, NU, 1, KS, ROWRED, WPR, MODE, ACC, true>(p, kt, s);
   }
   return launch_tile_t<IO, VEC, NU, 1, KS, ROWRED, WPR, MODE, ACC>(p, kt, s);
