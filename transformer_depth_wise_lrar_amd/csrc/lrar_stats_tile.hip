@@ -16,11 +16,10 @@
 //   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
 //     l = sum_i e_si (float64 on the lanes), written once per row;
 //   * value pass: the row is walked in chunks of 64 units; each chunk of every source is loaded
-//     once and folded into four queries' accumulators at a time, with the weights read from
-//     LDS; the accumulators are written straight out (acc = sum_i e_si o_i, not normalised),
-//     each store instruction covering 1 KiB of one accumulator row. The last pass over a chunk
-//     loads the next chunk of each source as soon as it has taken that source's values, so the
-//     loads are in flight while the pass folds and stores.
+//     once, and the accumulators of all the group's queries come from matrix-core products
+//     (weights x values, float32) whose outputs are whole units of the accumulator rows, written
+//     straight out (acc = sum_i e_si o_i, not normalised). The next chunk is loaded right after
+//     the current chunk's stores, so the loads are in flight while the next products run.
 // Every load is issued by every lane whatever the source count and the row's width: a source
 // slot past n reads source 0 and a unit past the row (or before the key) reads the nearest unit
 // inside it, and those values are discarded. With loads under conditions the compiler cannot
@@ -38,8 +37,8 @@ namespace {
 
 constexpr int kStatsBlock = 768;
 constexpr int kStatsWaves = kStatsBlock / kWave;
-constexpr int kValQ = 4;  // queries folded per pass over a chunk's source units
-static_assert(kStatsMaxQ % kValQ == 0, "whole passes");
+static_assert(kStatsMaxQ <= 16 && kStatsMaxSrc % 4 == 0,
+              "a query group fills at most the 16 rows of a matrix product, sources come in fours");
 // LDS a workgroup holds besides the staged queries (z_lds, w_lds)
 constexpr size_t kStatsStaticLds =
     kStatsWaves * kStatsMaxQ * kStatsMaxSrc * (sizeof(double) + sizeof(float));
@@ -83,8 +82,6 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
     sp[i] = static_cast<const IO*>(i < n ? p.src.ptr[i] : p.src.ptr[0]);
     sld[i] = i < n ? p.src.ld[i] : p.src.ld[0];
   }
-  constexpr bool kSplit = std::is_same<IO, bf16_bits>::value && std::is_same<ACC, float>::value;
-  const int ccol = kWave * VEC;  // columns per chunk
 
   for (int64_t row = wave; row < p.T; row += nwaves) {
     // ---- score pass: z_si of every (query, source) pair into z_lds. Rounds of kStatsKeySlots
@@ -181,105 +178,121 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
       }
     }
 
-    // ---- value pass: chunks of 64 units, every source's part of a chunk loaded together. The
-    // weights go through LDS (w_lds[wave][source][query]): a few wide reads bring a source's
-    // weights for the queries of a pass to every lane, in place of one cross-lane read per
-    // weight. With bf16 sources and float32 accumulators a lane takes two runs of 4 columns
-    // (4 lane and 256 + 4 lane of the chunk) instead of one run of 8, so each 16-byte store of
-    // the accumulators lands next to its neighbour lanes' and a store covers 1 KiB.
+    // ---- value pass on the matrix cores. Per row the accumulators are a small dense product,
+    // acc[s][c] = sum_i w_si o_i[c] (queries x sources times sources x columns), which
+    // v_mfma_f32_16x16x4f32 takes as A = w (16 queries x 4 sources), B = o (4 sources x 16
+    // columns) and D = acc (16 x 16), all float32. Lane l supplies A[l % 16][l / 16] and
+    // B[l / 16][l % 16] and receives D[4 (l / 16) + j][l % 16], j = 0..3. A lane that loads
+    // the unit of source 4 kb + l / 16 at unit 16 b + l % 16 of a chunk, and feeds its element e
+    // to the e-th product of block b, so holds after the VEC products the VEC columns of that
+    // unit for four queries: one whole unit of each, stored as such.
+    // Sources past n weigh zero (and read source 0).
 #pragma unroll
     for (int s = 0; s < kStatsMaxQ; ++s)
       if (s < nqg && lane < n) w_lds[wv][lane][s] = ew[s];
     __builtin_amdgcn_wave_barrier();
-    const auto load_src = [&](const IO* rp, int c, Unit<IO, VEC>& dst) {
-      if constexpr (kSplit) {
-        int col0 = c * ccol + 4 * lane;
-        int col1 = col0 + ccol / 2;
-        col0 = col0 < p.d ? col0 : p.d - 4;
-        col1 = col1 < p.d ? col1 : p.d - 4;
-        const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col0));
-        const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + col1));
-        dst.raw = u32x4{lo.x, lo.y, hi.x, hi.y};
-      } else {
-        int u = lane + kWave * c;
-        u = u < nur ? u : nur - 1;
-        dst.load(rp + u * VEC);
+    constexpr int kKb = kStatsMaxSrc / 4;  // blocks of four sources
+    constexpr int kBlocks = kWave / 16;    // blocks of 16 units in a chunk of 64
+    const int ql = lane & 15;              // A row (query), B and D column
+    const int kq = lane >> 4;              // A column and B row (source in the block), D row / 4
+    const int qa = ql < nqg ? ql : nqg - 1;  // rows past the group repeat the last query
+    float aw[kKb];
+    const IO* vrow[kKb];
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) {
+      const int src = 4 * kb + kq;
+      aw[kb] = src < n ? w_lds[wv][src][qa] : 0.f;
+      const IO* b0 = sp[4 * kb] + row * sld[4 * kb];
+      const IO* b1 = sp[4 * kb + 1] + row * sld[4 * kb + 1];
+      const IO* b2 = sp[4 * kb + 2] + row * sld[4 * kb + 2];
+      const IO* b3 = sp[4 * kb + 3] + row * sld[4 * kb + 3];
+      vrow[kb] = kq == 0 ? b0 : (kq == 1 ? b1 : (kq == 2 ? b2 : b3));
+    }
+    const bool two_blocks = n > 4;
+    // bf16 sources with float32 accumulators: a lane takes two runs of 4 columns of a block of
+    // 128 (4 l and 64 + 4 l) instead of one unit of 8, so that each 16-byte store of the
+    // accumulators lands next to its neighbour lanes' (256 contiguous bytes per 16 lanes).
+    constexpr bool kSplit = std::is_same<IO, bf16_bits>::value && std::is_same<ACC, float>::value;
+    constexpr int kBlockCols = 16 * VEC;
+    Unit<IO, VEC> buf[kBlocks][kKb];
+    const auto load_chunk = [&](int c) {
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) {
+        if constexpr (kSplit) {
+          int col0 = (kBlocks * c + b) * kBlockCols + 4 * ql;
+          int col1 = col0 + kBlockCols / 2;
+          col0 = col0 < p.d ? col0 : p.d - 4;
+          col1 = col1 < p.d ? col1 : p.d - 4;
+#pragma unroll
+          for (int kb = 0; kb < kKb; ++kb) {
+            const u32x2 lo =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vrow[kb] + col0));
+            const u32x2 hi =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vrow[kb] + col1));
+            buf[b][kb].raw = u32x4{lo.x, lo.y, hi.x, hi.y};
+            // issued in order, so a wait for one unit is a wait for it and the loads before it
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          int u = kWave * c + 16 * b + ql;
+          u = u < nur ? u : nur - 1;
+#pragma unroll
+          for (int kb = 0; kb < kKb; ++kb) {
+            buf[b][kb].load(vrow[kb] + u * VEC);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
     };
-    Unit<IO, VEC> buf[kStatsMaxSrc];
-    // issued in source order, as the reloads below are, so a wait for one source's unit is
-    // a wait for it and the loads before it only
-#pragma unroll
-    for (int i = 0; i < kStatsMaxSrc; ++i) {
-      load_src(sp[i] + row * sld[i], 0, buf[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    ACC* const acc_row = static_cast<ACC*>(p.acc) + row * p.acc_ld;
+    load_chunk(0);
     for (int c = 0; c < nslot; ++c) {
-      const int u = lane + kWave * c;
-      const int cn = c + 1 < nslot ? c + 1 : c;  // the last chunk reloads itself
-      // passes in reverse order, so the one that reloads (queries 0..3, always present) is last
 #pragma unroll
-      for (int s0 = kStatsMaxQ - kValQ; s0 >= 0; s0 -= kValQ) {
-        if (s0 == 0 || s0 < nqg) {
-          float a[kValQ][VEC];
+      for (int b = 0; b < kBlocks; ++b) {
+        f32x4 dacc[VEC];
 #pragma unroll
-          for (int j = 0; j < kValQ; ++j)
+        for (int e = 0; e < VEC; ++e) dacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) a[j][e] = 0.f;
-#pragma unroll
-          for (int i = 0; i < kStatsMaxSrc; ++i) {
+        for (int kb = 0; kb < kKb; ++kb) {
+          if (kb == 0 || two_blocks) {
             float x[VEC];
-            buf[i].get(x);
-            if (i < n) {
-              float w[kValQ];
-              const float* wp = &w_lds[wv][i][s0];
+            buf[b][kb].get(x);
 #pragma unroll
-              for (int j = 0; j < kValQ; ++j) w[j] = wp[j];
-#pragma unroll
-              for (int j = 0; j < kValQ; ++j)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) a[j][e] = fmaf(w[j], x[e], a[j][e]);
-            }
+            for (int e = 0; e < VEC; ++e)
+              dacc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[kb], x[e], dacc[e], 0, 0, 0);
           }
-          int64_t off = static_cast<int64_t>(q0 + s0) * p.acc_qstride + row * p.acc_ld;
-          asm volatile("" : "+v"(off));
-          // A lane past the row's end loaded the row's last unit in place of its own, so it
-          // holds that unit's sums bit for bit and stores them there too: every lane stores,
-          // with no branch, and the duplicate writes carry the same bytes.
-          if constexpr (kSplit) {
-            int col0 = c * ccol + 4 * lane;
-            int col1 = col0 + ccol / 2;
-            col0 = col0 < p.d ? col0 : p.d - 4;
-            col1 = col1 < p.d ? col1 : p.d - 4;
-            float* d0 = static_cast<float*>(p.acc) + off;
+        }
+        // Lanes whose query row lies past the group store nothing. These stores come before the
+        // next chunk's loads, so skipping some of them leaves the waits for those loads exact.
+        // A lane past the row's end loaded the row's last columns and stores their sums there
+        // again: the same bytes as the owning lane.
 #pragma unroll
-            for (int j = 0; j < kValQ; ++j) {
-              if (s0 + j < nqg) {
-                float* dj = d0 + j * p.acc_qstride;
-                out_store(f32x4{a[j][0], a[j][1], a[j][2], a[j][3]},
-                          reinterpret_cast<f32x4*>(dj + col0));
-                out_store(f32x4{a[j][4], a[j][5], a[j][6], a[j][7]},
-                          reinterpret_cast<f32x4*>(dj + col1));
-              }
-            }
-          } else {
-            const int us = u < nur ? u : nur - 1;
-            ACC* d0 = static_cast<ACC*>(p.acc) + off + us * VEC;
+        for (int j = 0; j < 4; ++j) {
+          const int s = 4 * kq + j;
+          float v[VEC];
 #pragma unroll
-            for (int j = 0; j < kValQ; ++j)
-              if (s0 + j < nqg) store_acc<ACC, VEC>(d0 + j * p.acc_qstride, a[j]);
-          }
-          if (s0 == 0) {
-            // the next chunk, after this chunk's last stores: a wait for one source's unit is
-            // then a wait for it and the loads and stores issued before it
-#pragma unroll
-            for (int i = 0; i < kStatsMaxSrc; ++i) {
-              load_src(sp[i] + row * sld[i], cn, buf[i]);
-              __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < VEC; ++e) v[e] = dacc[e][j];
+          if (s < nqg) {
+            if constexpr (kSplit) {
+              int col0 = (kBlocks * c + b) * kBlockCols + 4 * ql;
+              int col1 = col0 + kBlockCols / 2;
+              col0 = col0 < p.d ? col0 : p.d - 4;
+              col1 = col1 < p.d ? col1 : p.d - 4;
+              float* dq = reinterpret_cast<float*>(acc_row) +
+                          static_cast<int64_t>(q0 + s) * p.acc_qstride;
+              out_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dq + col0));
+              out_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(dq + col1));
+            } else {
+              int u = kWave * c + 16 * b + ql;
+              u = u < nur ? u : nur - 1;
+              const int64_t off = static_cast<int64_t>(q0 + s) * p.acc_qstride + u * VEC;
+              store_acc<ACC, VEC>(acc_row + off, v);
             }
           }
         }
       }
+      // the next chunk, after this chunk's stores (the last chunk reloads itself)
+      load_chunk(c + 1 < nslot ? c + 1 : c);
     }
     // the next row's weights overwrite w_lds only after every lane has read this row's
     __builtin_amdgcn_wave_barrier();
