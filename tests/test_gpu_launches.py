@@ -1,0 +1,78 @@
+"""Reads of many rows: the one-pass spread-key reads are cut into several launches over
+consecutive row ranges (at most a fixed number of tiles per row group each); reads with the
+key in the row units and merges run as one launch over the same rows.
+
+These tests fill the outputs with NaN first and then check that every row was written, that
+every row's weights sum to 1, and that rows on both sides of the launch boundaries (and the
+ragged last row) match the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import transformer_depth_wise_lrar_amd as lrar
+from gpu_util import f64, needs_gpu, sample_rows, say
+from transformer_depth_wise_lrar_amd import synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def boundary_rows(T, parts=12):
+    """Rows around every 1/parts of T, the ends, and random rows (sorted, distinct)."""
+    rows = set(sample_rows(T, 16, seed=T))
+    for k in range(1, parts):
+        c = T * k // parts
+        rows.update(x for x in range(c - 2, c + 2) if 0 <= x < T)
+    rows.update((0, 1, T - 2, T - 1))
+    return sorted(rows)
+
+
+def rows64(t, rows):
+    idx = torch.as_tensor(rows, device=t.device)
+    return f64(t.index_select(0, idx))
+
+
+@pytest.mark.parametrize("d,r,n,T", [
+    (2048, 64, 9, 65536 + 37),     # cut: one wave per row, spread key, three-deep ring
+    (2048, 64, 1, 65536 + 37),     # cut: one source, the two-stage tile alternation
+    (7168, 64, 3, 32768 + 5),      # cut: four waves per row
+    (2048, 512, 3, 65536 + 37),    # one launch: key from the row units
+    (7168, 1792, 3, 32768 + 5),    # one launch: the row's four waves exchange key sums
+])
+def test_every_row_written(d, r, n, T):
+    eps = 1e-6
+    srcs = synth.values(n, T, d, "bf16", seed=900 + n, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=901 + r, device="cuda")[0].contiguous()
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    alpha = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"[launches] read T={T} d={d} r={r} n={n}")
+    lrar.lrar_forward(srcs, q, r, eps, out=out, alpha=alpha)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(out).any()), "rows left unwritten"
+    sums = alpha.double().sum(dim=1)
+    assert float((sums - 1.0).abs().max()) <= 1e-6 * n, "weights of some rows do not sum to 1"
+    rows = boundary_rows(T)
+    s64 = [rows64(s, rows) for s in srcs]
+    h_ref, a_ref = oracle.forward(s64, f64(q), r, eps)
+    where = f"T={T} d={d} r={r} n={n}"
+    parity.assert_weights(rows64(alpha, rows), a_ref, where + " alpha")
+    parity.assert_read(rows64(out, rows), h_ref, a_ref, s64, "bf16", where + " h")
+
+
+def test_merge_every_row_written():
+    """Phase 2 over many rows: the merge of (m, l, acc) with one extra source."""
+    T, d, r, eps = 65536 + 37, 2048, 512, 1e-6
+    srcs = synth.values(4, T, d, "bf16", seed=950, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=951, device="cuda")[0].contiguous()
+    say(f"[launches] merge T={T} d={d} r={r}")
+    m, l, acc = lrar.lrar_forward_stats(srcs[:3], q[None, :].contiguous(), r, eps)
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lrar.lrar_merge(m[0], l[0], acc[0], srcs[3:], q, r, eps, out=out)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(out).any()), "rows left unwritten"
+    rows = boundary_rows(T)
+    s64 = [rows64(s, rows) for s in srcs]
+    h_ref, a_ref = oracle.forward(s64, f64(q), r, eps)
+    parity.assert_read(rows64(out, rows), h_ref, a_ref, s64, "bf16", f"merge T={T}")

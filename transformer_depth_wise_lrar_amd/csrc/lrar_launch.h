@@ -36,6 +36,9 @@ struct ReadParams {
   int64_t b_prev_ld;
   void* b_out;
   int64_t b_out_ld;
+  // register-tile read only, set by its launcher: the row tiles [tile_begin, tile_end) of one
+  // launch
+  int64_t tile_begin, tile_end;
 };
 
 // A spread key piece of ks elements per lane, reduced row-locally (rowred) or over the lanes.
