@@ -15,18 +15,20 @@
 //     the current round is folded;
 //   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
 //     l = sum_i e_si (float64 on the lanes), written once per row;
-//   * value pass: the row is walked in chunks of 64 units; each chunk of every source is loaded
-//     once, and the accumulators of all the group's queries come from matrix-core products
-//     (weights x values, float32) whose outputs are whole units of the accumulator rows, written
-//     straight out (acc = sum_i e_si o_i, not normalised). The next chunk is loaded right after
-//     the current chunk's stores, so the loads are in flight while the next products run.
+//   * value pass: the row is walked in chunks of 64 units, from the first chunk that holds key
+//     units; each chunk of every source is loaded once, and the accumulators of all the
+//     group's queries come from matrix-core products (weights x values, float32) whose outputs
+//     are whole units of the accumulator rows, written straight out (acc = sum_i e_si o_i, not
+//     normalised). The next chunk is loaded right after the current chunk's stores, so the
+//     loads are in flight while the next products run.
 // Every load is issued by every lane whatever the source count and the row's width: a source
 // slot past n reads source 0 and a unit past the row (or before the key) reads the nearest unit
 // inside it, and those values are discarded. With loads under conditions the compiler cannot
 // count the loads in flight and waits for all of them, and for every earlier store, before it
 // uses any one.
-// Each cached source row is read from HBM once per query group (its key again from L2), and
-// every accumulator element is written once.
+// Each cached source row is read from HBM once per query group (its key again, from L2 when
+// the key chunks are still there: the value pass visits them first), and every accumulator
+// element is written once.
 
 #include "lrar_device.h"
 #include "lrar_launch.h"
@@ -245,8 +247,13 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
       }
     };
     ACC* const acc_row = static_cast<ACC*>(p.acc) + row * p.acc_ld;
-    load_chunk(0);
-    for (int c = 0; c < nslot; ++c) {
+    // The chunks are walked from the first one that holds key units (k_lo) to the row's end,
+    // then from 0: the key units, just read by the score pass through the cache, are read again
+    // while still there. Each chunk's sums depend on that chunk alone, so the order changes no
+    // result.
+    load_chunk(k_lo);
+    for (int k = 0; k < nslot; ++k) {
+      const int c = k_lo + k < nslot ? k_lo + k : k_lo + k - nslot;
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
         f32x4 dacc[VEC];
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
         }
       }
       // the next chunk, after this chunk's stores (the last chunk reloads itself)
-      load_chunk(c + 1 < nslot ? c + 1 : c);
+      load_chunk(k + 1 < nslot ? (c + 1 < nslot ? c + 1 : 0) : c);
     }
     // the next row's weights overwrite w_lds only after every lane has read this row's
     __builtin_amdgcn_wave_barrier();
