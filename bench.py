@@ -190,9 +190,14 @@ def time_calls(torch, ev, fn, reps, warm=2):
     return t
 
 
-def row_entry(ms, nbytes):
+def row_entry(ms, nbytes, tokens=None):
+    """Median time, effective GB/s and fraction of peak of a timed call; with tokens, also
+    the call's tokens/s (tokens = the token rows one call processes, for Phase 1 times its
+    site queries)."""
     g = nbytes / (ms * 1e-3) / 1e9
     e = dict(ms=round(float(ms), 5), GBps=round(g, 1), frac=round(g / HBM_PEAK_GBPS, 4))
+    if tokens is not None:
+        e["tokens_per_s"] = round(tokens / (ms * 1e-3), 1)
     if getattr(ms, "cv", None) is not None:
         e["cv"] = round(ms.cv, 4)
     return e
@@ -211,7 +216,7 @@ def rows_block_routing(torch, lrar, ev, reps):
             for var in ("two_pass", "online"):
                 ms = time_calls(torch, ev, lrar.lrar_forward(
                     srcs[:n], q, r, 1e-6, out=out, variant=var, prepare=True), reps)
-                res[f"r{r}_n{n}_{var}"] = row_entry(ms, fwd_bytes(T, d, n, 2))
+                res[f"r{r}_n{n}_{var}"] = row_entry(ms, fwd_bytes(T, d, n, 2), T)
     del srcs, out
     return res
 
@@ -230,7 +235,7 @@ def rows_production(torch, lrar, ev, reps):
         for var in ("two_pass", "online"):
             ms = time_calls(torch, ev, lrar.lrar_forward(
                 srcs, q, r, 1e-6, out=out, variant=var, prepare=True), reps)
-            res[f"single_pass_r{r}_n9_{var}"] = row_entry(ms, fwd_bytes(T, d, 9, 2))
+            res[f"single_pass_r{r}_n9_{var}"] = row_entry(ms, fwd_bytes(T, d, 9, 2), T)
     r = 1792
     qs = gen_queries(torch, nq, r, seed=3100)
     for acc_name, acc_dt, ae in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
@@ -240,18 +245,18 @@ def rows_production(torch, lrar, ev, reps):
         ms1 = time_calls(torch, ev, lrar.lrar_forward_stats(
             srcs[:8], qs, r, 1e-6, m=m, l=l, acc=acc, prepare=True), reps)
         b1 = 2 * 8 * d * T + nq * (ae * d + 8) * T
-        res[f"phase1_r{r}_ninter8_q{nq}_acc{acc_name}"] = row_entry(ms1, b1)
+        res[f"phase1_r{r}_ninter8_q{nq}_acc{acc_name}"] = row_entry(ms1, b1, T * nq)
         ms2 = time_calls(torch, ev, lrar.lrar_merge(
             m[0], l[0], acc[0], srcs[8:9], qs[0], r, 1e-6, out=out, prepare=True), reps)
         b2 = (ae * d + 8 + 2 * d + 2 * d) * T
-        res[f"phase2_r{r}_acc{acc_name}"] = row_entry(ms2, b2)
+        res[f"phase2_r{r}_acc{acc_name}"] = row_entry(ms2, b2, T)
         # the same site with the partial-sum update fused in: b' = b + o is written and merged
         bnew = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
         ms3 = time_calls(torch, ev, lrar.lrar_merge_accumulate(
             m[0], l[0], acc[0], srcs[8], srcs[7], qs[0], r, 1e-6, out=out, b_out=bnew,
             prepare=True), reps)
         b3 = (ae * d + 8 + 2 * d + 2 * d + 2 * d + 2 * d) * T
-        res[f"phase2_fused_update_r{r}_acc{acc_name}"] = row_entry(ms3, b3)
+        res[f"phase2_fused_update_r{r}_acc{acc_name}"] = row_entry(ms3, b3, T)
         del m, l, acc, bnew
     del srcs, out
     return res
@@ -273,7 +278,7 @@ def rows_backward(torch, lrar, ev, reps):
     ms = time_calls(torch, ev, lrar.lrar_backward(
         srcs, q, dout, r, 1e-6, dsrc=dsrc, dq=dq, workspace=ws, prepare=True), reps)
     nbytes = (2 * n * d + 4 * d + 4 * n * d) * T + 4 * r
-    res = {f"backward_r{r}_n{n}": row_entry(ms, nbytes)}
+    res = {f"backward_r{r}_n{n}": row_entry(ms, nbytes, T)}
     del dsrc
     # bf16 gradients (dout and dsrc bf16), as the pages' own kernel writes them
     dout16 = dout.to(torch.bfloat16)
@@ -281,7 +286,7 @@ def rows_backward(torch, lrar, ev, reps):
     ms16 = time_calls(torch, ev, lrar.lrar_backward_grad(
         srcs, q, dout16, r, 1e-6, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True), reps)
     res[f"backward_bf16_grads_r{r}_n{n}"] = row_entry(
-        ms16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r)
+        ms16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r, T)
     del srcs, dsrc16, dout, dout16
     return res
 
@@ -299,14 +304,14 @@ def rows_read_variants(torch, lrar, ev, reps):
     for n in (13, 49):
         ms = time_calls(torch, ev, lrar.lrar_forward_fullrms(
             srcs[:n], q, r, 1e-6, out=out, prepare=True), reps)
-        res[f"fullrms_r{r}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2))
+        res[f"fullrms_r{r}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2), T)
     for rk in (32, 64):
         keys = gen_sources(torch, 49, T, rk, (0.5, 2.0), seed=5100 + rk, dtype=torch.bfloat16)
         qk = gen_queries(torch, 1, rk, seed=5002 + rk)[0]
         for n in (13, 49):
             ms = time_calls(torch, ev, lrar.lrar_forward_keys(
                 srcs[:n], keys[:n], qk, rk, 1e-6, out=out, prepare=True), reps)
-            res[f"keys_r{rk}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2) + 2 * n * rk * T)
+            res[f"keys_r{rk}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2) + 2 * n * rk * T, T)
         del keys
     del srcs, out
     return res
