@@ -76,3 +76,21 @@ def test_merge_every_row_written():
     s64 = [rows64(s, rows) for s in srcs]
     h_ref, a_ref = oracle.forward(s64, f64(q), r, eps)
     parity.assert_read(rows64(out, rows), h_ref, a_ref, s64, "bf16", f"merge T={T}")
+
+
+@pytest.mark.parametrize("d,r,n,T", [(2048, 64, 9, 65536 + 37), (7168, 64, 3, 32768 + 5)])
+def test_cut_read_matches_uncut_slices(d, r, n, T):
+    """Each row's result depends on that row alone: rows of a read cut into several launches
+    are bitwise equal to the same rows read on their own (a slice short enough for one
+    launch), at the launch boundaries and at the ragged end."""
+    eps = 1e-6
+    srcs = synth.values(n, T, d, "bf16", seed=970 + n, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=971, device="cuda")[0].contiguous()
+    say(f"[launches] cut vs uncut T={T} d={d} r={r} n={n}")
+    out, alpha = lrar.lrar_forward(srcs, q, r, eps, alpha=True)
+    for a in (0, T // 4 - 3, T // 2 - 5, T - 700):
+        b = min(T, a + 640)
+        o2, a2 = lrar.lrar_forward([s[a:b] for s in srcs], q, r, eps, alpha=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[a:b], o2), f"rows {a}..{b - 1}: h differs from the uncut read"
+        assert torch.equal(alpha[a:b], a2), f"rows {a}..{b - 1}: weights differ"

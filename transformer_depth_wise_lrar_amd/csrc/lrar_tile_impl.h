@@ -571,8 +571,8 @@ constexpr int deep_min_sources(int nu, int mode) {
 // drift apart, the window of rows they read together widens, and HBM serves it more slowly:
 // at 64 tiles per group such reads measured 4-7 % slower than the same reads cut into
 // launches of 16 tiles per group (d = 1024 to 7168, 9 sources). Reads with the key taken from
-// the row units, the two-pass read and the merges measured 4-10 % slower when cut, so they run
-// as one launch.
+// the row units, the two-pass read and the merges measured 2-10 % slower cut at 12 tiles per
+// group, and reads with the key in the row units -3 to +2 % at 16, so they run as one launch.
 constexpr int64_t kMaxTilesPerGroup = 16;
 constexpr bool cut_into_launches(int mode, int ks) {
   return ks > 0 && (mode == kTileOnline || mode == kTileKeys);
