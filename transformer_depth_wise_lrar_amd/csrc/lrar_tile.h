@@ -316,6 +316,10 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
                                                   double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
+  // A key that starts on a unit boundary fills its units: no column of them needs a mask (the
+  // same sums, without a select per element). Otherwise the first key unit straddles the key's
+  // first column and the columns before it are masked out.
+  const bool straddle = g.c0 % VEC != 0;
 #pragma unroll
   for (int k = NU - TU; k < NU; ++k) {
     const int u = g.unit(k);
@@ -324,12 +328,21 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
       row[k].get(x);
       typename QS::value_type qv[VEC];
       qs.template get<VEC>(u - g.ub, qv);
+      if (!straddle) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int col = u * VEC + e;
-        const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
-        dot = fma(static_cast<double>(qv[e]), kv, dot);
-        ss = fma(kv, kv, ss);
+        for (int e = 0; e < VEC; ++e) {
+          const double kv = static_cast<double>(x[e]);
+          dot = fma(static_cast<double>(qv[e]), kv, dot);
+          ss = fma(kv, kv, ss);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int col = u * VEC + e;
+          const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
+          dot = fma(static_cast<double>(qv[e]), kv, dot);
+          ss = fma(kv, kv, ss);
+        }
       }
     }
   }
@@ -343,6 +356,7 @@ __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
                                                  double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
+  const bool straddle = g.c0 % VEC != 0;  // as in key_partial_units
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
     const int u = g.unit(k);
@@ -357,11 +371,17 @@ __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
       if (u >= g.ub) {
         typename QS::value_type qv[VEC];
         qs.template get<VEC>(u - g.ub, qv);
+        if (!straddle) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int col = u * VEC + e;
-          const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
-          dot = fma(static_cast<double>(qv[e]), kv, dot);
+          for (int e = 0; e < VEC; ++e)
+            dot = fma(static_cast<double>(qv[e]), static_cast<double>(x[e]), dot);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const int col = u * VEC + e;
+            const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
+            dot = fma(static_cast<double>(qv[e]), kv, dot);
+          }
         }
       }
     }
