@@ -310,16 +310,12 @@ __device__ __forceinline__ void load_stage(Stage<IO, VEC, NU, R, KS>& st,
 // This lane's share of q . k and k . k for one row from its key units (KS = 0). Only the
 // last TU unit slots can hold key columns (the host picks TU so that the key starts in slot
 // NU - TU or later).
-template <int TU, typename IO, int VEC, int NU, typename QS>
+template <int TU, bool KA = false, typename IO, int VEC, int NU, typename QS>
 __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU],
                                                   const QS& qs, const TileGeom& g,
                                                   double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
-  // A key that starts on a unit boundary fills its units: no column of them needs a mask (the
-  // same sums, without a select per element). Otherwise the first key unit straddles the key's
-  // first column and the columns before it are masked out.
-  const bool straddle = g.c0 % VEC != 0;
 #pragma unroll
   for (int k = NU - TU; k < NU; ++k) {
     const int u = g.unit(k);
@@ -328,21 +324,13 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
       row[k].get(x);
       typename QS::value_type qv[VEC];
       qs.template get<VEC>(u - g.ub, qv);
-      if (!straddle) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const double kv = static_cast<double>(x[e]);
-          dot = fma(static_cast<double>(qv[e]), kv, dot);
-          ss = fma(kv, kv, ss);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int col = u * VEC + e;
-          const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
-          dot = fma(static_cast<double>(qv[e]), kv, dot);
-          ss = fma(kv, kv, ss);
-        }
+      for (int e = 0; e < VEC; ++e) {
+        // KA: the key starts on a unit boundary, so every column of a key unit is a key column
+        const double kv =
+            KA || u * VEC + e >= g.c0 ? static_cast<double>(x[e]) : 0.0;
+        dot = fma(static_cast<double>(qv[e]), kv, dot);
+        ss = fma(kv, kv, ss);
       }
     }
   }
@@ -350,13 +338,12 @@ __device__ __forceinline__ void key_partial_units(const Unit<IO, VEC> (&row)[NU]
 
 // This lane's share of q . k over the key columns and of o . o over the whole row, for the
 // full-width-RMS control: every unit slot of the row counts toward the square sum.
-template <typename IO, int VEC, int NU, typename QS>
+template <bool KA = false, typename IO, int VEC, int NU, typename QS>
 __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
                                                  const QS& qs, const TileGeom& g,
                                                  double& dot, double& ss) {
   dot = 0.0;
   ss = 0.0;
-  const bool straddle = g.c0 % VEC != 0;  // as in key_partial_units
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
     const int u = g.unit(k);
@@ -371,17 +358,10 @@ __device__ __forceinline__ void row_partial_full(const Unit<IO, VEC> (&row)[NU],
       if (u >= g.ub) {
         typename QS::value_type qv[VEC];
         qs.template get<VEC>(u - g.ub, qv);
-        if (!straddle) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            dot = fma(static_cast<double>(qv[e]), static_cast<double>(x[e]), dot);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const int col = u * VEC + e;
-            const double kv = col >= g.c0 ? static_cast<double>(x[e]) : 0.0;
-            dot = fma(static_cast<double>(qv[e]), kv, dot);
-          }
+        for (int e = 0; e < VEC; ++e) {
+          const double kv = KA || u * VEC + e >= g.c0 ? static_cast<double>(x[e]) : 0.0;
+          dot = fma(static_cast<double>(qv[e]), kv, dot);
         }
       }
     }

@@ -51,7 +51,7 @@ namespace lrar {
 
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int R, int PF, int WPR,
-          int MODE, typename ACC>
+          int MODE, typename ACC, bool KA>
 __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MODE> keys) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   extern __shared__ __attribute__((aligned(16))) float q_lds[];
@@ -248,9 +248,9 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       if constexpr (KS > 0)
         key_partial_spread<IO, KS>(st.kp[j], qs, red[2 * j], red[2 * j + 1]);
       else if constexpr (MODE == kTileFullRms)
-        row_partial_full(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
+        row_partial_full<KA>(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
       else
-        key_partial_units<TU>(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
+        key_partial_units<TU, KA>(st.t.u[j], qst, t, red[2 * j], red[2 * j + 1]);
     }
     if constexpr (KS > 0 && ROWRED && R <= 2) {
       // the spread key sits in lanes 0..31 of every wave of the row
@@ -579,11 +579,11 @@ constexpr bool cut_into_launches(int mode, int ks) {
 }
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, int MODE,
-          typename ACC, bool DEEP = false>
+          typename ACC, bool DEEP = false, bool KA = false>
 hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
   constexpr int PF = DEEP ? kDeepPrefetch : tile_prefetch(NU);
-  auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC>;
+  auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC, KA>;
   const int ub = (p.d - p.r) / VEC;
   const int nur = (p.d + VEC - 1) / VEC;
   const size_t lds = KS > 0 ? 0 : static_cast<size_t>(nur - ub) * VEC * sizeof(double);
@@ -637,6 +637,22 @@ hipError_t launch_tile_spread(const ReadParams& p, const KeyTable<MODE>& kt, hip
   return launch_tile_t<IO, VEC, NU, 1, KS, ROWRED, WPR, MODE, ACC>(p, kt, s);
 }
 
+// A read with the key in the row units (KS = 0). A key that starts on a unit boundary (always,
+// at one element per unit) fills every unit it touches, and takes the instantiation whose key
+// sums carry no per-column mask (KA); only a key whose first unit straddles its first column
+// keeps the masked sums. The masked and unmasked sums are the same numbers in the same order.
+template <typename IO, int VEC, int NU, int TU, int WPR, int MODE, typename ACC,
+          bool DEEP = false>
+hipError_t launch_tile_units(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
+  if constexpr (VEC == 1) {
+    return launch_tile_t<IO, VEC, NU, TU, 0, false, WPR, MODE, ACC, DEEP, true>(p, kt, s);
+  } else {
+    if ((p.d - p.r) % VEC == 0)
+      return launch_tile_t<IO, VEC, NU, TU, 0, false, WPR, MODE, ACC, DEEP, true>(p, kt, s);
+    return launch_tile_t<IO, VEC, NU, TU, 0, false, WPR, MODE, ACC, DEEP, false>(p, kt, s);
+  }
+}
+
 // Key path. Spread pieces of KS elements when the key is short: preferably KS = r / 32 rounded
 // up to a power of two, so the key fits lanes 0..31 (row-local sums), else 1 or 2 elements over
 // up to 64 lanes; a piece size must divide r and keep the loads aligned. Otherwise the row
@@ -648,16 +664,16 @@ hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStr
   if constexpr (MODE == kTileFullRms) {
     if constexpr (NU >= 2 && NU <= 4) {
       if (p.n >= kDeepMinSources)
-        return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC, true>(p, kt, s);
+        return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC, true>(p, kt, s);
     }
-    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
+    return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC>(p, kt, s);
   } else if constexpr (MODE == kTileMergeAcc) {
     const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
     if constexpr (NU > 1) {
       if (first_key_chunk / WPR >= NU - 1)
-        return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, kt, s);
+        return launch_tile_units<IO, VEC, NU, 1, WPR, MODE, ACC>(p, kt, s);
     }
-    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
+    return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC>(p, kt, s);
   } else if constexpr (MODE == kTileKeys) {
     switch (p.key_piece) {
       case key_piece_code(1, true):
@@ -703,9 +719,9 @@ hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStr
     const int first_key_chunk = (c0 / VEC) / kWave;
     if constexpr (NU > 1) {
       if (first_key_chunk / WPR >= NU - 1)
-        return launch_tile_t<IO, VEC, NU, 1, 0, false, WPR, MODE, ACC>(p, kt, s);
+        return launch_tile_units<IO, VEC, NU, 1, WPR, MODE, ACC>(p, kt, s);
     }
-    return launch_tile_t<IO, VEC, NU, NU, 0, false, WPR, MODE, ACC>(p, kt, s);
+    return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC>(p, kt, s);
   }
 }
 
