@@ -57,10 +57,11 @@ def test_merge_accumulate_against_oracle(io, acc_dtype, with_b, in_place):
     _case(1024, 64, io, acc_dtype, with_b, in_place, seed=700)
 
 
-@pytest.mark.parametrize("d,r", [(64, 16), (513, 64), (2048, 16), (4096, 1024), (7168, 1792),
-                                 (7168, 7168), (16384, 64)])
+@pytest.mark.parametrize("d,r", [(64, 16), (513, 64), (2048, 16), (2048, 509), (4096, 1024),
+                                 (7168, 1792), (7168, 7168), (16384, 64)])
 def test_merge_accumulate_shapes(d, r):
-    """One wave per row and four, the element path (d = 513), key widths up to r = d."""
+    """One wave per row and four, the element path (d = 513), key widths up to r = d, a key
+    whose first unit also holds non-key columns (r = 509)."""
     _case(d, r, "bf16", torch.float32, True, False, seed=710 + d)
 
 

@@ -106,7 +106,7 @@ def test_merge_against_oracle(n_inter, n_extra, io, acc_dtype):
     _merge_case(n_inter, n_extra, 1024, 64, io, acc_dtype, seed=110 + n_inter)
 
 
-@pytest.mark.parametrize("d,r", [(513, 64), (7168, 7168), (2048, 16)])
+@pytest.mark.parametrize("d,r", [(513, 64), (7168, 7168), (2048, 16), (2048, 509)])
 def test_merge_shapes(d, r):
     _merge_case(4, 1, d, r, "bf16", torch.float32, seed=120)
 

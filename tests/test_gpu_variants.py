@@ -68,11 +68,12 @@ def test_fullrms_closed_form(io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("d,r", [(64, 16), (1024, 64), (1024, 1000), (513, 64), (2048, 512),
-                                 (4096, 1024), (7168, 1792)])
+@pytest.mark.parametrize("d,r", [(64, 16), (1024, 64), (1024, 1000), (1024, 1001), (513, 64),
+                                 (2048, 512), (2048, 509), (4096, 1024), (7168, 1792)])
 def test_fullrms_shapes(io, d, r):
     """One wave per row (d up to 4 chunks) and four waves per row, the element path (d = 513),
-    keys of every width; ragged row count."""
+    keys of every width, keys whose first unit also holds non-key columns (r = 1001, 509);
+    ragged row count."""
     srcs = sources(10, 77, d, io, seed=600 + d + r, scale=(0.5, 4.0))
     q = query(r, seed=601)
     for n in (1, 3, 10):
