@@ -466,6 +466,39 @@ __device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R]
   return score_from_sums(x, ss, r, eps);
 }
 
+// Row sums over the whole wave for R = 1 or 2 tile rows whose key sits in the row units of one
+// wave: the transposed butterfly of row_scores_rowlocal runs in each half of the wave, then the
+// halves are added through the lane crossbar (a lane-xor-32 exchange, which is not a vector ALU
+// instruction). About 20 (R = 1) or 31 (R = 2) vector instructions instead of the 40 or 80 of
+// a full butterfly per value. Lane j (< R) returns row j's score; other lanes return values of
+// no meaning.
+template <int R>
+__device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], int lane, int r,
+                                                  double eps) {
+  static_assert(R == 1 || R == 2, "two or four values");
+  constexpr int kRor4 = 0x124, kRor8 = 0x128;
+  const bool b0 = (lane & 1) != 0;
+  double x;
+  if constexpr (R == 2) {
+    // as in row_scores_rowlocal: lane 0 dot0, lane 1 dot1, lane 2 ss0, lane 3 ss1 of each quad
+    const double keep0 = b0 ? red[2] : red[0], send0 = b0 ? red[0] : red[2];
+    const double keep1 = b0 ? red[3] : red[1], send1 = b0 ? red[1] : red[3];
+    const double w0 = keep0 + dpp_f64<kDppXor1>(send0, 0.0);
+    const double w1 = keep1 + dpp_f64<kDppXor1>(send1, 0.0);
+    const bool b1 = (lane & 2) != 0;
+    x = (b1 ? w1 : w0) + dpp_f64<kDppXor2>(b1 ? w0 : w1, 0.0);
+  } else {
+    x = (b0 ? red[1] : red[0]) + dpp_f64<kDppXor1>(b0 ? red[0] : red[1], 0.0);
+    x += dpp_f64<kDppXor2>(x, 0.0);
+  }
+  x += dpp_f64<kRor4>(x, 0.0);
+  x += dpp_f64<kRor8>(x, 0.0);
+  x += swizzle_xor16_f64(x);
+  x += shfl_xor_f64(x, 32);
+  const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
+  return score_from_sums(x, ss, r, eps);
+}
+
 // Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
 // lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
 // division run once for all rows.

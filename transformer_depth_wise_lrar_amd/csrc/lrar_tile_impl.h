@@ -257,6 +257,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       return row_scores_rowlocal<R>(red, lane, nrm, p.eps);
     } else if constexpr (KS > 0) {
       lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
+    } else if constexpr (WPR == 1 && R <= 2) {
+      return row_scores_wave<R>(red, lane, nrm, p.eps);
     } else {
       wave_sums_dpp(red);
       if constexpr (WPR > 1) {
