@@ -466,15 +466,14 @@ __device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R]
   return score_from_sums(x, ss, r, eps);
 }
 
-// Row sums over the whole wave for R = 1 or 2 tile rows whose key sits in the row units of one
-// wave: the transposed butterfly of row_scores_rowlocal runs in each half of the wave, then the
-// halves are added through the lane crossbar (a lane-xor-32 exchange, which is not a vector ALU
-// instruction). About 20 (R = 1) or 31 (R = 2) vector instructions instead of the 40 or 80 of
-// a full butterfly per value. Lane j (< R) returns row j's score; other lanes return values of
-// no meaning.
+// Sums over the whole wave of R = 1 or 2 rows' (q . k, k . k) pairs: the transposed butterfly
+// of row_scores_rowlocal runs in each half of the wave, then the halves are added through the
+// lane crossbar (a lane-xor-32 exchange, which is not a vector ALU instruction). About 20
+// (R = 1) or 31 (R = 2) vector instructions instead of the 40 or 80 of a full butterfly per
+// value. Lane l < 2R returns the sum of red[transposed_index<R>(l)]; lanes past 2R repeat
+// those values.
 template <int R>
-__device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], int lane, int r,
-                                                  double eps) {
+__device__ __forceinline__ double wave_sums_transposed(const double (&red)[2 * R], int lane) {
   static_assert(R == 1 || R == 2, "two or four values");
   constexpr int kRor4 = 0x124, kRor8 = 0x128;
   const bool b0 = (lane & 1) != 0;
@@ -495,6 +494,24 @@ __device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], in
   x += dpp_f64<kRor8>(x, 0.0);
   x += swizzle_xor16_f64(x);
   x += shfl_xor_f64(x, 32);
+  return x;
+}
+
+// The index into red[] (dot0, ss0, dot1, ss1) of the sum that lane l < 2R holds after
+// wave_sums_transposed.
+template <int R>
+__device__ __forceinline__ int transposed_index(int lane) {
+  return R == 2 ? 2 * (lane & 1) + ((lane >> 1) & 1) : (lane & 1);
+}
+
+// Scores of R = 1 or 2 rows whose key sits in the row units of one wave, from
+// wave_sums_transposed. Lane j (< R) returns row j's score; other lanes return values of no
+// meaning.
+template <int R>
+__device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], int lane, int r,
+                                                  double eps) {
+  const double x = wave_sums_transposed<R>(red, lane);
+  // ss of row j sits R lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1)
   const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
   return score_from_sums(x, ss, r, eps);
 }

@@ -259,6 +259,21 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
     } else if constexpr (WPR == 1 && R <= 2) {
       return row_scores_wave<R>(red, lane, nrm, p.eps);
+    } else if constexpr (R <= 2) {
+      // the row's waves each reduce their own sums, then add all waves' in a fixed order (so
+      // every wave of the row gets bitwise the same score)
+      const double x = wave_sums_transposed<R>(red, lane);
+      if (lane < 2 * R) xch[parity][wib][transposed_index<R>(lane)] = x;
+      __syncthreads();
+      const int base = wib - t.w;
+#pragma unroll
+      for (int j = 0; j < 2 * R; ++j) {
+        double v = xch[parity][base][j];
+#pragma unroll
+        for (int o = 1; o < WPR; ++o) v += xch[parity][base + o][j];
+        red[j] = v;
+      }
+      parity ^= 1;
     } else {
       wave_sums_dpp(red);
       if constexpr (WPR > 1) {
