@@ -109,10 +109,18 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         }
       }
       red[2] = s;
-      wave_sums_dpp(red);
-      if constexpr (WPR > 1) {
-        double mine = lane == 0 ? red[0] : (lane == 1 ? red[1] : red[2]);
-        if (lane < 3) xch[parity][wib][lane] = mine;
+      // The three sums (q . k, k . k, g . o) by the transposed butterfly, as a fourth zero
+      // value: lane l < 4 then holds sum v4[transposed_index<2>(l)].
+      const double v4[4] = {red[0], red[1], red[2], 0.0};
+      const double x = wave_sums_transposed<2>(v4, lane);
+      if constexpr (WPR == 1) {
+        // transposed_index<2>: lane 0 holds q . k, lane 2 k . k, lane 1 g . o
+        red[0] = lane_f64(x, 0);
+        red[1] = lane_f64(x, 2);
+        red[2] = lane_f64(x, 1);
+      } else {
+        const int idx = transposed_index<2>(lane);
+        if (lane < 4 && idx < 3) xch[parity][wib][idx] = x;
         __syncthreads();
         const int base = wib - g.w;
 #pragma unroll
