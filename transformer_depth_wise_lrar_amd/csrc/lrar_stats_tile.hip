@@ -10,9 +10,10 @@
 //   * each wave takes one token row at a time, rows dealt out in bands over all waves;
 //   * score pass: per source, the key units are taken kStatsKeySlots slots at a time; float64
 //     partial sums of q_s . k for every query s and of k . k accumulate per lane, and the
-//     (queries + 1) sums are reduced by interleaved DPP chains; lane i keeps z_si. The next
-//     round's key units (the next source's first round after a source's last) are loaded while
-//     the current round is folded;
+//     (queries + 1) sums are reduced together by a transposed butterfly (each lane of a quad
+//     ends with four of them); the scores z_si go to LDS. The next round's key units (the next
+//     source's first round after a source's last) are loaded while the current round is
+//     folded;
 //   * statistics: per query, m = max_i z_si rounded to float32, e_si = exp(z_si - m),
 //     l = sum_i e_si (float64 on the lanes), written once per row;
 //   * value pass: the row is walked in chunks of 64 units, from the first chunk that holds key
@@ -32,6 +33,7 @@
 
 #include "lrar_device.h"
 #include "lrar_launch.h"
+#include "lrar_tile.h"
 
 namespace lrar {
 
@@ -146,14 +148,22 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
         }
       }
       if (last) {
-        wave_sums_dpp(red);
-        const double rho = sqrt(red[kStatsMaxQ] / p.r + p.eps);
+        // the query sums and k . k (value kStatsMaxQ) of the 16 reduced together: lane l < 4
+        // holds values 4 l' .. 4 l' + 3 with l' = 2 (l & 1) + ((l >> 1) & 1), so k . k (value
+        // 12) sits in lane 3, slot 0
+        static_assert(kStatsMaxQ == 12, "k . k is value 12 of the transposed sums");
+        double v16[16];
 #pragma unroll
-        for (int s = 0; s < kStatsMaxQ; ++s) {
-          if (lane == s && s < nqg) z_lds[wv][s][i] = red[s] / rho;
-          red[s] = 0.0;
-        }
-        red[kStatsMaxQ] = 0.0;
+        for (int s = 0; s < 16; ++s) v16[s] = s <= kStatsMaxQ ? red[s] : 0.0;
+        double u[4];
+        wave_sums_transposed16(v16, lane, u);
+        const double rho = sqrt(lane_f64(u[0], 3) / p.r + p.eps);
+        const int s0 = 8 * (lane & 1) + 4 * ((lane >> 1) & 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (lane < 4 && s0 + k < nqg) z_lds[wv][s0 + k][i] = u[k] / rho;
+#pragma unroll
+        for (int s = 0; s <= kStatsMaxQ; ++s) red[s] = 0.0;
         ++i;
       }
       kb = kb_next;
