@@ -430,15 +430,14 @@ __device__ __forceinline__ double swizzle_xor16_f64(double v) {
   return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 
-// Row-local sums for R = 1 or 2 tile rows when the spread key sits in lanes 0..31: the 2R
-// values (q . k, k . k per row) are reduced by a transposed butterfly. Partners that differ in
-// lane bit 0, then bit 1, swap halves of their value set, so after two steps each lane carries
-// one value summed over its quad; rotations of each DPP row by 4 and 8 lanes add the row's
-// four quads, and a lane-xor-16 swizzle adds the second row. Lane j (< R) returns row j's
-// score.
+// Sums over each half of the wave (lanes 0..31, 32..63) of R = 1 or 2 rows' (q . k, k . k)
+// pairs by a transposed butterfly. Partners that differ in lane bit 0, then bit 1, swap halves
+// of their value set, so after two steps each lane carries one value summed over its quad;
+// rotations of each DPP row by 4 and 8 lanes add the row's four quads, and a lane-xor-16
+// swizzle adds the half's second row. Lane l then holds the half's sum of
+// red[transposed_index<R>(l & 3)].
 template <int R>
-__device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
-                                                      double eps) {
+__device__ __forceinline__ double half_sums_transposed(const double (&red)[2 * R], int lane) {
   static_assert(R == 1 || R == 2, "two or four values");
   constexpr int kRor4 = 0x124, kRor8 = 0x128;
   const bool b0 = (lane & 1) != 0;
@@ -461,40 +460,34 @@ __device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R]
   x += dpp_f64<kRor4>(x, 0.0);
   x += dpp_f64<kRor8>(x, 0.0);
   x += swizzle_xor16_f64(x);
-  // ss of row j sits R lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1)
+  return x;
+}
+
+// The score of row j (< R) in lane j from transposed (dot, ss) sums: the ss of row j sits R
+// lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1).
+template <int R>
+__device__ __forceinline__ double score_from_transposed(double x, int r, double eps) {
   const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
   return score_from_sums(x, ss, r, eps);
 }
 
-// Sums over the whole wave of R = 1 or 2 rows' (q . k, k . k) pairs: the transposed butterfly
-// of row_scores_rowlocal runs in each half of the wave, then the halves are added through the
-// lane crossbar (a lane-xor-32 exchange, which is not a vector ALU instruction). About 20
-// (R = 1) or 31 (R = 2) vector instructions instead of the 40 or 80 of a full butterfly per
-// value. Lane l < 2R returns the sum of red[transposed_index<R>(l)]; lanes past 2R repeat
-// those values.
+// Row-local sums for R = 1 or 2 tile rows when the spread key sits in lanes 0..31: the sums of
+// the wave's first half are the rows' sums. Lane j (< R) returns row j's score.
+template <int R>
+__device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
+                                                      double eps) {
+  return score_from_transposed<R>(half_sums_transposed<R>(red, lane), r, eps);
+}
+
+// Sums over the whole wave of R = 1 or 2 rows' (q . k, k . k) pairs: the halves' transposed
+// sums added through the lane crossbar (a lane-xor-32 exchange, which is not a vector ALU
+// instruction). About 20 (R = 1) or 31 (R = 2) vector instructions instead of the 40 or 80 of
+// a full butterfly per value. Lane l < 2R returns the sum of red[transposed_index<R>(l)];
+// lanes past 2R repeat those values.
 template <int R>
 __device__ __forceinline__ double wave_sums_transposed(const double (&red)[2 * R], int lane) {
-  static_assert(R == 1 || R == 2, "two or four values");
-  constexpr int kRor4 = 0x124, kRor8 = 0x128;
-  const bool b0 = (lane & 1) != 0;
-  double x;
-  if constexpr (R == 2) {
-    // as in row_scores_rowlocal: lane 0 dot0, lane 1 dot1, lane 2 ss0, lane 3 ss1 of each quad
-    const double keep0 = b0 ? red[2] : red[0], send0 = b0 ? red[0] : red[2];
-    const double keep1 = b0 ? red[3] : red[1], send1 = b0 ? red[1] : red[3];
-    const double w0 = keep0 + dpp_f64<kDppXor1>(send0, 0.0);
-    const double w1 = keep1 + dpp_f64<kDppXor1>(send1, 0.0);
-    const bool b1 = (lane & 2) != 0;
-    x = (b1 ? w1 : w0) + dpp_f64<kDppXor2>(b1 ? w0 : w1, 0.0);
-  } else {
-    x = (b0 ? red[1] : red[0]) + dpp_f64<kDppXor1>(b0 ? red[0] : red[1], 0.0);
-    x += dpp_f64<kDppXor2>(x, 0.0);
-  }
-  x += dpp_f64<kRor4>(x, 0.0);
-  x += dpp_f64<kRor8>(x, 0.0);
-  x += swizzle_xor16_f64(x);
-  x += shfl_xor_f64(x, 32);
-  return x;
+  const double x = half_sums_transposed<R>(red, lane);
+  return x + shfl_xor_f64(x, 32);
 }
 
 // Sums over the whole wave of 16 values: two transposed butterfly steps leave each lane of a
@@ -540,10 +533,7 @@ __device__ __forceinline__ int transposed_index(int lane) {
 template <int R>
 __device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], int lane, int r,
                                                   double eps) {
-  const double x = wave_sums_transposed<R>(red, lane);
-  // ss of row j sits R lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1)
-  const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
-  return score_from_sums(x, ss, r, eps);
+  return score_from_transposed<R>(wave_sums_transposed<R>(red, lane), r, eps);
 }
 
 // Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
