@@ -36,9 +36,19 @@
  *   - Every function validates all arguments before touching the device and returns a
  *     status; nothing throws or aborts. lrar_last_error() describes the last failure on
  *     the calling thread.
+ *   - Aliasing: no output may share a byte with any other buffer of the call (inputs may share
+ *     bytes with each other: repeated and strided sources are legal). Buffers are compared as
+ *     the rows they touch, exactly when they share one row stride, so column slices of one
+ *     wide buffer may be sources and output together; a partial overlap returns
+ *     LRAR_ERR_INVALID (at T > 0). The one exception is lrar_merge_accumulate's in-place update.
  *   - Rows are fully vectorised (16-byte accesses) when d is a multiple of 8 (bf16) or 4
  *     (f32) and every row start is 16-byte aligned; other shapes (e.g. d = 513, odd
- *     strides) take a scalar path that computes the same result more slowly.
+ *     strides) take a scalar-element path that computes the same result more slowly.
+ *   - A "register tile" holds a whole row in registers: up to 32 chunks of 64 units, i.e.
+ *     d <= 16384 (bf16) / 8192 (f32) on the vector path and d <= 2048 on the element path.
+ *     The one-pass reads run on such tiles; rows wider than a tile are served by a
+ *     column-chunked kernel that reads the keys first, takes the softmax once and then streams
+ *     the rows (the key bytes are read twice).
  */
 #ifndef LRATTNRES_H_
 #define LRATTNRES_H_
@@ -68,19 +78,19 @@ typedef enum lrar_variant {
   LRAR_VARIANT_ONLINE = 2    /* one pass per source with an online-softmax accumulator */
 } lrar_variant;
 
-/* The depth-mix read (LR-AttnRes paper §3.1/§3.3; explainer, "A short description...").
+/* The depth-mix read (LR-AttnRes paper §3.1 routing equation, §3.3 routing keys; explainer,
+ * "A short description chooses a full-width value").
  *   T, d, r, eps : tokens, width, key width (1 <= r <= d), RMS epsilon (>= 0, finite;
  *                  eps = 0 is allowed and yields NaN for an all-zero key slice).
  *   io           : element type of the sources and of out.
  *   n, src, src_ld : 1 <= n <= LRAR_MAX_SOURCES sources; src[i] is a device [T, src_ld[i]]
  *                  matrix of which the first d columns are used.
  *   q            : device float32 [r], the site query.
- *   out, out_ld  : device [T, out_ld] of type io; receives h. Must not be one of src.
+ *   out, out_ld  : device [T, out_ld] of type io; receives h. Overlaps no source.
  *   alpha, alpha_ld : optional device float32 [T, alpha_ld >= n]; receives the weights.
- *   variant      : lrar_variant. LRAR_ERR_UNSUPPORTED if ONLINE is asked for a d it does
- *                  not cover: d > 16384 (bf16) / 8192 (f32) on the vector path, taken when
- *                  d is a multiple of 8 (bf16) / 4 (f32) and every row of the sources and
- *                  of out starts 16-byte aligned; d > 2048 on the element path otherwise.
+ *   variant      : lrar_variant. AUTO runs ONLINE when the row fits a register tile and
+ *                  TWO_PASS otherwise; TWO_PASS serves any width; ONLINE returns
+ *                  LRAR_ERR_UNSUPPORTED for rows wider than a register tile.
  * With n = 1 the output equals src[0] exactly (the embedding-only read is the identity). */
 lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                          int32_t n, const void* const* src, const int64_t* src_ld,
@@ -90,8 +100,9 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
 /* The full-width-RMS control read (LR-AttnRes paper §4.4, Eq. 13 "control"; App. B.1): the
  * key of source i is its last r coordinates divided by the RMS of the whole row,
  *     kbar_i = tail_r(o_i) / sqrt(||o_i||^2 / d + eps),   z_i = q . kbar_i,
- * and h = sum_i softmax_i(z) o_i as in lrar_forward. Arguments as for lrar_forward; always one
- * pass over the sources. LRAR_ERR_UNSUPPORTED for rows wider than the online variant covers. */
+ * and h = sum_i softmax_i(z) o_i as in lrar_forward. Arguments as for lrar_forward. One pass
+ * over the sources on a register tile; rows wider than a tile take the column-chunked kernel
+ * (its key pass sums the square of every column). */
 lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                                  int32_t n, const void* const* src, const int64_t* src_ld,
                                  const float* q, void* out, int64_t out_ld, float* alpha,
@@ -102,11 +113,12 @@ lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lr
  * elements). Source i's value is src[i] (d wide) and its key the first r columns of key[i]:
  *     z_i = q . k_i / sqrt(||k_i||^2 / r + eps),   h = sum_i softmax_i(z) o_i.
  *   key, key_ld : host arrays of n device pointers [T, key_ld[i] >= r] of type io (1 <= r <= d).
- * Other arguments as for lrar_forward; one pass over the sources and keys. Served for r <= 64
- * with any key alignment, and for r <= 512 when r is a multiple of the per-lane key piece
- * (r / 32 or r / 64 rounded up to a power of two) and the key rows are aligned to that piece
- * (16 bytes at most); LRAR_ERR_UNSUPPORTED otherwise, or for rows wider than the online variant
- * covers. */
+ * Other arguments as for lrar_forward. One pass over the sources and keys on a register tile
+ * when the row fits one and a spread key piece serves the key: r <= 64 with any key alignment,
+ * or r <= 512 when r is a multiple of the per-lane piece (r / 32 or r / 64 rounded up to a power
+ * of two) and the key rows are aligned to it (16 bytes at most). Every other key (any r, any
+ * alignment) and rows wider than a tile take the column-chunked kernel, whose key pass reads the
+ * key rows element by element. */
 lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                               int32_t n, const void* const* src, const int64_t* src_ld,
                               const void* const* key, const int64_t* key_ld, const float* q,
@@ -122,22 +134,26 @@ lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_
  *   m, l, ml_ld   : device float32, element (s, t) at s * ml_ld + t, ml_ld >= T.
  *   acc           : element (s, t, j) at s * acc_qstride + t * acc_ld + j, in acc_dtype
  *                   (LRAR_F32 is exact enough for parity; LRAR_BF16 halves the bytes).
- *                   acc_ld >= d, acc_qstride >= T * acc_ld. Must not overlap the sources. */
+ *                   acc_ld >= d, acc_qstride >= T * acc_ld. m, l and acc overlap no other
+ *                   buffer of the call. */
 lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                                int32_t n, const void* const* src, const int64_t* src_ld,
                                int32_t nq, const float* q, int64_t q_ld, float* m, float* l,
                                int64_t ml_ld, void* acc, lrar_dtype acc_dtype, int64_t acc_ld,
                                int64_t acc_qstride, void* stream);
 
-/* Phase 2: merge one site's Phase-1 statistics with n >= 0 further sources (normally the
- * site's intra-block partial sum) by the online-softmax update, and normalise:
+/* Phase 2 (AttnRes technical-report summary, "Method": Phase 2 merges each site's intra-block
+ * partial sum into the Phase-1 statistics by an online-softmax update; LR-AttnRes paper §3.4:
+ * the sliced key keeps that merge exact). Merges one site's (m, l, acc) with n >= 0 further
+ * sources (normally the site's intra-block partial sum), and normalises:
  *     m' = max(m, max_b z_b),  l' = l e^{m-m'} + sum_b e^{z_b-m'},
  *     h  = (acc e^{m-m'} + sum_b e^{z_b-m'} o_b) / l'.
  *   m, l          : device float32 [T]; acc: device [T, acc_ld] of acc_dtype.
  *   n, src, src_ld, q : the extra sources and the site query (q may be NULL when n = 0).
  *   out, out_ld   : device [T, out_ld] of type io.
  *   m_out, l_out  : optional device float32 [T]; receive m' (rounded to float32) and l'
- *                   relative to that rounded m'. */
+ *                   relative to that rounded m'.
+ * Rows wider than a register tile take the column-chunked kernel. */
 lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                        const float* m, const float* l, const void* acc, lrar_dtype acc_dtype,
                        int64_t acc_ld, int32_t n, const void* const* src,
@@ -145,8 +161,9 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
                        float* m_out, float* l_out, void* stream);
 
 /* Phase 2 with the partial-sum update fused in (LR-AttnRes paper §3.3 "Partial-block routing":
- * each sub-layer output updates the full-width partial sum, b <- b + o, and the site routes
- * over the updated sum; AttnRes technical-report summary, "Method", Phase 2). In one pass:
+ * the block's running partial sum is kept at full width, a new sub-layer output is added to it,
+ * and the next read site takes the sum as a source; AttnRes technical-report summary, "Method",
+ * Phase 2). In one pass:
  *     b_out = b + o                 (element type io, round to nearest even; b = 0 if NULL),
  *     then lrar_merge of (m, l, acc) with the single extra source b_out.
  * Reading b and o once and writing b_out replaces an update kernel plus a merge that reads
@@ -157,8 +174,8 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
  *   b_out, b_out_ld : device [T, b_out_ld] of type io; receives b + o. It may be b or o itself
  *                   (same pointer and row stride: updated in place) but may not otherwise
  *                   overlap them, acc or out.
- *   Other arguments as for lrar_merge with n = 1. Rows wider than the online variant covers
- *   return LRAR_ERR_UNSUPPORTED. */
+ *   Other arguments as for lrar_merge with n = 1. Rows wider than a register tile run as two
+ *   kernels: b_out = b + o, then the column-chunked merge reads b_out. */
 lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                                   const float* m, const float* l, const void* acc,
                                   lrar_dtype acc_dtype, int64_t acc_ld, const void* b,
@@ -179,9 +196,13 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
  *                   order, so results are bitwise reproducible.
  *   workspace     : device scratch of at least lrar_backward_workspace_size(T, d, r, n)
  *                   bytes, 8-byte aligned; its contents are not needed after the call.
- * Supported on the vector path (d a multiple of 8 (bf16) / 4 (f32), every row of the
- * sources, dout and dsrc 16-byte aligned) for d <= 16384 (bf16) / 8192 (f32), on the element path for d <= 2048;
- * LRAR_ERR_UNSUPPORTED otherwise. */
+ * Rows that fit a register tile (vector path: d a multiple of 8 (bf16) / 4 (f32), every row of
+ * the sources, dout and dsrc 16-byte aligned, d <= 16384 / 8192) run on row tiles, with any r.
+ * Other rows (the element path at any width; wider vector rows) run one wave per row and keep
+ * query-gradient partials for the key's chunks of 64 units in registers: served when the key
+ * spans at most 64 such chunks on the element path (r <= 4032 always) or 8 on the vector path
+ * (8 x 64 units, r <= 3584 (bf16) / 1792 (f32) always); LRAR_ERR_UNSUPPORTED otherwise.
+ * dsrc, dq and the workspace overlap no other buffer of the call (nor each other). */
 lrar_status lrar_backward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
                           int32_t n, const void* const* src, const int64_t* src_ld,
                           const float* q, const float* dout, int64_t dout_ld,

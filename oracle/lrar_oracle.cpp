@@ -305,9 +305,10 @@ static double round_to_format(double x, int p) {
   return std::nearbyint(x / spacing) * spacing;  // the default mode: nearest, ties to even
 }
 
-// Phase 2 with the partial-sum update fused in ([Paper] §3.3 "Partial-block routing": each
-// sub-layer output o updates the full-width partial sum, b <- b + o, and the key of the sum is
-// taken after the update; [AttnRes-TR] Method, Phase 2 merges the intra-block lookback). The
+// Phase 2 with the partial-sum update fused in ([Paper] §3.3 "Partial-block routing": the
+// block's running sum is kept at full width, a new sub-layer output is added into it before
+// the next read, and that read keys the sum by its last r columns after the addition;
+// [AttnRes-TR] Method, Phase 2 merges the intra-block lookback). The
 // updated sum is stored in the sources' element type with a p-bit significand,
 //   b' = round_to_format(b + o, p)      (b null: the block's first write, b' = round(o)),
 // and the site merges its Phase-1 statistics with the single source b' as orc_merge does.

@@ -89,7 +89,8 @@ def test_forward_fullrms_rejects(L, kw):
 
 def test_forward_fullrms_limits(L):
     assert fwd_full(L, T=0) == lrar.LRAR_OK
-    assert fwd_full(L, T=0, d=16392, r=16, ld=16392, out_ld=16392) == lrar.LRAR_ERR_UNSUPPORTED
+    # rows wider than a register tile take the column-chunked kernel
+    assert fwd_full(L, T=0, d=16392, r=16, ld=16392, out_ld=16392) == lrar.LRAR_OK
 
 
 def fwd_keys(L, T=4, d=8, r=4, io=1, n=2, ld=8, key=FAKE * 4, key_ld=8, keys=True, q=FAKE,
@@ -112,14 +113,14 @@ def test_forward_keys_rejects(L, kw):
 
 def test_forward_keys_limits(L):
     assert fwd_keys(L, T=0) == lrar.LRAR_OK
-    # r = 96 takes pieces of 4 (8-byte loads): served at 8-byte alignment, not at 2
+    # keys that no spread piece serves (misaligned pieces, r = 1000) and rows wider than a
+    # tile take the column-chunked kernel, which reads the keys element by element
     big = dict(T=0, d=1024, r=96, ld=1024, out_ld=1024, key_ld=96)
     assert fwd_keys(L, **big) == lrar.LRAR_OK
-    assert fwd_keys(L, key=FAKE * 4 + 2, **big) == lrar.LRAR_ERR_UNSUPPORTED
-    # r = 64 needs no alignment beyond the element's
+    assert fwd_keys(L, key=FAKE * 4 + 2, **big) == lrar.LRAR_OK
     assert fwd_keys(L, key=FAKE * 4 + 2, **dict(big, r=64, key_ld=64)) == lrar.LRAR_OK
-    # r = 1000 is wider than a spread key reaches
-    assert fwd_keys(L, **dict(big, r=1000, key_ld=1000)) == lrar.LRAR_ERR_UNSUPPORTED
+    assert fwd_keys(L, **dict(big, r=1000, key_ld=1000)) == lrar.LRAR_OK
+    assert fwd_keys(L, **dict(big, d=16392, ld=16392, out_ld=16392)) == lrar.LRAR_OK
 
 
 def merge_acc(L, T=4, d=8, r=4, io=1, acc_dtype=0, acc_ld=8, b=FAKE * 7, b_ld=8, o=FAKE * 8,
@@ -151,7 +152,7 @@ def test_merge_accumulate_in_place_and_limits(L):
     assert merge_acc(L, T=0, b=None) == lrar.LRAR_OK           # the block's first write
     wide = dict(T=0, d=16392, acc_ld=16392, b_ld=16392, o_ld=16392, b_out_ld=16392,
                 out_ld=16392)
-    assert merge_acc(L, **wide) == lrar.LRAR_ERR_UNSUPPORTED
+    assert merge_acc(L, **wide) == lrar.LRAR_OK  # an add kernel, then the column-chunked merge
 
 
 def test_online_too_wide_is_unsupported(L):
@@ -242,12 +243,76 @@ def test_backward_workspace_size(L):
     assert L.lrar_backward_workspace_size(16384, 4096, 2048, 10) > a
 
 
-def test_backward_too_wide_is_unsupported(L):
-    p, ld = _src(1, 20000)
-    dp = (ctypes.c_void_p * 1)(FAKE * 10)
-    dl = (ctypes.c_int64 * 1)(20000)
-    assert L.lrar_backward(4, 20000, 8, 1e-6, 1, 1, p, ld, FAKE * 2, FAKE * 3, 20000, dp, dl, 0,
+@pytest.mark.parametrize("d,r,ld", [
+    (20000, 20000, 20000),  # vector rows past a tile: the key spans 40 chunks (at most 8)
+    (20000, 4104, 20000),   # the same, 9 chunks
+    (8192, 8192, 8193),     # element path (odd stride): 128 chunks (at most 64)
+    (4097, 4097, 4097),     # element path, unaligned width: 65 chunks
+])
+def test_backward_key_too_wide_is_unsupported(L, d, r, ld):
+    """Rows that no row tile holds keep query-gradient partials for the key's chunks of 64
+    units in registers; a key spanning more of them is refused, at T > 0, before any device
+    work."""
+    p, lds_ = _src(1, ld)
+    dp = (ctypes.c_void_p * 1)(FAKE * 100)
+    dl = (ctypes.c_int64 * 1)(ld)
+    assert L.lrar_backward(4, d, r, 1e-6, 1, 1, p, lds_, FAKE * 2, FAKE * 300, ld, dp, dl, 0,
                            FAKE * 4, FAKE * 5, 1 << 30, None) == lrar.LRAR_ERR_UNSUPPORTED
+    assert "chunks" in L.lrar_last_error().decode()
+
+
+# ---- partial overlaps: every output is checked by byte range against every other buffer ----
+# Sources sit at FAKE (rows of 8 bf16 = 16 bytes, 4 rows); an offset of 16 bytes starts one row in.
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(out=FAKE + 16), "out overlaps src"),                     # out one row into a source
+    (dict(out=FAKE + 48 + 8), "out overlaps src"),                 # into the last row's tail
+    (dict(alpha=FAKE + 8, alpha_ld=2), "alpha overlaps src"),
+    (dict(alpha=FAKE * 2 + 32, alpha_ld=2), "alpha overlaps out"),
+    (dict(q=FAKE * 2 + 4), "out overlaps q"),
+])
+def test_forward_rejects_partial_overlaps(L, kw, what):
+    assert fwd(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
+
+
+def test_forward_keys_rejects_partial_overlap(L):
+    assert fwd_keys(L, key=FAKE * 2 + 16) == lrar.LRAR_ERR_INVALID
+    assert "out overlaps key" in L.lrar_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(acc=FAKE + 32), "acc overlaps src"),
+    (dict(m=FAKE * 4 - 8), "l overlaps m"),
+    (dict(acc=FAKE * 2 + 16), "acc overlaps q"),
+    (dict(m=FAKE * 5 + 100), "acc overlaps m"),
+])
+def test_stats_rejects_partial_overlaps(L, kw, what):
+    assert stats(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(out=FAKE + 16), "out overlaps src"),
+    (dict(out=FAKE * 5 + 64), "out overlaps acc"),
+    (dict(m_out=FAKE * 3 + 4), "m_out overlaps m"),
+    (dict(m_out=FAKE * 7, l_out=FAKE * 7 + 8), "l_out overlaps m_out"),
+])
+def test_merge_rejects_partial_overlaps(L, kw, what):
+    assert merge(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(dsrc=[FAKE * 10, FAKE * 10 + 64]), "dsrc[1] overlaps dsrc[0]"),
+    (dict(dsrc=[FAKE * 7 + 32, FAKE * 11]), "dsrc[0] overlaps dout"),
+    (dict(dsrc=[FAKE + 16, FAKE * 11]), "dsrc[0] overlaps src"),
+    (dict(dq=FAKE * 10 + 4), "dq overlaps dsrc[0]"),
+    (dict(ws=FAKE * 7 + 16), "workspace overlaps dout"),
+])
+def test_backward_rejects_partial_overlaps(L, kw, what):
+    assert bwd(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
 
 
 def test_copy_rejects(L):

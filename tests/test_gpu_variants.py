@@ -167,24 +167,29 @@ def test_keys_widths(io, d, r):
 
 
 def test_keys_equal_value_tails_match_slice_read():
-    """Keys copied from the values' last r columns give the sliced read's weights."""
+    """Keys copied from the values' last r columns: the separate-key read and the sliced read
+    both meet the oracle's sliced read (LR-AttnRes paper App. C.1: a key taken from the value's
+    own tail is the sliced key)."""
     T, d, r = 50, 1024, 64
     srcs = sources(7, T, d, "bf16", seed=650)
     keys = [s[:, d - r:].contiguous() for s in srcs]
     q = query(r, seed=651)
     say("[keys] keys = value tails")
-    _, a1 = lrar.lrar_forward_keys(srcs, keys, q, r, 1e-6, alpha=True)
-    _, a2 = lrar.lrar_forward(srcs, q, r, 1e-6, alpha=True)
+    o1, a1 = lrar.lrar_forward_keys(srcs, keys, q, r, 1e-6, alpha=True)
+    o2, a2 = lrar.lrar_forward(srcs, q, r, 1e-6, alpha=True)
     torch.cuda.synchronize()
-    parity.assert_weights(f64(a1), f64(a2), "keys vs slice")
+    s64 = [f64(s) for s in srcs]
+    h_ref, a_ref = oracle.forward(s64, f64(q), r, 1e-6)
+    for name, o, a in (("keys", o1, a1), ("slice", o2, a2)):
+        parity.assert_weights(f64(a), a_ref, f"{name} read vs oracle slice alpha")
+        parity.assert_read(f64(o), h_ref, a_ref, s64, "bf16", f"{name} read vs oracle slice h")
 
 
-def test_keys_unsupported_rank_raises():
-    srcs = sources(2, 8, 1024, "bf16", seed=660)
-    keys = key_tensors(2, 8, 1000, "bf16", seed=661)
-    with pytest.raises(lrar.LrarError) as e:
-        lrar.lrar_forward_keys(srcs, keys, query(1000, seed=662), 1000, 1e-6)
-    assert e.value.status == lrar.LRAR_ERR_UNSUPPORTED
+def test_keys_wide_rank_takes_the_chunked_read():
+    """r = 1000 is wider than a spread key piece reaches: the column-chunked read serves it."""
+    srcs = sources(3, 8, 1024, "bf16", seed=660)
+    keys = key_tensors(3, 8, 1000, "bf16", seed=661)
+    check_keys(srcs, keys, query(1000, seed=662), 1000, 1e-6, "r=1000")
 
 
 def test_keys_full_size_d1024():

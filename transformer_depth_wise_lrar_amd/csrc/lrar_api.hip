@@ -88,10 +88,107 @@ lrar_status check_sources(const char* fn, int64_t T, int32_t d, lrar_dtype io, i
   return LRAR_OK;
 }
 
-bool overlaps_source(const void* p, const lrar::SrcList& S, int n) {
-  for (int i = 0; i < n; ++i)
-    if (S.ptr[i] == p) return true;
-  return false;
+// ---- aliasing --------------------------------------------------------------------------------
+// A buffer an entry point touches, as `rows` rows of `width` bytes every `ld` bytes from `base`
+// (a plain span is one row). Outputs may overlap no other buffer of the call; inputs may overlap
+// each other (repeated or strided sources are legal).
+struct Region {
+  uintptr_t base;
+  int64_t rows, ld, width;
+  const char* name;
+  int index;     // for tables of buffers (-1 for a single buffer)
+  // An output and an input that both carry this flag may be the same buffer (same start, row
+  // stride and shape): an in-place update.
+  bool inplace;
+};
+
+Region rows_region(const void* p, int64_t T, int64_t ld, int64_t d, size_t es, const char* name,
+                   int index = -1) {
+  Region g{reinterpret_cast<uintptr_t>(p), p == nullptr ? 0 : T, ld * static_cast<int64_t>(es),
+           d * static_cast<int64_t>(es), name, index, false};
+  return g;
+}
+
+Region span_region(const void* p, int64_t bytes, const char* name, int index = -1) {
+  Region g{reinterpret_cast<uintptr_t>(p), (p == nullptr || bytes <= 0) ? 0 : 1, bytes, bytes,
+           name, index, false};
+  return g;
+}
+
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+  const int64_t q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// Whether two regions share a byte: exact when both use one row stride (or one is a span),
+// else by their bounding ranges.
+bool regions_overlap(Region a, Region b) {
+  if (a.rows <= 0 || b.rows <= 0 || a.width <= 0 || b.width <= 0) return false;
+  const auto end = [](const Region& g) {
+    return g.base + static_cast<uintptr_t>((g.rows - 1) * g.ld + g.width);
+  };
+  if (end(a) <= b.base || end(b) <= a.base) return false;
+  if (a.rows == 1) a.ld = b.ld;
+  if (b.rows == 1) b.ld = a.ld;
+  if (a.ld != b.ld || a.width > a.ld || b.width > b.ld) return true;
+  // row i of a meets row j of b iff -wb < delta + (j - i) L < wa, delta = b.base - a.base
+  const int64_t L = a.ld;
+  const int64_t delta = static_cast<int64_t>(b.base - a.base);
+  const int64_t k_lo = floor_div(-b.width - delta, L) + 1;
+  const int64_t k_hi = -floor_div(-(a.width - delta), L) - 1;  // ceil((wa - delta) / L) - 1
+  const int64_t lo = k_lo > -(a.rows - 1) ? k_lo : -(a.rows - 1);
+  const int64_t hi = k_hi < b.rows - 1 ? k_hi : b.rows - 1;
+  return lo <= hi;
+}
+
+constexpr int kMaxRegions = 4 * LRAR_MAX_SOURCES + 16;
+
+struct Regions {
+  Region in[kMaxRegions];
+  Region out[kMaxRegions / 2];
+  int n_in = 0, n_out = 0;
+  void input(const Region& g) {
+    if (n_in < kMaxRegions) in[n_in++] = g;
+  }
+  void output(const Region& g) {
+    if (n_out < kMaxRegions / 2) out[n_out++] = g;
+  }
+};
+
+void region_label(const Region& g, char* buf, size_t len) {
+  if (g.index >= 0) snprintf(buf, len, "%s[%d]", g.name, g.index);
+  else snprintf(buf, len, "%s", g.name);
+}
+
+// Every output against every input and every other output.
+lrar_status check_disjoint(const char* fn, const Regions& R) {
+  char a[48], b[48];
+  for (int i = 0; i < R.n_out; ++i) {
+    const Region& w = R.out[i];
+    for (int j = 0; j < R.n_in; ++j) {
+      const Region& x = R.in[j];
+      const bool same = w.base == x.base && w.ld == x.ld && w.width == x.width && w.rows == x.rows;
+      if (same && x.inplace && w.inplace) continue;
+      if (regions_overlap(w, x)) {
+        region_label(w, a, sizeof(a));
+        region_label(x, b, sizeof(b));
+        return fail(LRAR_ERR_INVALID, "%s: %s overlaps %s", fn, a, b);
+      }
+    }
+    for (int j = 0; j < i; ++j) {
+      if (regions_overlap(w, R.out[j])) {
+        region_label(w, a, sizeof(a));
+        region_label(R.out[j], b, sizeof(b));
+        return fail(LRAR_ERR_INVALID, "%s: %s overlaps %s", fn, a, b);
+      }
+    }
+  }
+  return LRAR_OK;
+}
+
+void add_sources(Regions& R, const lrar::SrcList& S, int n, int64_t T, int64_t d, size_t es,
+                 const char* name) {
+  for (int i = 0; i < n; ++i) R.input(rows_region(S.ptr[i], T, S.ld[i], d, es, name, i));
 }
 
 // Checks the arguments every forward read shares and fills the parameter block; use_vec is
@@ -109,8 +206,6 @@ lrar_status check_read(const char* fn, int64_t T, int32_t d, int32_t r, double e
   if (q == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: q is null", fn);
   if (out == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: out is null", fn);
   if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
-  if (out != nullptr && overlaps_source(out, p.src, n))
-    return fail(LRAR_ERR_INVALID, "%s: out aliases a source", fn);
   if (alpha != nullptr && alpha_ld < n)
     return fail(LRAR_ERR_INVALID, "%s: alpha_ld = %lld < n = %d", fn, (long long)alpha_ld, n);
   const int vec = vec_of(io);
@@ -129,15 +224,12 @@ lrar_status check_read(const char* fn, int64_t T, int32_t d, int32_t r, double e
   return LRAR_OK;
 }
 
-// Byte ranges of two [T, ld] row-major matrices (first d columns used; elements of es_a and
-// es_b bytes) intersect.
-bool rows_overlap(const void* a, int64_t a_ld, const void* b, int64_t b_ld, int64_t T, int32_t d,
-                  size_t es_a, size_t es_b) {
-  if (a == nullptr || b == nullptr || T == 0) return false;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  const uintptr_t a1 = a0 + static_cast<uintptr_t>((T - 1) * a_ld + d) * es_a;
-  const uintptr_t b1 = b0 + static_cast<uintptr_t>((T - 1) * b_ld + d) * es_b;
-  return a0 < b1 && b0 < a1;
+// The buffers of a forward read: the sources and q read, out and alpha written.
+void read_regions(Regions& R, const lrar::ReadParams& p, lrar_dtype io) {
+  add_sources(R, p.src, p.n, p.T, p.d, esize(io), "src");
+  R.input(span_region(p.q, static_cast<int64_t>(p.r) * 4, "q"));
+  R.output(rows_region(p.out, p.T, p.out_ld, p.d, esize(io), "out"));
+  if (p.alpha != nullptr) R.output(rows_region(p.alpha, p.T, p.alpha_ld, p.n, 4, "alpha"));
 }
 
 // A row fits a register tile when it has at most tile_max_chunks() chunks of 64 units.
@@ -176,6 +268,10 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
     kind = tile_fits ? lrar::ReadKind::kOnline : lrar::ReadKind::kTwoPass;
   }
   if (T == 0) return LRAR_OK;
+  Regions R;
+  read_regions(R, p, io);
+  st = check_disjoint(fn, R);
+  if (st != LRAR_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = tile_fits ? lrar::launch_tile(p, kind, io == LRAR_BF16, use_vec, 0, hs)
                                  : lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0, hs);
@@ -192,13 +288,18 @@ lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lr
   lrar_status st = check_read(fn, T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
                               alpha_ld, p, use_vec);
   if (st != LRAR_OK) return st;
-  if (!row_fits_tile(d, use_vec))
-    return fail(LRAR_ERR_UNSUPPORTED, "%s: the control read holds a whole row in registers; "
-                "d = %d is too wide on this path", fn, d);
   if (T == 0) return LRAR_OK;
-  return device_status(lrar::launch_tile_fullrms(p, io == LRAR_BF16, use_vec,
-                                                 static_cast<hipStream_t>(stream)),
-                       fn);
+  Regions R;
+  read_regions(R, p, io);
+  st = check_disjoint(fn, R);
+  if (st != LRAR_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // rows too wide for a register tile: key pass over the whole rows, then the values
+  if (!row_fits_tile(d, use_vec))
+    return device_status(lrar::launch_read(p, lrar::ReadKind::kTwoPass, io == LRAR_BF16, use_vec,
+                                           0, hs, lrar::kKeyFullRms),
+                         fn);
+  return device_status(lrar::launch_tile_fullrms(p, io == LRAR_BF16, use_vec, hs), fn);
 }
 
 lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
@@ -223,27 +324,30 @@ lrar_status lrar_forward_keys(int64_t T, int32_t d, int32_t r, double eps, lrar_
       return fail(LRAR_ERR_INVALID, "%s: key_ld[%d] = %lld < r = %d", fn, i,
                   (long long)key_ld[i], r);
     if (!stride_ok(key_ld[i], esize(io))) return stride_fail(fn, "key_ld", key_ld[i]);
-    if (key[i] == out && out != nullptr)
-      return fail(LRAR_ERR_INVALID, "%s: out aliases key[%d]", fn, i);
     const uintptr_t bits = reinterpret_cast<uintptr_t>(key[i]) |
                            static_cast<uintptr_t>(key_ld[i]) * esize(io);
     while (align > 1 && (bits & (align - 1)) != 0) align >>= 1;
     keys.ptr[i] = key[i];
     keys.ld[i] = key_ld[i];
   }
-  if (!row_fits_tile(d, use_vec))
-    return fail(LRAR_ERR_UNSUPPORTED, "%s: the read holds a whole row in registers; d = %d is "
-                "too wide on this path", fn, d);
-  p.key_piece = lrar::tile_keys_piece(r, static_cast<int>(align), static_cast<int>(esize(io)),
-                                      use_vec);
-  if (p.key_piece == 0)
-    return fail(LRAR_ERR_UNSUPPORTED, "%s: r = %d is not served with keys aligned to %d bytes "
-                "on the %s path (r <= 64, or r <= 512 divisible by its piece with aligned rows)",
-                fn, r, static_cast<int>(align), use_vec > 1 ? "vector" : "element");
   if (T == 0) return LRAR_OK;
-  return device_status(lrar::launch_tile_keys(p, keys, io == LRAR_BF16, use_vec,
-                                              static_cast<hipStream_t>(stream)),
-                       fn);
+  Regions R;
+  read_regions(R, p, io);
+  for (int i = 0; i < n; ++i) R.input(rows_region(key[i], T, key_ld[i], r, esize(io), "key", i));
+  st = check_disjoint(fn, R);
+  if (st != LRAR_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // One pass on register tiles when the row fits one and a spread key piece serves this key;
+  // otherwise the key pass reads the key rows element by element, then the values.
+  p.key_piece = row_fits_tile(d, use_vec)
+                    ? lrar::tile_keys_piece(r, static_cast<int>(align),
+                                            static_cast<int>(esize(io)), use_vec)
+                    : 0;
+  if (p.key_piece == 0)
+    return device_status(lrar::launch_read(p, lrar::ReadKind::kTwoPass, io == LRAR_BF16, use_vec,
+                                           0, hs, lrar::kKeySeparate, &keys),
+                         fn);
+  return device_status(lrar::launch_tile_keys(p, keys, io == LRAR_BF16, use_vec, hs), fn);
 }
 
 lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
@@ -269,9 +373,6 @@ lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar
     return fail(LRAR_ERR_INVALID, "%s: acc_qstride = %lld < T * acc_ld", fn, (long long)acc_qstride);
   if (T > 0 && (q == nullptr || m == nullptr || l == nullptr || acc == nullptr))
     return fail(LRAR_ERR_INVALID, "%s: null q, m, l or acc", fn);
-  if (m == l && m != nullptr) return fail(LRAR_ERR_INVALID, "%s: m and l alias", fn);
-  if (acc != nullptr && overlaps_source(acc, p.src, n))
-    return fail(LRAR_ERR_INVALID, "%s: acc aliases a source", fn);
   const int vec = vec_of(io);
   // acc units are VEC elements of acc_dtype; rows must start 16-byte aligned when acc is fp32
   // and units are 8 wide (two 16-byte halves), or whenever acc is written 16 bytes at a time.
@@ -281,6 +382,21 @@ lrar_status lrar_forward_stats(int64_t T, int32_t d, int32_t r, double eps, lrar
       (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0 || acc_qstride % acc_elems_per_16 != 0))
     vec_ok = false;
   if (T == 0) return LRAR_OK;
+  {
+    Regions R;
+    add_sources(R, p.src, n, T, d, esize(io), "src");
+    R.input(rows_region(q, nq, q_ld, r, 4, "q"));
+    R.output(rows_region(m, nq, ml_ld, T, 4, "m"));
+    R.output(rows_region(l, nq, ml_ld, T, 4, "l"));
+    // the accumulators as nq * T rows when the query blocks follow each other, else as one span
+    if (nq == 1 || acc_qstride == T * acc_ld)
+      R.output(rows_region(acc, nq * T, acc_ld, d, esize(acc_dtype), "acc"));
+    else
+      R.output(span_region(acc, ((nq - 1) * acc_qstride + (T - 1) * acc_ld + d) *
+                                    static_cast<int64_t>(esize(acc_dtype)), "acc"));
+    st = check_disjoint(fn, R);
+    if (st != LRAR_OK) return st;
+  }
   p.n = n;
   p.d = d;
   p.r = r;
@@ -321,15 +437,25 @@ lrar_status lrar_merge(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype i
     return fail(LRAR_ERR_INVALID, "%s: null m, l, acc or out", fn);
   if (T > 0 && n > 0 && q == nullptr) return fail(LRAR_ERR_INVALID, "%s: q is null", fn);
   if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
-  if (out != nullptr && overlaps_source(out, p.src, n))
-    return fail(LRAR_ERR_INVALID, "%s: out aliases a source", fn);
-  if (m_out != nullptr && m_out == l_out) return fail(LRAR_ERR_INVALID, "%s: m_out and l_out alias", fn);
   const int vec = vec_of(io);
   if (!aligned16(out) || out_ld % vec != 0) vec_ok = false;
   const int acc_elems_per_16 = acc_dtype == LRAR_BF16 ? 8 : 4;
   if ((esize(acc_dtype) * vec) % 16 == 0 && (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0))
     vec_ok = false;
   if (T == 0) return LRAR_OK;
+  {
+    Regions R;
+    add_sources(R, p.src, n, T, d, esize(io), "src");
+    if (n > 0) R.input(span_region(q, static_cast<int64_t>(r) * 4, "q"));
+    R.input(span_region(m, T * 4, "m"));
+    R.input(span_region(l, T * 4, "l"));
+    R.input(rows_region(acc, T, acc_ld, d, esize(acc_dtype), "acc"));
+    R.output(rows_region(out, T, out_ld, d, esize(io), "out"));
+    R.output(span_region(m_out, T * 4, "m_out"));
+    R.output(span_region(l_out, T * 4, "l_out"));
+    st = check_disjoint(fn, R);
+    if (st != LRAR_OK) return st;
+  }
   p.n = n;
   p.d = d;
   p.r = r;
@@ -388,22 +514,6 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
     return fail(LRAR_ERR_INVALID, "%s: null m, l, acc, o, b_out, q or out", fn);
   if (m_out != nullptr && m_out == l_out)
     return fail(LRAR_ERR_INVALID, "%s: m_out and l_out alias", fn);
-  const size_t es = esize(io);
-  // b_out may replace b or o in place (same start and row stride), but overlap nothing else;
-  // out overlaps none of the row buffers.
-  const auto same = [](const void* x, int64_t xl, const void* y, int64_t yl) {
-    return x == y && xl == yl;
-  };
-  if (rows_overlap(b_out, b_out_ld, o, o_ld, T, d, es, es) && !same(b_out, b_out_ld, o, o_ld))
-    return fail(LRAR_ERR_INVALID, "%s: b_out partly overlaps o", fn);
-  if (rows_overlap(b_out, b_out_ld, b, b_ld, T, d, es, es) && !same(b_out, b_out_ld, b, b_ld))
-    return fail(LRAR_ERR_INVALID, "%s: b_out partly overlaps b", fn);
-  if (rows_overlap(out, out_ld, o, o_ld, T, d, es, es) ||
-      rows_overlap(out, out_ld, b, b_ld, T, d, es, es) ||
-      rows_overlap(out, out_ld, b_out, b_out_ld, T, d, es, es))
-    return fail(LRAR_ERR_INVALID, "%s: out overlaps b, o or b_out", fn);
-  if (rows_overlap(acc, acc_ld, b_out, b_out_ld, T, d, esize(acc_dtype), es))
-    return fail(LRAR_ERR_INVALID, "%s: acc overlaps b_out", fn);
   const int vec = vec_of(io);
   bool vec_ok = d % vec == 0;
   for (const auto& [ptr, ld] : {std::pair<const void*, int64_t>{o, o_ld}, {b, b_ld},
@@ -413,10 +523,29 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
   if ((esize(acc_dtype) * vec) % 16 == 0 && (!aligned16(acc) || acc_ld % acc_elems_per_16 != 0))
     vec_ok = false;
   const int use_vec = vec_ok ? vec : 1;
-  if (!row_fits_tile(d, use_vec))
-    return fail(LRAR_ERR_UNSUPPORTED, "%s: the fused update holds a whole row in registers; "
-                "d = %d is too wide on this path", fn, d);
   if (T == 0) return LRAR_OK;
+  {
+    // b_out may replace b or o in place (same start and row stride) but overlap nothing else
+    const size_t es = esize(io);
+    Regions R;
+    Region rb = rows_region(b, T, b_ld, d, es, "b");
+    Region ro = rows_region(o, T, o_ld, d, es, "o");
+    rb.inplace = ro.inplace = true;
+    R.input(rb);
+    R.input(ro);
+    R.input(span_region(q, static_cast<int64_t>(r) * 4, "q"));
+    R.input(span_region(m, T * 4, "m"));
+    R.input(span_region(l, T * 4, "l"));
+    R.input(rows_region(acc, T, acc_ld, d, esize(acc_dtype), "acc"));
+    Region rbo = rows_region(b_out, T, b_out_ld, d, es, "b_out");
+    rbo.inplace = true;
+    R.output(rbo);
+    R.output(rows_region(out, T, out_ld, d, es, "out"));
+    R.output(span_region(m_out, T * 4, "m_out"));
+    R.output(span_region(l_out, T * 4, "l_out"));
+    lrar_status st2 = check_disjoint(fn, R);
+    if (st2 != LRAR_OK) return st2;
+  }
   lrar::ReadParams p;
   std::memset(&p, 0, sizeof(p));
   p.src.ptr[0] = o;
@@ -439,9 +568,21 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
   p.b_prev_ld = b_ld;
   p.b_out = b_out;
   p.b_out_ld = b_out_ld;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!row_fits_tile(d, use_vec)) {
+    // rows too wide for a register tile: b_out = b + o first, then the merge reads b_out
+    hipError_t e = lrar::launch_add_rows(b, b_ld, o, o_ld, b_out, b_out_ld, T, d, io == LRAR_BF16,
+                                         use_vec, hs);
+    if (e == hipSuccess) {
+      p.src.ptr[0] = b_out;
+      p.src.ld[0] = b_out_ld;
+      e = lrar::launch_read(p, lrar::ReadKind::kMerge, io == LRAR_BF16, use_vec,
+                            acc_dtype == LRAR_BF16, hs);
+    }
+    return device_status(e, fn);
+  }
   return device_status(lrar::launch_tile(p, lrar::ReadKind::kMergeAccumulate, io == LRAR_BF16,
-                                         use_vec, acc_dtype == LRAR_BF16,
-                                         static_cast<hipStream_t>(stream)),
+                                         use_vec, acc_dtype == LRAR_BF16, hs),
                        fn);
 }
 
@@ -478,19 +619,15 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
     if (dsrc[i] == nullptr && T > 0) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] is null", fn, i);
     if (dsrc_ld[i] < d)
       return fail(LRAR_ERR_INVALID, "%s: dsrc_ld[%d] = %lld < d", fn, i, (long long)dsrc_ld[i]);
-    for (int j = 0; j < i; ++j)
-      if (dsrc[j] == dsrc[i]) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] and dsrc[%d] alias", fn, j, i);
-    if (overlaps_source(dsrc[i], p.src, n))
-      return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases a source", fn, i);
-    if (dsrc[i] == dout) return fail(LRAR_ERR_INVALID, "%s: dsrc[%d] aliases dout", fn, i);
     if (!aligned16(dsrc[i]) || dsrc_ld[i] % grad_per_16 != 0) vec_ok = false;
     p.dsrc.ptr[i] = dsrc[i];
     p.dsrc.ld[i] = dsrc_ld[i];
   }
   const int use_vec = vec_ok ? vec : 1;
   if (!lrar::backward_supported(d, r, use_vec))
-    return fail(LRAR_ERR_UNSUPPORTED, "%s: d = %d is too wide for the %s path", fn, d,
-                use_vec > 1 ? "vector" : "scalar");
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: the key of r = %d columns at d = %d spans more "
+                "chunks of 64 units than the %s path keeps query-gradient partials for", fn, r,
+                d, use_vec > 1 ? "vector" : "scalar");
   const size_t need = lrar::backward_workspace(T, r);
   if (T > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(LRAR_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -498,6 +635,18 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
   if (T > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
     return fail(LRAR_ERR_INVALID, "%s: workspace must be 8-byte aligned", fn);
   if (T == 0) return LRAR_OK;
+  {
+    Regions R;
+    add_sources(R, p.src, n, T, d, esize(io), "src");
+    R.input(span_region(q, static_cast<int64_t>(r) * 4, "q"));
+    R.input(rows_region(dout, T, dout_ld, d, esize(grad), "dout"));
+    for (int i = 0; i < n; ++i)
+      R.output(rows_region(dsrc[i], T, dsrc_ld[i], d, esize(grad), "dsrc", i));
+    R.output(span_region(dq, static_cast<int64_t>(r) * 4, "dq"));
+    R.output(span_region(workspace, static_cast<int64_t>(need), "workspace"));
+    st = check_disjoint(fn, R);
+    if (st != LRAR_OK) return st;
+  }
   p.n = n;
   p.d = d;
   p.r = r;

@@ -1,19 +1,23 @@
-// Backward of the depth-mix read, scalar-element path and the dq reduction (LR-AttnRes paper
-// App. B.3: Lemma 2 gives
-// dL/do_i = alpha_i g + alpha_i <g, o_i - h> grad z_i; Corollary 2.1 gives the slice-RMS
-// gradient grad z_i = P_r^T (q - z_i kbar_i / r) / rho_i; the query gradient follows from
-// z_i = q . kbar_i). Each source slot is an independent input, as in the paper.
+// Backward of the depth-mix read on one wavefront per token row, and the dq reduction
+// (LR-AttnRes paper App. B.3: Lemma 2 gives dL/do_i = alpha_i g + alpha_i <g, o_i - h> grad z_i;
+// Corollary 2.1 gives the slice-RMS gradient grad z_i = P_r^T (q - z_i kbar_i / r) / rho_i; the
+// query gradient follows from z_i = q . kbar_i). Each source slot is an independent input, as
+// in the paper. k_backward serves the rows the row-tile backward (lrar_backward_tile.hip) does
+// not: the scalar-element path (unaligned widths or strides) at any width, and vector rows wider
+// than a tile.
 //
 // k_backward, one wavefront per token row:
 //   1. key pass (float64): z_i, rho_i, alpha_i of every source, as in the forward;
-//   2. the row of g = dL/dh is loaded once into registers (float32);
-//   3. s_i = <g, o_i> over all d (float64 sums of exact products); then
+//   2. s_i = <g, o_i> over all d (float64 sums of exact products), streaming g = dL/dh and the
+//      source rows in column chunks (g is read again from the cache for every source); then
 //      dz_i = alpha_i (s_i - sum_j alpha_j s_j), which equals alpha_i <g, o_i - h>;
-//   4. dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns,
+//   3. dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns,
 //      optionally added to the existing gradient, written in the gradient type (float32, or
 //      bf16 rounded to nearest even once after the optional addition);
-//   5. dz_i k_i / rho_i is accumulated into per-lane dq partials kept in registers across
-//      all rows of the wave.
+//   4. dz_i k_i / rho_i is accumulated into per-lane dq partials kept in registers across all
+//      rows of the wave. Only the key's columns have partials: the key window is the TU chunks
+//      of 64 units from the chunk that holds the key's first unit (TU <= 64 on the element
+//      path, <= 8 on the vector path), which bounds the key width this kernel serves.
 // At the end the four waves of a workgroup combine their dq partials through LDS in a fixed
 // order and write one float64 partial per workgroup; two small kernels then sum those
 // partials in a fixed order. The token sum of dq is therefore bitwise reproducible.
@@ -26,14 +30,17 @@ namespace lrar {
 namespace {
 constexpr int kBwdMaxBlocks = 2048;
 constexpr int kReduceGroups = 32;
+constexpr int kElemMaxWindow = 64;  // key-window chunks on the element path
+constexpr int kVecMaxWindow = 8;    // and on the vector path (VEC floats per slot)
+
+// First unit of the key window: the start of the 64-unit chunk holding the key's first unit.
+__host__ __device__ __forceinline__ int key_window_start(int d, int r, int vec) {
+  return (((d - r) / vec) / kWave) * kWave;
+}
 }  // namespace
 
-// NU: units per lane that cover a row. TU: how many of the last unit slots may hold key
-// columns (the host checks that no key unit falls below slot NU - TU).
-template <typename IO, typename GIO, int VEC, int NU, int TU>
+template <typename IO, typename GIO, int VEC, int TU>
 __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __restrict__ block_dq) {
-  constexpr int B = NU >= 4 ? 1 : (NU >= 2 ? 2 : 4);  // sources loaded together in the <g, o_i> pass
-  constexpr int K0 = NU - TU;        // first unit slot that may hold key columns
   __shared__ float lds[kWavesPerBlock][kWave * VEC];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -41,6 +48,7 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
   const int nur = (p.d + VEC - 1) / VEC;
   const int c0 = p.d - p.r;
   const int ub = c0 / VEC;
+  const int ws = key_window_start(p.d, p.r, VEC);
 
   float dqa[TU][VEC];
 #pragma unroll
@@ -56,58 +64,26 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
     const double m = wave_max((lane < p.n) ? z : -INFINITY);
     const double ex = (lane < p.n) ? exp(z - m) : 0.0;
     const double a = ex / wave_sum(ex);
-
-    // 2. upstream gradient row
-    float gr[NU][VEC];
     const GIO* grow = static_cast<const GIO*>(p.dout) + row * p.dout_ld;
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = lane + kWave * k;
-      if (u < nur) {
-        load_grad<GIO, VEC>(grow + u * VEC, gr[k]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) gr[k][e] = 0.f;
-      }
-    }
 
-    // 3. s_i = <g, o_i>, then dz_i
+    // 2. s_i = <g, o_i>, then dz_i
     double s_mine = 0.0;
-    for (int i = 0; i < p.n; i += B) {
-      const int nb = (p.n - i) < B ? (p.n - i) : B;
-      Unit<IO, VEC> un[B][NU];
+    for (int i = 0; i < p.n; ++i) {
+      const IO* orow = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
+      double part = 0.0;
+#pragma unroll 4
+      for (int u = lane; u < nur; u += kWave) {
+        float gv[VEC], x[VEC];
+        load_grad<GIO, VEC>(grow + u * VEC, gv);
+        Unit<IO, VEC> un;
+        un.load_cached(orow + u * VEC);
+        un.get(x);
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        if (b < nb) {
-          const IO* orow = static_cast<const IO*>(p.src.ptr[i + b]) + row * p.src.ld[i + b];
-#pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            const int u = lane + kWave * k;
-            if (u < nur) un[b][k].load_cached(orow + u * VEC); else un[b][k].zero();
-          }
-        }
+        for (int e = 0; e < VEC; ++e)
+          part = fma(static_cast<double>(gv[e]), static_cast<double>(x[e]), part);
       }
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        if (b < nb) {
-          double part = 0.0;
-#pragma unroll
-          for (int k = 0; k < NU; ++k) {
-            float x[VEC];
-            un[b][k].get(x);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              // keep the float64 copy of g local to this product (no hoisting out of the
-              // source loop, which would double g's register footprint)
-              float gv = gr[k][e];
-              asm volatile("" : "+v"(gv));
-              part = fma(static_cast<double>(gv), static_cast<double>(x[e]), part);
-            }
-          }
-          const double s = wave_sum(part);
-          if (lane == i + b) s_mine = s;
-        }
-      }
+      const double s = wave_sum(part);
+      if (lane == i) s_mine = s;
     }
     const double sbar = wave_sum((lane < p.n) ? a * s_mine : 0.0);
     const double dz = a * (s_mine - sbar);
@@ -115,37 +91,37 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
     const float c1f = static_cast<float>(dz / rho);                       // dz / rho
     const float c2f = static_cast<float>(dz * z / (p.r * rho * rho));     // dz z / (r rho^2)
 
-    // 4./5. source gradients and dq partials
+    // 3./4. source gradients and dq partials
     for (int i = 0; i < p.n; ++i) {
       const float ai = lane_f32(af, i);
       const float c1 = lane_f32(c1f, i);
       const float c2 = lane_f32(c2f, i);
       const IO* orow = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
       GIO* drow = static_cast<GIO*>(p.dsrc.ptr[i]) + row * p.dsrc.ld[i];
+      // columns before the key window: alpha_i g only
+#pragma unroll 2
+      for (int u = lane; u < ws; u += kWave) {
+        float v[VEC];
+        load_grad<GIO, VEC>(grow + u * VEC, v);
 #pragma unroll
-      for (int k = 0; k < K0; ++k) {
-        const int u = lane + kWave * k;
-        if (u < nur) {
-          float v[VEC];
+        for (int e = 0; e < VEC; ++e) v[e] *= ai;
+        if (p.accumulate) {
+          float old[VEC];
+          load_grad<GIO, VEC>(drow + u * VEC, old);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];
-          if (p.accumulate) {
-            float old[VEC];
-            load_grad<GIO, VEC>(drow + u * VEC, old);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] += old[e];
-          }
-          store_grad<GIO, VEC>(drow + u * VEC, v);
+          for (int e = 0; e < VEC; ++e) v[e] += old[e];
         }
+        store_grad<GIO, VEC>(drow + u * VEC, v);
       }
+      // the key window, one register slot per chunk
 #pragma unroll
       for (int t = 0; t < TU; ++t) {
-        const int k = K0 + t;
-        const int u = lane + kWave * k;
+        const int u = ws + kWave * t + lane;
         if (u < nur) {
           float v[VEC];
+          load_grad<GIO, VEC>(grow + u * VEC, v);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = ai * gr[k][e];
+          for (int e = 0; e < VEC; ++e) v[e] *= ai;
           if (u >= ub) {
             Unit<IO, VEC> un;
             un.load_cached(orow + u * VEC);
@@ -181,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
     for (int e = 0; e < VEC; ++e) lds[wave][lane * VEC + e] = dqa[t][e];
     __syncthreads();
     if (wave == 0) {
-      const int u = lane + kWave * (K0 + t);
+      const int u = ws + kWave * t + lane;
       if (u >= ub && u < nur) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -236,49 +212,33 @@ __global__ __launch_bounds__(kBlock) void k_dq_reduce2(const double* __restrict_
 
 namespace {
 
-template <int VEC>
-int units_per_lane(int d) {
-  const int nur = (d + VEC - 1) / VEC;
-  return (nur + kWave - 1) / kWave;
+// Key-window chunks this shape needs (see k_backward).
+int key_window_chunks(int d, int r, int vec) {
+  const int nur = (d + vec - 1) / vec;
+  return (nur - key_window_start(d, r, vec) + kWave - 1) / kWave;
 }
 
-// Smallest register window TU (among the built ones) that covers the key for this shape.
-int needed_tail_slots(int nu, int d, int r, int vec) {
-  const int ub = (d - r) / vec;
-  const int first_slot = ub / kWave;  // lanes' unit slots below this never reach the key
-  return nu - first_slot;
-}
-
-template <typename IO, typename GIO, int VEC, int NU>
-hipError_t launch_nu(const BwdParams& p, double* block_dq, int grid, int need, hipStream_t s) {
-  const dim3 g(grid), b(kBlock);
-  if (need <= 1 && NU >= 1) {
-    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, 1>), g, b, 0, s, p, block_dq);
-  } else if (need <= 2 && NU >= 2) {
-    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, (NU >= 2 ? 2 : NU)>), g, b, 0, s, p,
-                       block_dq);
-  } else if (need <= 4 && NU >= 4) {
-    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, (NU >= 4 ? 4 : NU)>), g, b, 0, s, p,
-                       block_dq);
-  } else {
-    hipLaunchKernelGGL((k_backward<IO, GIO, VEC, NU, NU>), g, b, 0, s, p, block_dq);
-  }
-  return hipGetLastError();
+template <typename IO, typename GIO, int VEC, int TU>
+void launch_tu(const BwdParams& p, double* block_dq, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_backward<IO, GIO, VEC, TU>), dim3(grid), dim3(kBlock), 0, s, p, block_dq);
 }
 
 template <typename IO, typename GIO, int VEC>
 hipError_t launch_bwd_t(const BwdParams& p, double* block_dq, int grid, hipStream_t s) {
-  const int nu = units_per_lane<VEC>(p.d);
-  const auto need = [&](int nu_b) { return needed_tail_slots(nu_b, p.d, p.r, VEC); };
-  if (nu <= 1) return launch_nu<IO, GIO, VEC, 1>(p, block_dq, grid, need(1), s);
-  if (nu <= 2) return launch_nu<IO, GIO, VEC, 2>(p, block_dq, grid, need(2), s);
-  if (nu <= 4) return launch_nu<IO, GIO, VEC, 4>(p, block_dq, grid, need(4), s);
-  if (nu <= 8) return launch_nu<IO, GIO, VEC, 8>(p, block_dq, grid, need(8), s);
-  if (nu <= 16) return launch_nu<IO, GIO, VEC, 16>(p, block_dq, grid, need(16), s);
-  if constexpr (VEC == 1) {
-    if (nu <= 32) return launch_nu<IO, GIO, VEC, 32>(p, block_dq, grid, need(32), s);
+  const int need = key_window_chunks(p.d, p.r, VEC);
+  if (need <= 1) launch_tu<IO, GIO, VEC, 1>(p, block_dq, grid, s);
+  else if (need <= 2) launch_tu<IO, GIO, VEC, 2>(p, block_dq, grid, s);
+  else if (need <= 4) launch_tu<IO, GIO, VEC, 4>(p, block_dq, grid, s);
+  else if (need <= 8) launch_tu<IO, GIO, VEC, 8>(p, block_dq, grid, s);
+  else if constexpr (VEC == 1) {
+    if (need <= 16) launch_tu<IO, GIO, VEC, 16>(p, block_dq, grid, s);
+    else if (need <= 32) launch_tu<IO, GIO, VEC, 32>(p, block_dq, grid, s);
+    else if (need <= 64) launch_tu<IO, GIO, VEC, 64>(p, block_dq, grid, s);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -288,10 +248,14 @@ int backward_grid(int64_t T) {
   return static_cast<int>(blocks < kBwdMaxBlocks ? (blocks > 0 ? blocks : 1) : kBwdMaxBlocks);
 }
 
-bool backward_supported(int d, int r, int vec) {
+bool backward_uses_tile(int d, int vec) {
   const int nur = (d + vec - 1) / vec;
-  const int nu = (nur + kWave - 1) / kWave;
-  return vec > 1 ? nu <= backward_tile_max_chunks() : nu <= 32;
+  return vec > 1 && (nur + kWave - 1) / kWave <= backward_tile_max_chunks();
+}
+
+bool backward_supported(int d, int r, int vec) {
+  if (backward_uses_tile(d, vec)) return true;
+  return key_window_chunks(d, r, vec) <= (vec > 1 ? kVecMaxWindow : kElemMaxWindow);
 }
 
 // Workspace: [grid][r] float64 workgroup partials, then [kReduceGroups][r] float64.
@@ -308,15 +272,23 @@ hipError_t launch_backward(const BwdParams& p, int io_bf16, int grad_bf16, int v
   double* block_dq = static_cast<double*>(p.workspace);
   double* level2 = block_dq + static_cast<int64_t>(max_grid) * p.r;
   hipError_t e;
-  if (vec > 1) {
-    // the vector path runs on row tiles (lrar_backward_tile.hip)
+  if (backward_uses_tile(p.d, vec)) {
+    // vector rows that fit a tile run on row tiles (lrar_backward_tile.hip)
     e = launch_backward_tile(p, io_bf16, grad_bf16, block_dq, max_grid, &grid, s);
   } else if (io_bf16) {
-    e = grad_bf16 ? launch_bwd_t<bf16_bits, bf16_bits, 1>(p, block_dq, grid, s)
-                  : launch_bwd_t<bf16_bits, float, 1>(p, block_dq, grid, s);
+    if (vec > 1)
+      e = grad_bf16 ? launch_bwd_t<bf16_bits, bf16_bits, 8>(p, block_dq, grid, s)
+                    : launch_bwd_t<bf16_bits, float, 8>(p, block_dq, grid, s);
+    else
+      e = grad_bf16 ? launch_bwd_t<bf16_bits, bf16_bits, 1>(p, block_dq, grid, s)
+                    : launch_bwd_t<bf16_bits, float, 1>(p, block_dq, grid, s);
   } else {
-    e = grad_bf16 ? launch_bwd_t<float, bf16_bits, 1>(p, block_dq, grid, s)
-                  : launch_bwd_t<float, float, 1>(p, block_dq, grid, s);
+    if (vec > 1)
+      e = grad_bf16 ? launch_bwd_t<float, bf16_bits, 4>(p, block_dq, grid, s)
+                    : launch_bwd_t<float, float, 4>(p, block_dq, grid, s);
+    else
+      e = grad_bf16 ? launch_bwd_t<float, bf16_bits, 1>(p, block_dq, grid, s)
+                    : launch_bwd_t<float, float, 1>(p, block_dq, grid, s);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dq_reduce1, dim3((p.r + kWave - 1) / kWave, kReduceGroups), dim3(kBlock), 0, s,

@@ -610,57 +610,91 @@ __device__ __forceinline__ double q_at(const float* __restrict__ q, int col, int
   return col >= c0 ? static_cast<double>(q[col - c0]) : 0.0;
 }
 
-// Slice scores of the n sources of one row. On return lane i (< n) holds z_i and rho_i of
-// source i; other lanes hold unspecified values. float64 throughout: each bf16 x fp32 product
-// is exact in float64, so the only rounding is in the sums.
-template <typename IO, int VEC>
+// How a one-wave-per-row kernel forms each source's key and its RMS.
+enum RowKeyMode : int {
+  kKeySlice = 0,    // the last r columns of the row, RMS over those r columns
+  kKeyFullRms = 1,  // the last r columns of the row, RMS over the whole row (the control)
+  kKeySeparate = 2  // the first r columns of the source's own key row, RMS over those
+};
+
+// Scores of the n sources of one row. On return lane i (< n) holds z_i and rho_i of source i;
+// other lanes hold unspecified values. float64 throughout: each bf16 x fp32 product is exact in
+// float64, so the only rounding is in the sums. The lanes are cut into groups, one source per
+// group per iteration; a group walks its source's key units (KM = kKeySlice), every unit of the
+// row (kKeyFullRms: the square sum covers the row, the dot product the key columns), or the
+// elements of the source's key row K->ptr[i] (kKeySeparate: single elements, so key rows need
+// no alignment).
+template <typename IO, int VEC, int KM = kKeySlice>
 __device__ __forceinline__ void row_scores(const SrcList& S, int n, int64_t row, int d, int r,
                                            double eps, const float* __restrict__ q, int lane,
-                                           double& z_mine, double& rho_mine) {
+                                           double& z_mine, double& rho_mine,
+                                           const SrcList* K = nullptr) {
   const KeyGeom g = key_geom<VEC>(d, r);
-  const int slot = lane / g.group;
-  const int sub = lane % g.group;
-  const int iters = (n + g.per_it - 1) / g.per_it;
+  // the range each group walks, in units of VEC elements (single elements for separate keys)
+  const int w_begin = KM == kKeySlice ? g.ub : 0;
+  const int w_end = KM == kKeySeparate ? r : g.nur;
+  int group = 1;
+  while (group < w_end - w_begin && group < kWave) group <<= 1;
+  const int per_it = kWave / group;
+  const int slot = lane / group;
+  const int sub = lane % group;
+  const int iters = (n + per_it - 1) / per_it;
+  const int nrm = KM == kKeyFullRms ? d : r;
   z_mine = 0.0;
   rho_mine = 1.0;
   for (int it = 0; it < iters; ++it) {
     // The source of this lane's group; the pointer table is indexed with a uniform index
     // per candidate and selected per lane, so the table stays in scalar registers.
-    const int i = it * g.per_it + slot;
+    const int i = it * per_it + slot;
     const IO* base = nullptr;
     int64_t ld = 0;
-    for (int c = 0; c < g.per_it; ++c) {
-      const int ic = it * g.per_it + c;
+    for (int c = 0; c < per_it; ++c) {
+      const int ic = it * per_it + c;
       if (ic < n && c == slot) {
-        base = static_cast<const IO*>(S.ptr[ic]);
-        ld = S.ld[ic];
+        if constexpr (KM == kKeySeparate) {
+          base = static_cast<const IO*>(K->ptr[ic]);
+          ld = K->ld[ic];
+        } else {
+          base = static_cast<const IO*>(S.ptr[ic]);
+          ld = S.ld[ic];
+        }
       }
     }
     double dot = 0.0, ss = 0.0;
     if (i < n) {
       const IO* rowp = base + row * ld;
-      for (int u = g.ub + sub; u < g.nur; u += g.group) {
-        Unit<IO, VEC> un;
-        un.load_cached(rowp + u * VEC);
-        float x[VEC];
-        un.get(x);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int col = u * VEC + e;
-          const double k = (col >= g.c0) ? static_cast<double>(x[e]) : 0.0;
-          dot = fma(q_at(q, col, g.c0), k, dot);
+      if constexpr (KM == kKeySeparate) {
+        for (int j = w_begin + sub; j < w_end; j += group) {
+          const double k = static_cast<double>(to_f32<IO>(rowp[j]));
+          dot = fma(static_cast<double>(q[j]), k, dot);
           ss = fma(k, k, ss);
+        }
+      } else {
+        for (int u = w_begin + sub; u < w_end; u += group) {
+          Unit<IO, VEC> un;
+          un.load_cached(rowp + u * VEC);
+          float x[VEC];
+          un.get(x);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const int col = u * VEC + e;
+            const double v = static_cast<double>(x[e]);
+            const double k = (col >= g.c0) ? v : 0.0;
+            dot = fma(q_at(q, col, g.c0), k, dot);
+            // the control's RMS covers every column of the row, the slice RMS the key alone
+            ss = KM == kKeyFullRms ? fma(v, v, ss) : fma(k, k, ss);
+          }
         }
       }
     }
-    dot = group_sum(dot, g.group);
-    ss = group_sum(ss, g.group);
-    const double rho = sqrt(ss / r + eps);
+    dot = group_sum(dot, group);
+    ss = group_sum(ss, group);
+    const double rho = sqrt(ss / nrm + eps);
     const double z = dot / rho;
-    const int src_lane = (lane % g.per_it) * g.group;
+    const int src_lane = (lane % per_it) * group;
     const double zt = __shfl(z, src_lane, kWave);
     const double rt = __shfl(rho, src_lane, kWave);
-    if (lane / g.per_it == it) {
+    if (lane / per_it == it) {
       z_mine = zt;
       rho_mine = rt;
     }

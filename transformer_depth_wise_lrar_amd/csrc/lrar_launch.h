@@ -82,8 +82,15 @@ struct BwdParams {
 };
 
 // Column-chunked two-pass read (any width; also the merge when a row does not fit a tile).
+// key_mode is a RowKeyMode: the sliced key, the full-width-RMS control or separate key rows
+// (keys, only for kKeySeparate); the merge (kind kMerge) takes the sliced key.
 hipError_t launch_read(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
-                       hipStream_t s);
+                       hipStream_t s, int key_mode = kKeySlice, const SrcList* keys = nullptr);
+// b_out = b + o on [T, d] rows of the element type (b may be null), for the fused Phase-2
+// update of rows too wide for a tile.
+hipError_t launch_add_rows(const void* b, int64_t b_ld, const void* o, int64_t o_ld, void* bout,
+                           int64_t bout_ld, int64_t T, int d, int io_bf16, int vec,
+                           hipStream_t s);
 // Register-tile read (online, two-pass or merge) for rows of at most tile_max_chunks() chunks
 // of 64 units.
 hipError_t launch_tile(const ReadParams& p, ReadKind kind, int io_bf16, int vec, int acc_bf16,
