@@ -256,6 +256,33 @@ class Oracle:
         return self._bwd(self.lib.orc_backward_fullrms, srcs, q, dout, r, eps)
 
 
+def block_ends(M: int, N: int) -> list:
+    """Last write of each of the N blocks over M sub-layer writes: ceil(M j / N), j = 1..N
+    (the author's explainer, "The mechanism in PyTorch-style code", block-end rule)."""
+    return [-(-M * j // N) for j in range(1, N + 1)]
+
+
+def block_sources(M: int, N: int, w: int) -> list:
+    """The sources a read sees after write w (0 <= w <= M) under block routing, each as the list
+    of writes summed into it (0 = the embedding): the embedding, every completed block as one
+    sum, and the writes of the unfinished block if there are any (the explainer, "Full history
+    or a few block summaries"; an empty partial sum is not a source). With N = M every write is
+    its own source: full routing."""
+    if not (0 <= w <= M and 1 <= N <= M):
+        raise ValueError("need 0 <= w <= M and 1 <= N <= M")
+    out = [[0]]
+    start = 1
+    for end in block_ends(M, N):
+        if end <= w:
+            out.append(list(range(start, end + 1)))
+            start = end + 1
+        else:
+            break
+    if start <= w:
+        out.append(list(range(start, w + 1)))
+    return out
+
+
 _default = None
 _lock = threading.Lock()
 

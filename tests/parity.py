@@ -3,9 +3,13 @@
 The bars (element by element):
   * weights alpha: |alpha - alpha_ref| <= 1e-6;
   * fp32 output: |y - h_ref| <= 1e-5 * max|v| with v the source values of the read;
-  * bf16 output: |y - h_ref| <= ulp_bf16(h_ref) + (n + 3) * 2^-24 * sum_i alpha_i |o_ij|.
-    The first term is one bf16 ulp of the value; the second is the float32 accumulation
-    slack of a sum of n products (it only matters under cancellation).
+  * bf16 output: |y - h_ref| <= ulp_bf16(h_ref) + (n + 3 + 2k) * 2^-24 * sum_i alpha_i |o_ij|.
+    The first term is one bf16 ulp of the value; the second bounds the float32 arithmetic
+    before that rounding (it only matters under cancellation): n roundings of the n fused
+    multiply-adds, one of each weight's float32 rounding, one of 1/l and one of the final
+    scaling by it (the two-pass read has neither of the last two), and two for each of the k
+    times the online fold moves its reference and rescales the accumulator (the scale factor's
+    rounding and the product's). k is counted per row from the oracle's weights.
   * Phase-1 statistics: m within one float32 rounding; l and acc within the float32
     accumulation bound after rescaling the oracle to the kernel's m.
   * backward: dsrc_i within 1e-5 * max|dsrc_i ref| per source (plus one bf16 ulp of the
@@ -38,6 +42,25 @@ def _nan_equal_mask(a, b):
     return np.isnan(a) & np.isnan(b)
 
 
+LAZY_RESCALE = 8.0  # the online fold moves its reference when a score passes it by more
+
+
+def lazy_rescales(alpha_ref):
+    """Per row, how often an online-softmax fold over the sources in order rescales its
+    accumulator after the first source: a score more than LAZY_RESCALE above the reference
+    becomes the new reference. Score differences are read from the oracle's weights
+    (z_i - z_j = ln(alpha_i / alpha_j)); a margin makes borderline rows count (more slack)."""
+    with np.errstate(divide="ignore"):
+        lz = np.log(np.asarray(alpha_ref, dtype=np.float64))
+    k = np.zeros(lz.shape[0])
+    ref = lz[:, 0].copy()
+    for i in range(1, lz.shape[1]):
+        grow = lz[:, i] > ref + LAZY_RESCALE - 1e-6
+        k += grow
+        ref = np.where(grow, lz[:, i], ref)
+    return k
+
+
 def assert_read(y64, h_ref, alpha_ref, srcs64, io, where="read"):
     """y64: kernel output decoded to float64 [T, d]; h_ref, alpha_ref from the oracle."""
     n = len(srcs64)
@@ -45,7 +68,8 @@ def assert_read(y64, h_ref, alpha_ref, srcs64, io, where="read"):
         mag = np.zeros_like(h_ref)
         for i in range(n):
             mag += alpha_ref[:, i:i + 1] * np.abs(srcs64[i])
-        tol = ulp_bf16(h_ref) + (n + 3) * U * mag
+        slack = (n + 3 + 2 * lazy_rescales(alpha_ref))[:, None]
+        tol = ulp_bf16(h_ref) + slack * U * mag
     else:
         vmax = max(float(np.nanmax(np.abs(s))) for s in srcs64)
         tol = np.full_like(h_ref, 1e-5 * vmax)
@@ -81,16 +105,19 @@ def assert_stats(m_g, l_g, acc_g, m_o, l_o, acc_o, z_o, srcs64, acc_io, where="s
 
 def assert_merge(y64, h_ref, w_prior, acc_norm, w_extra, extra64, io, where="merge"):
     """h = w_prior * (acc / l) + sum_b w_b o_b; w_* from the oracle (w_prior [T], w_extra
-    [T, n_extra]); acc_norm = acc / l [T, d]."""
+    [T, n_extra]); acc_norm = acc / l [T, d]. The slack counts, besides the read's terms, the
+    stored accumulator's scaling, and one possible rescale per extra source (the fold starts
+    from the Phase-1 maximum)."""
     mag = w_prior[:, None] * np.abs(acc_norm)
     for i, b in enumerate(extra64):
         mag += w_extra[:, i:i + 1] * np.abs(b)
     n = len(extra64) + 1
+    slack = n + 4 + 2 * len(extra64)
     if io == "bf16":
-        tol = ulp_bf16(h_ref) + (n + 4) * U * mag
+        tol = ulp_bf16(h_ref) + slack * U * mag
     else:
         vmax = max([float(np.abs(acc_norm).max())] + [float(np.abs(b).max()) for b in extra64])
-        tol = np.full_like(h_ref, 1e-5 * vmax) + (n + 4) * U * mag
+        tol = np.full_like(h_ref, 1e-5 * vmax) + slack * U * mag
     err = np.abs(y64 - h_ref)
     err[_nan_equal_mask(y64, h_ref)] = 0.0
     _report(err, tol, where)

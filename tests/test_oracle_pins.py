@@ -55,3 +55,31 @@ def test_pins_module_lists_every_pin():
     names = [p.__name__ for p in ALL_PINS]
     assert len(names) == len(set(names)) >= 15
     assert all(callable(getattr(oracle_pins, n)) for n in names)
+
+
+def test_block_schedule_golden():
+    """The block-routing schedule against the explainer's six-write example (its entries after
+    writes three and four; tests/golden/block_schedule_example.json), the block-end rule, full
+    routing as N = M, and the production-width reading of 93 writes in 8 blocks."""
+    import json
+    import os
+
+    import oracle
+
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "block_schedule_example.json")) as f:
+        g = json.load(f)
+    M, N = g["M"], g["N"]
+    assert oracle.block_ends(M, N) == g["expected_ends"]
+    for w, want in g["expected_sources_after_write"].items():
+        assert oracle.block_sources(M, N, int(w)) == want, w
+    # full routing (every write its own block): the read after write w sees w + 1 sources
+    assert all(oracle.block_sources(48, 48, w) == [[i] for i in range(w + 1)] for w in range(49))
+    # 93 writes in 8 blocks: blocks of 11-12 writes, at most N + 1 = 9 sources at any read
+    assert oracle.block_ends(93, 8) == [12, 24, 35, 47, 59, 70, 82, 93]
+    counts = [len(oracle.block_sources(93, 8, w)) for w in range(94)]
+    assert max(counts) == 9 and counts[93] == 9 and counts[12] == 2
+    # every write lands in exactly one source at every read
+    for w in range(94):
+        flat = sorted(i for s in oracle.block_sources(93, 8, w) for i in s)
+        assert flat == list(range(w + 1))

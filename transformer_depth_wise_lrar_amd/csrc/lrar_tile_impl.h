@@ -556,16 +556,8 @@ int device_cus() {
 // Rows per tile and prefetch depth for NU units per lane: the tile's accumulators and its
 // PF + 1 stages must leave room for several waves per SIMD, and the loads in flight
 // (waves x PF tiles) must cover the HBM latency.
-#ifndef LRAR_TILE_R
 constexpr int tile_rows(int nu) { return nu <= 1 ? 4 : (nu <= 2 ? 2 : 1); }
-#else
-constexpr int tile_rows(int nu) { return nu <= 4 ? LRAR_TILE_R : 1; }
-#endif
-#ifndef LRAR_TILE_PF
 constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
-#else
-constexpr int tile_prefetch(int nu) { return nu <= 4 ? LRAR_TILE_PF : 1; }
-#endif
 
 // Reads of many sources keep one more source in flight: three sources ahead measured 8 %
 // (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two for spread keys, in
