@@ -1,6 +1,7 @@
 """Throughput of the LR-AttnRes depth-mix read on one MI355X (gfx950).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
+                    [--rows NAME,...] [--fixed-reps K]
 
 One step is the depth mix of one forward pass of the full-routing model shape of the
 LR-AttnRes paper's 0.5B runs (§4.1: d = 1024, 24 layers = 48 sub-layer writes, so 49
@@ -18,8 +19,13 @@ Output: ONE JSON line on stdout. `value` is tokens/s per read site averaged over
 sites (tokens x sites / total read time); `roofline` prices the read kernel's algorithmic
 bytes, e (n + 1) d per token at a site with n sources, against MI355X's 8 TB/s HBM peak;
 `rows` reports the other hot-path steps (block routing at d = 2048, production width
-d = 7168 single-pass and two-phase, and the backward) on their own workloads;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+d = 7168 single-pass and two-phase, and the backward) on their own workloads, each timed
+until two consecutive windows of six launches agree (the LR-AttnRes paper's App. I timing
+rule: coefficient of variation <= 1 % in each window, medians within 0.5 %, at most 30
+windows); `rooflines_wide` prices the bf16 forward at d >= 2048 the same way as `roofline`;
+`ceilings` holds a plain streaming read and copy measured the same way, and the write rate
+and per-read mix ceilings derived from them; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -36,6 +42,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+WINDOW = 6                      # launches per timing window (the pages' stop rule)
+MAX_WINDOWS = 30
+CV_MAX = 0.01
+DRIFT_MAX = 0.005
+HOST_THREADS_MAX = 16           # the host CPU share of one GPU on the measurement boxes
 EVICT_BYTES = 256 << 20         # copied per eviction: 256 MiB read + 256 MiB written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "transformer_depth_wise_lrar_amd", "csrc")
@@ -170,23 +181,61 @@ def headline(torch, lrar, args, ev):
 # ---- the other hot-path steps on their own workloads --------------------------------------------
 
 class Timing(float):
-    """A median launch time in ms that also carries the coefficient of variation of the
-    timed launches it was taken from."""
+    """A launch time in ms (the median of the last two timing windows) that also carries the
+    coefficient of variation of those launches, the mean, how many windows were run and
+    whether the stop rule was met."""
     cv = None
+    mean = None
+    windows = None
+    converged = None
 
 
-def time_calls(torch, ev, fn, reps, warm=2):
+def _cv(xs):
+    m = sum(xs) / len(xs)
+    return (sum((x - m) ** 2 for x in xs) / len(xs)) ** 0.5 / m
+
+
+def _median(xs):
+    v = sorted(xs)
+    k = len(v) // 2
+    return v[k] if len(v) % 2 else 0.5 * (v[k - 1] + v[k])
+
+
+FIXED_REPS = None  # set by --fixed-reps: time exactly that many launches (profiling runs)
+
+
+def time_calls(torch, ev, fn, reps=None, warm=3):
+    """Times fn launch by launch (an eviction before each) in windows of WINDOW launches until
+    two consecutive windows each have CV <= 1 % and their medians differ by <= 0.5 %, or
+    MAX_WINDOWS windows have run."""
     tm = Timer(torch)
     for _ in range(warm):
         ev()
         fn()
-    for _ in range(reps):
-        ev()
-        tm.run(fn)
-    ms = sorted(tm.collect_ms())
-    t = Timing(ms[len(ms) // 2])
-    mean = sum(ms) / len(ms)
-    t.cv = (sum((x - mean) ** 2 for x in ms) / len(ms)) ** 0.5 / mean
+    if FIXED_REPS is not None:
+        for _ in range(FIXED_REPS):
+            ev()
+            tm.run(fn)
+        ms = tm.collect_ms()
+        t = Timing(_median(ms))
+        t.cv, t.mean, t.windows, t.converged = _cv(ms), sum(ms) / len(ms), 0, False
+        return t
+    wins = []
+    converged = False
+    for _ in range(MAX_WINDOWS):
+        for _ in range(WINDOW):
+            ev()
+            tm.run(fn)
+        wins.append(tm.collect_ms())
+        if len(wins) >= 2:
+            a, b = wins[-2], wins[-1]
+            ma, mb = _median(a), _median(b)
+            if _cv(a) <= CV_MAX and _cv(b) <= CV_MAX and abs(mb - ma) <= DRIFT_MAX * ma:
+                converged = True
+                break
+    last = wins[-2] + wins[-1] if len(wins) >= 2 else wins[-1]
+    t = Timing(_median(last))
+    t.cv, t.mean, t.windows, t.converged = _cv(last), sum(last) / len(last), len(wins), converged
     return t
 
 
@@ -200,6 +249,11 @@ def row_entry(ms, nbytes, tokens=None):
         e["tokens_per_s"] = round(tokens / (ms * 1e-3), 1)
     if getattr(ms, "cv", None) is not None:
         e["cv"] = round(ms.cv, 4)
+    if getattr(ms, "windows", None):
+        e["windows"] = ms.windows
+        e["converged"] = ms.converged
+    if getattr(ms, "mean", None) is not None:
+        e["mean_ms"] = round(float(ms.mean), 5)
     return e
 
 
@@ -215,7 +269,7 @@ def rows_block_routing(torch, lrar, ev, reps):
         for n in (9, 10):
             for var in ("two_pass", "online"):
                 ms = time_calls(torch, ev, lrar.lrar_forward(
-                    srcs[:n], q, r, 1e-6, out=out, variant=var, prepare=True), reps)
+                    srcs[:n], q, r, 1e-6, out=out, variant=var, prepare=True))
                 res[f"r{r}_n{n}_{var}"] = row_entry(ms, fwd_bytes(T, d, n, 2), T)
     del srcs, out
     return res
@@ -234,7 +288,7 @@ def rows_production(torch, lrar, ev, reps):
         q = gen_queries(torch, 1, r, seed=3001 + r)[0]
         for var in ("two_pass", "online"):
             ms = time_calls(torch, ev, lrar.lrar_forward(
-                srcs, q, r, 1e-6, out=out, variant=var, prepare=True), reps)
+                srcs, q, r, 1e-6, out=out, variant=var, prepare=True))
             res[f"single_pass_r{r}_n9_{var}"] = row_entry(ms, fwd_bytes(T, d, 9, 2), T)
     r = 1792
     qs = gen_queries(torch, nq, r, seed=3100)
@@ -243,18 +297,18 @@ def rows_production(torch, lrar, ev, reps):
         l = torch.empty((nq, T), dtype=torch.float32, device="cuda")
         acc = torch.empty((nq, T, d), dtype=acc_dt, device="cuda")
         ms1 = time_calls(torch, ev, lrar.lrar_forward_stats(
-            srcs[:8], qs, r, 1e-6, m=m, l=l, acc=acc, prepare=True), reps)
+            srcs[:8], qs, r, 1e-6, m=m, l=l, acc=acc, prepare=True))
         b1 = 2 * 8 * d * T + nq * (ae * d + 8) * T
         res[f"phase1_r{r}_ninter8_q{nq}_acc{acc_name}"] = row_entry(ms1, b1, T * nq)
         ms2 = time_calls(torch, ev, lrar.lrar_merge(
-            m[0], l[0], acc[0], srcs[8:9], qs[0], r, 1e-6, out=out, prepare=True), reps)
+            m[0], l[0], acc[0], srcs[8:9], qs[0], r, 1e-6, out=out, prepare=True))
         b2 = (ae * d + 8 + 2 * d + 2 * d) * T
         res[f"phase2_r{r}_acc{acc_name}"] = row_entry(ms2, b2, T)
         # the same site with the partial-sum update fused in: b' = b + o is written and merged
         bnew = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
         ms3 = time_calls(torch, ev, lrar.lrar_merge_accumulate(
             m[0], l[0], acc[0], srcs[8], srcs[7], qs[0], r, 1e-6, out=out, b_out=bnew,
-            prepare=True), reps)
+            prepare=True))
         b3 = (ae * d + 8 + 2 * d + 2 * d + 2 * d + 2 * d) * T
         res[f"phase2_fused_update_r{r}_acc{acc_name}"] = row_entry(ms3, b3, T)
         del m, l, acc, bnew
@@ -276,7 +330,7 @@ def rows_backward(torch, lrar, ev, reps):
     ws = torch.empty((lrar.lrar_backward_workspace_size(T, d, r, n),), dtype=torch.uint8,
                      device="cuda")
     ms = time_calls(torch, ev, lrar.lrar_backward(
-        srcs, q, dout, r, 1e-6, dsrc=dsrc, dq=dq, workspace=ws, prepare=True), reps)
+        srcs, q, dout, r, 1e-6, dsrc=dsrc, dq=dq, workspace=ws, prepare=True))
     nbytes = (2 * n * d + 4 * d + 4 * n * d) * T + 4 * r
     res = {f"backward_r{r}_n{n}": row_entry(ms, nbytes, T)}
     del dsrc
@@ -284,7 +338,7 @@ def rows_backward(torch, lrar, ev, reps):
     dout16 = dout.to(torch.bfloat16)
     dsrc16 = [torch.empty((T, d), dtype=torch.bfloat16, device="cuda") for _ in range(n)]
     ms16 = time_calls(torch, ev, lrar.lrar_backward_grad(
-        srcs, q, dout16, r, 1e-6, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True), reps)
+        srcs, q, dout16, r, 1e-6, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True))
     res[f"backward_bf16_grads_r{r}_n{n}"] = row_entry(
         ms16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r, T)
     del srcs, dsrc16, dout, dout16
@@ -303,14 +357,14 @@ def rows_read_variants(torch, lrar, ev, reps):
     q = gen_queries(torch, 1, r, seed=5001)[0]
     for n in (13, 49):
         ms = time_calls(torch, ev, lrar.lrar_forward_fullrms(
-            srcs[:n], q, r, 1e-6, out=out, prepare=True), reps)
+            srcs[:n], q, r, 1e-6, out=out, prepare=True))
         res[f"fullrms_r{r}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2), T)
     for rk in (32, 64):
         keys = gen_sources(torch, 49, T, rk, (0.5, 2.0), seed=5100 + rk, dtype=torch.bfloat16)
         qk = gen_queries(torch, 1, rk, seed=5002 + rk)[0]
         for n in (13, 49):
             ms = time_calls(torch, ev, lrar.lrar_forward_keys(
-                srcs[:n], keys[:n], qk, rk, 1e-6, out=out, prepare=True), reps)
+                srcs[:n], keys[:n], qk, rk, 1e-6, out=out, prepare=True))
             res[f"keys_r{rk}_n{n}"] = row_entry(ms, fwd_bytes(T, d, n, 2) + 2 * n * rk * T, T)
         del keys
     del srcs, out
@@ -319,9 +373,21 @@ def rows_read_variants(torch, lrar, ev, reps):
 
 # ---- the CPU baseline: the oracle on a bounded sample -------------------------------------------
 
-def cpu_baseline(torch, budget_s=12.0):
-    """The fp64 oracle on the first R rows of the headline workload, all 49 sites, run on
-    host threads over row chunks (the oracle itself is single-threaded)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(torch, budget_s=15.0):
+    """The fp64 oracle on the first R rows of the headline workload, all 49 sites, run on the
+    host cores this process may use (the oracle itself is single-threaded), at most the host
+    CPU share of one GPU."""
     import numpy as np
 
     import oracle
@@ -329,7 +395,11 @@ def cpu_baseline(torch, budget_s=12.0):
 
     c = FULL
     d, r, eps, S = c["d"], c["r"], c["eps"], c["n_sources"]
-    threads = max(1, min(16, os.cpu_count() or 1))
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(HOST_THREADS_MAX, avail))
     srcs_dev = gen_sources(torch, S, 4096, d, c["scale"], seed=1000, dtype=torch.bfloat16)
     qs = synth.to_f64(gen_queries(torch, S, r, seed=1001))
     srcs = [synth.to_f64(s) for s in srcs_dev]
@@ -350,7 +420,7 @@ def cpu_baseline(torch, budget_s=12.0):
 
     R = threads * 4
     dt = run(R)
-    R = int(min(4096, max(R, R * budget_s / max(dt, 1e-3))))
+    R = int(min(4096, max(R, R * budget_s / 3 / max(dt, 1e-3))))
     R -= R % threads or 0
     # Whole passes over the sample until the budget is spent.
     passes, dt = 0, 0.0
@@ -359,26 +429,48 @@ def cpu_baseline(torch, budget_s=12.0):
         passes += 1
     rate = passes * R * S / dt
     return dict(value=round(rate, 1), unit="tokens/s per read site", cores=threads,
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(), host_logical_cpus=os.cpu_count(),
+                affinity_cpus=avail,
                 sample=f"full routing d=1024 r=64: rows 0..{R - 1} of T=16384, all 49 sites, "
-                       f"{passes} passes, fp64 oracle on {threads} host threads ({dt:.1f} s)")
+                       f"{passes} passes, fp64 oracle (C++, -O2) on {threads} host threads "
+                       f"({dt:.1f} s); threads capped at the {HOST_THREADS_MAX}-core host share "
+                       f"of one GPU")
 
 
-def copy_ceiling(torch, lrar, ev, reps):
-    """A plain 1 GiB device copy (2 GiB of traffic): what streaming reaches on this GPU."""
+def ceilings(torch, lrar, ev):
+    """Plain streams over 1 GiB, timed like the rows: a read (lrar_read_stream) and a copy
+    (lrar_copy, 1 GiB read + 1 GiB written). The write rate follows from the copy's time less
+    the read time of its read half: W = B / (t_copy - B / R)."""
     nbytes = 1 << 30
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(3)
-    ms = time_calls(torch, ev, lrar.lrar_copy(b, a, prepare=True), reps)
+    ms_r = time_calls(torch, ev, lrar.lrar_read_stream(a, prepare=True))
+    ms_c = time_calls(torch, ev, lrar.lrar_copy(b, a, prepare=True))
     del a, b
-    return row_entry(ms, 2 * nbytes)
+    read = row_entry(ms_r, nbytes)
+    copy = row_entry(ms_c, 2 * nbytes)
+    R = read["GBps"]
+    t_write = ms_c * 1e-3 - nbytes / (R * 1e9)
+    W = nbytes / t_write / 1e9 if t_write > 0 else None
+    return dict(read=read, copy=copy, write_GBps_derived=round(W, 1) if W else None)
+
+
+def mix_ceiling(ceil, n):
+    """Streaming ceiling of a read of n sources that writes one row per n rows read."""
+    if not ceil:
+        return None
+    R, W = ceil["read"]["GBps"], ceil.get("write_GBps_derived")
+    if not W:
+        return None
+    return 1.0 / ((n / (n + 1)) / R + (1.0 / (n + 1)) / W)
 
 
 # ---- main ------------------------------------------------------------------------------------------
 
-def traffic_entry(digest, launches_bytes):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on these sources."""
+def traffic_entry(digest, key):
+    """HBM bytes per launch of one measured kernel from rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by what they read for a copy of known size), if taken on these sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -386,23 +478,69 @@ def traffic_entry(digest, launches_bytes):
         return None
     if t.get("source_digest") != digest:
         return None
-    return t.get("bytes_per_launch")
+    e = t.get("kernels", {}).get(key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+ROW_GROUPS = (("block_routing_d2048", rows_block_routing),
+              ("production_d7168", rows_production),
+              ("backward_d4096", rows_backward),
+              ("read_variants_d1024", rows_read_variants))
+
+# The bf16 forward at d >= 2048 (block routing and production width, online variant): each row
+# is priced like `roofline`, algorithmic bytes per launch over the mean launch time.
+WIDE_ROOFLINES = (
+    [("block_routing_d2048", f"r{r}_n{n}_online", 16 * 4096, 2048, n, r)
+     for n in (10, 9) for r in (16, 64, 512, 2048)]
+    + [("production_d7168", f"single_pass_r{r}_n9_online", 32768, 7168, 9, r)
+       for r in (64, 1792, 7168)])
+
+
+def wide_rooflines(rows, ceil, digest):
+    out = []
+    for group, key, T, d, n, r in WIDE_ROOFLINES:
+        e = rows.get(group, {}).get(key)
+        if e is None:
+            continue
+        nbytes = fwd_bytes(T, d, n, 2)
+        ms = e.get("mean_ms", e["ms"])
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        mix = mix_ceiling(ceil, n) if ceil else None
+        out.append(dict(workload=f"{group.replace('_', ' ')}: T={T} d={d} r={r} n={n}, bf16",
+                        row=f"{group}/{key}", bound="hbm", achieved=round(achieved, 1),
+                        peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                        traffic=traffic_entry(digest, f"{group}/{key}"),
+                        algorithmic_bytes_per_launch=nbytes, avg_launch_us=round(ms * 1e3, 3),
+                        mix_ceiling_GBps=round(mix, 1) if mix else None,
+                        frac_of_mix_ceiling=round(achieved / mix, 4) if mix else None))
+    return out
 
 
 def main():
+    global FIXED_REPS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--reps", type=int, default=10, help="launches per extra row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline step (profiling runs of single rows)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming ceilings (profiling runs of single rows)")
+    ap.add_argument("--rows", default=None,
+                    help="comma-separated row groups to run (default: all): "
+                         + ", ".join(n for n, _ in ROW_GROUPS))
+    ap.add_argument("--fixed-reps", type=int, default=None,
+                    help="time exactly this many launches per row instead of the stop rule "
+                         "(profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the depth-mix read shards by token rows with no "
               "exchange in the forward, so there is no multi-GPU run here (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+    FIXED_REPS = args.fixed_reps
 
     import torch
 
@@ -413,62 +551,77 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
     ev = Evictor(torch, lrar)
-    log(f"bench: headline full routing, steps={args.steps} warmup={args.warmup}")
-    h = headline(torch, lrar, args, ev)
-    log(f"bench: headline {h['step_ms']:.3f} ms/step, {h['gbps']:.0f} GB/s")
+    h = None
+    if not args.no_headline:
+        log(f"bench: headline full routing, steps={args.steps} warmup={args.warmup}")
+        h = headline(torch, lrar, args, ev)
+        log(f"bench: headline {h['step_ms']:.3f} ms/step, {h['gbps']:.0f} GB/s")
+    ceil = None
+    if not args.no_ceilings:
+        ceil = ceilings(torch, lrar, ev)
+        log(f"bench: ceilings read {ceil['read']['GBps']:.0f} GB/s, copy "
+            f"{ceil['copy']['GBps']:.0f} GB/s, write (derived) {ceil['write_GBps_derived']} GB/s")
     rows = {}
-    copy = copy_ceiling(torch, lrar, ev, args.reps)
-    log(f"bench: copy ceiling {copy['GBps']:.0f} GB/s")
+    want = None if args.rows is None else set(args.rows.split(","))
     if not args.no_rows:
-        for name, fn in (("block_routing_d2048", rows_block_routing),
-                         ("production_d7168", rows_production),
-                         ("backward_d4096", rows_backward),
-                         ("read_variants_d1024", rows_read_variants)):
+        for name, fn in ROW_GROUPS:
+            if want is not None and name not in want:
+                continue
             log(f"bench: row {name}")
-            rows[name] = fn(torch, lrar, ev, args.reps)
+            rows[name] = fn(torch, lrar, ev, None)
             torch.cuda.empty_cache()
     digest = source_digest()
-    # The dominant kernel: at d = 1024 the library reads 20 or more sources with its deeper-ring
-    # tile instantiation (three sources in flight), which serves sites n = 20..49 and moves 84 %
-    # of the step's bytes; sites n = 2..19 run the two-deep instantiation.
-    deep = range(DEEP_MIN_SOURCES, h["S"] + 1)
-    bytes_launch = sum(fwd_bytes(h["T"], FULL["d"], n, 2) for n in deep) / len(deep)
-    avg_launch_s = sum(h["site_mean_ms"][n - 1] for n in deep) * 1e-3 / len(deep)
-    achieved = bytes_launch / avg_launch_s / 1e9
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4),
-                    traffic=traffic_entry(digest, bytes_launch),
-                    kernel="k_read_tile<bf16, 8, 2, 1, 2, true, 2, 3, 1, online> "
-                           "(d=1024, r=64; sites n=20..49)",
-                    algorithmic_bytes_per_launch=round(bytes_launch),
-                    avg_launch_us=round(avg_launch_s * 1e6, 3),
-                    launches_per_step=len(deep))
+    roofline = None
+    if h is not None:
+        # The dominant kernel: at d = 1024 the library reads 20 or more sources with its
+        # deeper-ring tile instantiation (three sources in flight), which serves sites n = 20..49
+        # and moves 84 % of the step's bytes; sites n = 2..19 run the two-deep instantiation.
+        deep = range(DEEP_MIN_SOURCES, h["S"] + 1)
+        bytes_launch = sum(fwd_bytes(h["T"], FULL["d"], n, 2) for n in deep) / len(deep)
+        avg_launch_s = sum(h["site_mean_ms"][n - 1] for n in deep) * 1e-3 / len(deep)
+        achieved = bytes_launch / avg_launch_s / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                        traffic=traffic_entry(digest, "headline"),
+                        kernel="k_read_tile<bf16, 8, 2, 1, 2, true, 2, 3, 1, online> "
+                               "(d=1024, r=64; sites n=20..49)",
+                        algorithmic_bytes_per_launch=round(bytes_launch),
+                        avg_launch_us=round(avg_launch_s * 1e6, 3),
+                        launches_per_step=len(deep))
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(torch)
-    tokens_site_per_s = h["T"] * h["S"] / (h["step_ms"] * 1e-3)
     line = {
         "metric": "depth-mix tokens/sec and effective HBM GB/s (% of MI355X peak), bf16, per site",
-        "value": round(tokens_site_per_s, 1),
-        "unit": "tokens/s per read site (mean over 49 sites)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(h["step_ms"], 4),
-        "step_cv": round(h["step_cv"], 4),
+        "value": None, "unit": "tokens/s per read site (mean over 49 sites)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full routing d=1024 r=64, 49 sources / 49 read sites, "
                                "T=8x2048 tokens, bf16 sources, fp32 queries",
                    "global_batch": 8, "seq_len": 2048, "parallelism": "none (1 GPU)"},
-        "effective_GBps": round(h["gbps"], 1),
-        "copy_ceiling": copy,
-        "wall_ms_per_step_with_eviction": round(h["wall_ms"], 3),
-        "sites": h["sites"],
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "rows": rows,
-        "source_digest": digest,
     }
+    if h is not None:
+        line.update({
+            "value": round(h["T"] * h["S"] / (h["step_ms"] * 1e-3), 1),
+            "ms_per_step": round(h["step_ms"], 4),
+            "step_cv": round(h["step_cv"], 4),
+            "effective_GBps": round(h["gbps"], 1),
+            "wall_ms_per_step_with_eviction": round(h["wall_ms"], 3),
+            "sites": h["sites"],
+            "mix_ceiling_n49_GBps": round(mix_ceiling(ceil, 49), 1) if ceil else None,
+        })
+    line.update({
+        "roofline": roofline,
+        "rooflines_wide": wide_rooflines(rows, ceil, digest),
+        "cpu_baseline": cpu,
+        "ceilings": ceil,
+        "rows": rows,
+        "timing": dict(window=WINDOW, max_windows=MAX_WINDOWS, cv_max=CV_MAX,
+                       drift_max=DRIFT_MAX, fixed_reps=FIXED_REPS),
+        "source_digest": digest,
+    })
     print(json.dumps(line), flush=True)
 
 

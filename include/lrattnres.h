@@ -231,6 +231,15 @@ size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n);
  * calibrate hardware traffic counters and to measure the achievable copy bandwidth. */
 lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* A plain streaming read of `bytes` bytes (src 16-byte aligned, bytes a multiple of 16) that
+ * folds them into one 32-bit word per thread written to `sink` (device, 4-byte aligned,
+ * lrar_read_stream_sink_bytes() bytes, not overlapping src). Not part of the read: it is the
+ * reference kernel for the read-bandwidth ceiling. */
+lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* stream);
+
+/* Bytes of the sink lrar_read_stream writes. */
+size_t lrar_read_stream_sink_bytes(void);
+
 /* Static description of a status code. */
 const char* lrar_status_string(lrar_status status);
 

@@ -321,6 +321,17 @@ def test_copy_rejects(L):
     assert L.lrar_copy(FAKE, FAKE * 2, 0, None) == lrar.LRAR_OK
 
 
+def test_read_stream_rejects(L):
+    sink_bytes = L.lrar_read_stream_sink_bytes()
+    assert sink_bytes > 0 and sink_bytes % 4 == 0
+    assert L.lrar_read_stream(FAKE + 8, 64, FAKE * 4, None) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_read_stream(FAKE, 60, FAKE * 4, None) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_read_stream(FAKE, 64, None, None) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_read_stream(FAKE, 64, FAKE * 4 + 2, None) == lrar.LRAR_ERR_INVALID
+    assert L.lrar_read_stream(FAKE, 64, FAKE + 32, None) == lrar.LRAR_ERR_INVALID  # overlap
+    assert L.lrar_read_stream(FAKE, 0, None, None) == lrar.LRAR_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lrar, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(lrar, "_lib", None)

@@ -82,9 +82,13 @@ def lib():
             L.lrar_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+            L.lrar_read_stream.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+            L.lrar_read_stream_sink_bytes.argtypes = []
+            L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
             for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
                        "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
-                       "lrar_backward", "lrar_backward_grad", "lrar_copy"):
+                       "lrar_backward", "lrar_backward_grad", "lrar_copy",
+                       "lrar_read_stream"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -98,8 +102,9 @@ def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
     return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
             "lrar_merge", "lrar_merge_accumulate", "lrar_backward", "lrar_backward_grad",
-            "lrar_backward_workspace_size", "lrar_copy", "lrar_status_string",
-            "lrar_last_error", "lrar_version"]
+            "lrar_backward_workspace_size", "lrar_copy", "lrar_read_stream",
+            "lrar_read_stream_sink_bytes", "lrar_status_string", "lrar_last_error",
+            "lrar_version"]
 
 
 class Prepared:
@@ -459,6 +464,20 @@ def lrar_copy(dst, src, stream=None, prepare: bool = False):
         raise ValueError("dst and src must have the same byte size")
     args = (dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream))
     return _run(lib().lrar_copy, args, dst, (dst, src), prepare)
+
+
+def lrar_read_stream(src, sink=None, stream=None, prepare: bool = False):
+    """Plain streaming read of src (a 16-byte multiple): the read-bandwidth reference.
+    Returns the sink (int32 [lrar_read_stream_sink_bytes() / 4]) the kernel folds it into."""
+    torch = _torch()
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty((int(lib().lrar_read_stream_sink_bytes()) // 4,), dtype=torch.int32,
+                           device=src.device)
+    if sink.numel() * 4 < int(lib().lrar_read_stream_sink_bytes()):
+        raise ValueError("sink too small")
+    args = (src.data_ptr(), nbytes, sink.data_ptr(), _stream(stream))
+    return _run(lib().lrar_read_stream, args, sink, (src, sink), prepare)
 
 
 def version() -> str:

@@ -699,6 +699,25 @@ lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream) {
   return device_status(lrar::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)), fn);
 }
 
+size_t lrar_read_stream_sink_bytes(void) {
+  return static_cast<size_t>(lrar::kCalibBlocks) * lrar::kBlock * sizeof(uint32_t);
+}
+
+lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* stream) {
+  const char* fn = "lrar_read_stream";
+  if (bytes == 0) return LRAR_OK;
+  if (src == nullptr || sink == nullptr) return fail(LRAR_ERR_INVALID, "%s: null pointer", fn);
+  if (!aligned16(src) || bytes % 16 != 0)
+    return fail(LRAR_ERR_INVALID, "%s: src and size must be 16-byte multiples", fn);
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return fail(LRAR_ERR_INVALID, "%s: sink must be 4-byte aligned", fn);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(sink), b = reinterpret_cast<uintptr_t>(src);
+  const size_t sb = lrar_read_stream_sink_bytes();
+  if (a < b + bytes && b < a + sb) return fail(LRAR_ERR_INVALID, "%s: sink overlaps src", fn);
+  return device_status(lrar::launch_read_stream(src, bytes, sink, static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
 const char* lrar_status_string(lrar_status s) {
   switch (s) {
     case LRAR_OK: return "ok";
@@ -715,23 +734,67 @@ const char* lrar_version(void) { return "0.1.0"; }
 
 }  // extern "C"
 
-// ---- the calibration copy kernel ---------------------------------------------------------------
+// ---- the calibration kernels --------------------------------------------------------------------
+// Plain streams that set the bandwidth ceilings the read is measured against. Each lane keeps
+// U independent 16-byte loads in flight, and the workgroups walk the buffer in one shared
+// window (workgroup b takes the U * kBlock units from b * U * kBlock, then jumps by the grid):
+// on MI355X a grid of 1024 workgroups with two (copy) or four (read) loads per lane measured
+// fastest in a sweep of 1024-8192 workgroups and 1-8 loads per lane.
 
 namespace lrar {
 
 __global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
                                                  const u32x4* __restrict__ src, int64_t n16) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * kCopyUnroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * kCopyUnroll + threadIdx.x;
+       base < n16; base += stride) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) {
+      const int64_t i = base + static_cast<int64_t>(k) * kBlock;
+      v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) {
+      const int64_t i = base + static_cast<int64_t>(k) * kBlock;
+      if (i < n16) __builtin_nontemporal_store(v[k], dst + i);
+    }
+  }
+}
+
+// Reads n16 units and folds them into one 32-bit word per thread (written to sink, so the
+// loads cannot be dropped): the traffic is the read alone, plus 4 bytes per thread.
+__global__ __launch_bounds__(kBlock) void k_read_stream(const u32x4* __restrict__ src, int64_t n16,
+                                                        uint32_t* __restrict__ sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * kReadUnroll;
+  uint32_t x = 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * kReadUnroll + threadIdx.x;
+       base < n16; base += stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) {
+      const int64_t i = base + static_cast<int64_t>(k) * kBlock;
+      v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  sink[static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x] = x;
 }
 
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
-  int64_t blocks = (n16 + kBlock - 1) / kBlock;
-  if (blocks > 8192) blocks = 8192;
+  int64_t blocks = (n16 + kBlock * kCopyUnroll - 1) / (kBlock * kCopyUnroll);
+  if (blocks > kCalibBlocks) blocks = kCalibBlocks;
   hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
                      static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  hipLaunchKernelGGL(k_read_stream, dim3(kCalibBlocks), dim3(kBlock), 0, s,
+                     static_cast<const u32x4*>(src), n16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
 }
 

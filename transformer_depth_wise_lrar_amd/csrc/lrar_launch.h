@@ -128,6 +128,12 @@ int backward_tile_max_chunks();
 hipError_t launch_backward_tile(const BwdParams& p, int io_bf16, int grad_bf16, double* block_dq,
                                 int max_blocks, int* grid, hipStream_t s);
 
+// The calibration streams (lrar_copy, lrar_read_stream): workgroups, and 16-byte loads in flight
+// per lane.
+constexpr int kCalibBlocks = 1024;
+constexpr int kCopyUnroll = 2;
+constexpr int kReadUnroll = 4;
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStream_t s);
 
 }  // namespace lrar
