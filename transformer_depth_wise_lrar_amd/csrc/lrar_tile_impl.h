@@ -558,6 +558,11 @@ int device_cus() {
 // (waves x PF tiles) must cover the HBM latency.
 constexpr int tile_rows(int nu) { return nu <= 1 ? 4 : (nu <= 2 ? 2 : 1); }
 constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
+// Keys read from the row units that reach every unit slot of a 4-slot row (r = d at d = 2048;
+// r >= 1792 at d = 7168) keep one source in flight instead of two: their float64 scoring keeps
+// the vector unit busy, and the smaller ring measured 2-3 % faster there (r = d = 2048,
+// r = 1792 at d = 7168) but 4 % slower for a key in the last slot alone (r = 512, d = 2048).
+constexpr bool key_fills_slots(int ks, int tu, int nu) { return ks == 0 && nu == 4 && tu == nu; }
 
 // Reads of many sources keep one more source in flight: three sources ahead measured 8 %
 // (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two for spread keys, in
@@ -591,7 +596,7 @@ template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, in
           typename ACC, bool DEEP = false, bool KA = false>
 hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
-  constexpr int PF = DEEP ? kDeepPrefetch : tile_prefetch(NU);
+  constexpr int PF = DEEP ? kDeepPrefetch : (key_fills_slots(KS, TU, NU) ? 1 : tile_prefetch(NU));
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC, KA>;
   const int ub = (p.d - p.r) / VEC;
   const int nur = (p.d + VEC - 1) / VEC;
