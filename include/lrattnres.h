@@ -223,6 +223,24 @@ lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar
                                int32_t accumulate, float* dq, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* lrar_backward_grad with no workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the query-gradient partials go to a 32 MiB scratch array that the library holds in each
+ * GPU's memory until the process ends. The call allocates and frees nothing. Arguments, results
+ * and limits as for lrar_backward_grad. The workspace entry point's workgroup count is kept
+ * when its partials ((grid + 32) * r float64 values) fit the scratch, so the results are the
+ * same bits; otherwise fewer workgroups are used (dq then sums in another fixed order), and a
+ * key so wide that fewer than min(256, that count) workgroups would fit returns
+ * LRAR_ERR_UNSUPPORTED (only possible for r > 14563).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or host threads) race, and must be ordered by the caller. Nothing in the scratch
+ * needs to be cleared between calls. */
+lrar_status lrar_backward_noalloc(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                  int32_t n, const void* const* src, const int64_t* src_ld,
+                                  const float* q, lrar_dtype grad_dtype, const void* dout,
+                                  int64_t dout_ld, void* const* dsrc, const int64_t* dsrc_ld,
+                                  int32_t accumulate, float* dq, void* stream);
+
 /* Bytes of device workspace lrar_backward needs for this shape (0 if T = 0). */
 size_t lrar_backward_workspace_size(int64_t T, int32_t d, int32_t r, int32_t n);
 

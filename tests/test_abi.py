@@ -349,3 +349,25 @@ def test_row_strides_of_256_mib_are_unsupported(L):
     assert merge_acc(L, T=0, o_ld=most + 8) == lrar.LRAR_ERR_UNSUPPORTED
     assert merge_acc(L, T=0, b_ld=most + 8) == lrar.LRAR_ERR_UNSUPPORTED
     assert merge_acc(L, T=0, acc_ld=most // 2 + 8) == lrar.LRAR_ERR_UNSUPPORTED  # fp32 acc
+
+
+def bwd_noalloc(L, T=4, d=8, r=4, n=2, dsrc=None, dq=FAKE * 8, dout=FAKE * 7, ld=8):
+    p, lds_ = _src(n, ld)
+    dsrc = dsrc if dsrc is not None else [FAKE * (10 + i) for i in range(n)]
+    dp = (ctypes.c_void_p * n)(*dsrc)
+    dl = (ctypes.c_int64 * n)(*([ld] * n))
+    return L.lrar_backward_noalloc(T, d, r, 1e-6, 1, n, p, lds_, FAKE * 2, 0, dout, ld, dp, dl, 0,
+                                   dq, None)
+
+
+def test_backward_noalloc_checks_before_device_work(L):
+    """The no-allocation backward validates like lrar_backward_grad and refuses a key whose
+    query-gradient partials would not fit its scratch, all before touching the device."""
+    assert bwd_noalloc(L, T=0) == lrar.LRAR_OK
+    assert bwd_noalloc(L, dsrc=[FAKE * 10, FAKE * 10 + 64]) == lrar.LRAR_ERR_INVALID
+    assert bwd_noalloc(L, dq=None) == lrar.LRAR_ERR_INVALID
+    # d = r = 16384 over 2048 rows: at least 256 workgroups' partials, more than 32 MiB
+    big = 16384
+    assert bwd_noalloc(L, T=2048, d=big, r=big, n=1, ld=big, dsrc=[FAKE * 5000],
+                       dout=FAKE * 9000, dq=FAKE * 20000) == lrar.LRAR_ERR_UNSUPPORTED
+    assert "scratch" in L.lrar_last_error().decode()

@@ -79,6 +79,9 @@ def lib():
             L.lrar_backward_grad.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
                                              _vp, _i32, _vp, _i64, _vpp, _i64p, _i32, _vp, _vp,
                                              ctypes.c_size_t, _vp]
+            L.lrar_backward_noalloc.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
+                                                _vp, _i32, _vp, _i64, _vpp, _i64p, _i32, _vp,
+                                                _vp]
             L.lrar_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
@@ -87,8 +90,8 @@ def lib():
             L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
             for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
                        "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
-                       "lrar_backward", "lrar_backward_grad", "lrar_copy",
-                       "lrar_read_stream"):
+                       "lrar_backward", "lrar_backward_grad", "lrar_backward_noalloc",
+                       "lrar_copy", "lrar_read_stream"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -102,7 +105,7 @@ def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
     return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
             "lrar_merge", "lrar_merge_accumulate", "lrar_backward", "lrar_backward_grad",
-            "lrar_backward_workspace_size", "lrar_copy", "lrar_read_stream",
+            "lrar_backward_noalloc", "lrar_backward_workspace_size", "lrar_copy", "lrar_read_stream",
             "lrar_read_stream_sink_bytes", "lrar_status_string", "lrar_last_error",
             "lrar_version"]
 
@@ -402,7 +405,7 @@ def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
 
 
 def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, workspace, stream,
-              prepare):
+              prepare, noalloc=False):
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, None)
     n = len(srcs)
@@ -423,13 +426,17 @@ def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, worksp
     if dq is None:
         dq = torch.empty((r,), dtype=torch.float32, device=dev)
     _need(dq, (r,), torch.float32, "dq")
-    need = lrar_backward_workspace_size(T, d, r, n)
-    if workspace is None:
-        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
     gp, gld = _rows(dout, "dout")
     head = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr())
     if grad_code is not None:
         head = head + (grad_code,)
+    if noalloc:
+        args = head + (gp, gld, dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
+                       _stream(stream))
+        return _run(fn, args, (dsrc, dq), (srcs, q, dout, dsrc, dq), prepare)
+    need = lrar_backward_workspace_size(T, d, r, n)
+    if workspace is None:
+        workspace = torch.empty((max(need, 8),), dtype=torch.uint8, device=dev)
     args = head + (gp, gld, dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                    _stream(stream))
@@ -455,6 +462,15 @@ def lrar_backward_grad(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=
     that dtype (bf16 rounded once, after the optional accumulation); dq stays fp32 [r]."""
     return _backward(lib().lrar_backward_grad, _dtype_code(dout), srcs, q, dout, r, eps, dsrc,
                      accumulate, dq, workspace, stream, prepare)
+
+
+def lrar_backward_noalloc(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
+                          accumulate: bool = False, dq=None, stream=None, prepare: bool = False):
+    """lrar_backward_grad without a workspace: the library's per-device scratch holds the
+    query-gradient partials (the call allocates nothing on the device when dsrc and dq are
+    given). Calls that overlap on one GPU race on that scratch."""
+    return _backward(lib().lrar_backward_noalloc, _dtype_code(dout), srcs, q, dout, r, eps, dsrc,
+                     accumulate, dq, None, stream, prepare, noalloc=True)
 
 
 def lrar_copy(dst, src, stream=None, prepare: bool = False):

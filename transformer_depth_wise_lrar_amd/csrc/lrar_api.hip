@@ -8,12 +8,20 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 
 #include "../../include/lrattnres.h"
 #include "lrar_device.h"
 #include "lrar_launch.h"
+
+// Device scratch of lrar_backward_noalloc: the query-gradient partials, for callers that cannot
+// allocate. Each GPU the library runs on holds its own copy until the process ends; host code
+// never uses this name as an address (it is a host-side stand-in), only the per-device address
+// that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
 
 namespace {
 
@@ -591,12 +599,41 @@ lrar_status lrar_merge_accumulate(int64_t T, int32_t d, int32_t r, double eps, l
 namespace {
 
 // The backward with gradients (dout, dsrc) of type grad; shared by both entry points.
+// The no-allocation backward's scratch: at most kScratchBytes of dq partials. The workspace
+// entry point's grid is kept when its rows fit; otherwise fewer workgroups (at least
+// kScratchMinGrid, or as many as the rows need) share the rows.
+constexpr int kScratchMinGrid = 256;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the calling thread's current device's copy of `scratch`, looked up once per device.
+lrar_status device_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LRAR_ERR_UNSUPPORTED, "%s: device %d beyond the %d the scratch table covers", fn,
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, fn);
+    if (ptr == nullptr) return fail(LRAR_ERR_DEVICE, "%s: no scratch address on device %d", fn, dev);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LRAR_OK;
+}
+
+// workspace == nullptr with use_scratch: the partials go to the device scratch.
 lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, double eps,
                           lrar_dtype io, int32_t n, const void* const* src,
                           const int64_t* src_ld, const float* q, lrar_dtype grad,
                           const void* dout, int64_t dout_ld, void* const* dsrc,
                           const int64_t* dsrc_ld, int32_t accumulate, float* dq, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, bool use_scratch = false) {
   lrar_status st = check_shape(fn, T, d, r, eps, io);
   if (st != LRAR_OK) return st;
   if (!dtype_ok(grad)) return fail(LRAR_ERR_INVALID, "%s: unknown gradient dtype %d", fn, (int)grad);
@@ -628,12 +665,26 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
     return fail(LRAR_ERR_UNSUPPORTED, "%s: the key of r = %d columns at d = %d spans more "
                 "chunks of 64 units than the %s path keeps query-gradient partials for", fn, r,
                 d, use_vec > 1 ? "vector" : "scalar");
-  const size_t need = lrar::backward_workspace(T, r);
-  if (T > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(LRAR_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                workspace_bytes);
-  if (T > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
-    return fail(LRAR_ERR_INVALID, "%s: workspace must be 8-byte aligned", fn);
+  size_t need = lrar::backward_workspace(T, r);
+  int ws_grid = 0;
+  if (use_scratch) {
+    // the workspace entry point's grid when its rows fit the scratch, else fewer workgroups
+    const int full = T > 0 ? lrar::backward_grid(T) : 0;
+    const int64_t fit = static_cast<int64_t>(kScratchBytes / (sizeof(double) * r)) - 32;
+    const int floor_grid = full < kScratchMinGrid ? full : kScratchMinGrid;
+    if (T > 0 && fit < floor_grid)
+      return fail(LRAR_ERR_UNSUPPORTED, "%s: r = %d needs more than the %zu bytes of scratch "
+                  "(its query-gradient partials of %d workgroups at r = %d)", fn, r,
+                  kScratchBytes, floor_grid, r);
+    ws_grid = static_cast<int>(fit < full ? fit : full);
+    need = T > 0 ? lrar::backward_workspace_rows(ws_grid, r) : 0;
+  } else {
+    if (T > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(LRAR_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace_bytes);
+    if (T > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+      return fail(LRAR_ERR_INVALID, "%s: workspace must be 8-byte aligned", fn);
+  }
   if (T == 0) return LRAR_OK;
   {
     Regions R;
@@ -643,8 +694,12 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
     for (int i = 0; i < n; ++i)
       R.output(rows_region(dsrc[i], T, dsrc_ld[i], d, esize(grad), "dsrc", i));
     R.output(span_region(dq, static_cast<int64_t>(r) * 4, "dq"));
-    R.output(span_region(workspace, static_cast<int64_t>(need), "workspace"));
+    if (!use_scratch) R.output(span_region(workspace, static_cast<int64_t>(need), "workspace"));
     st = check_disjoint(fn, R);
+    if (st != LRAR_OK) return st;
+  }
+  if (use_scratch) {
+    st = device_scratch(fn, &workspace);
     if (st != LRAR_OK) return st;
   }
   p.n = n;
@@ -659,7 +714,7 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
   p.dq = dq;
   p.workspace = workspace;
   return device_status(lrar::launch_backward(p, io == LRAR_BF16, grad == LRAR_BF16, use_vec,
-                                             static_cast<hipStream_t>(stream)),
+                                             static_cast<hipStream_t>(stream), ws_grid),
                        fn);
 }
 
@@ -686,6 +741,15 @@ lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar
   return backward_impl("lrar_backward_grad", T, d, r, eps, io, n, src, src_ld, q, grad_dtype,
                        dout, dout_ld, dsrc, dsrc_ld, accumulate, dq, workspace, workspace_bytes,
                        stream);
+}
+
+lrar_status lrar_backward_noalloc(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                                  int32_t n, const void* const* src, const int64_t* src_ld,
+                                  const float* q, lrar_dtype grad_dtype, const void* dout,
+                                  int64_t dout_ld, void* const* dsrc, const int64_t* dsrc_ld,
+                                  int32_t accumulate, float* dq, void* stream) {
+  return backward_impl("lrar_backward_noalloc", T, d, r, eps, io, n, src, src_ld, q, grad_dtype,
+                       dout, dout_ld, dsrc, dsrc_ld, accumulate, dq, nullptr, 0, stream, true);
 }
 
 lrar_status lrar_copy(void* dst, const void* src, size_t bytes, void* stream) {

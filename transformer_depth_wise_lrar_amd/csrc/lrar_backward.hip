@@ -261,13 +261,18 @@ bool backward_supported(int d, int r, int vec) {
 // Workspace: [grid][r] float64 workgroup partials, then [kReduceGroups][r] float64.
 size_t backward_workspace(int64_t T, int r) {
   if (T <= 0) return 0;
-  return (static_cast<size_t>(backward_grid(T)) + kReduceGroups) * static_cast<size_t>(r) * sizeof(double);
+  return backward_workspace_rows(backward_grid(T), r);
+}
+
+size_t backward_workspace_rows(int grid, int r) {
+  return (static_cast<size_t>(grid) + kReduceGroups) * static_cast<size_t>(r) * sizeof(double);
 }
 
 hipError_t launch_backward(const BwdParams& p, int io_bf16, int grad_bf16, int vec,
-                           hipStream_t s) {
-  // The workspace holds backward_grid(T) workgroup rows; a launch may fill fewer of them.
-  const int max_grid = backward_grid(p.T);
+                           hipStream_t s, int ws_grid) {
+  // The workspace holds max_grid workgroup rows (backward_grid(T) unless the caller sized it
+  // for fewer); a launch may fill fewer of them.
+  const int max_grid = ws_grid > 0 ? ws_grid : backward_grid(p.T);
   int grid = max_grid;
   double* block_dq = static_cast<double*>(p.workspace);
   double* level2 = block_dq + static_cast<int64_t>(max_grid) * p.r;

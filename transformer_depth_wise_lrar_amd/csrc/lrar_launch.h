@@ -120,8 +120,13 @@ int backward_grid(int64_t T);
 // Lanes' register window for dq partials must cover the key; false if this shape needs more.
 bool backward_supported(int d, int r, int vec);
 size_t backward_workspace(int64_t T, int r);
+// Workspace bytes for `grid` workgroup rows of dq partials (backward_workspace uses
+// backward_grid(T)).
+size_t backward_workspace_rows(int grid, int r);
+// ws_grid > 0: the workspace holds that many workgroup rows (at most backward_grid(T)) and the
+// launch uses at most that many workgroups.
 hipError_t launch_backward(const BwdParams& p, int io_bf16, int grad_bf16, int vec,
-                           hipStream_t s);
+                           hipStream_t s, int ws_grid = 0);
 // Row-tile backward for the vector path (lrar_backward_tile.hip): writes the dq partials of
 // *grid <= max_blocks workgroups into block_dq.
 int backward_tile_max_chunks();
