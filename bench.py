@@ -341,7 +341,20 @@ def rows_backward(torch, lrar, ev, reps):
         srcs, q, dout16, r, 1e-6, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True))
     res[f"backward_bf16_grads_r{r}_n{n}"] = row_entry(
         ms16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r, T)
-    del srcs, dsrc16, dout, dout16
+    # the same from the forward's saved statistics (z_i, 1 / rho_i per row: 16 n more bytes
+    # read per row), with fp32 and bf16 gradients
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    _, saved = lrar.lrar_forward_save(srcs, q, r, 1e-6, out=out)
+    dsrc = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(n)]
+    mss = time_calls(torch, ev, lrar.lrar_backward_saved(
+        srcs, q, saved, dout, r, dsrc=dsrc, dq=dq, workspace=ws, prepare=True))
+    res[f"backward_saved_r{r}_n{n}"] = row_entry(mss, nbytes + 16 * n * T, T)
+    del dsrc
+    mss16 = time_calls(torch, ev, lrar.lrar_backward_saved(
+        srcs, q, saved, dout16, r, dsrc=dsrc16, dq=dq, workspace=ws, prepare=True))
+    res[f"backward_saved_bf16_grads_r{r}_n{n}"] = row_entry(
+        mss16, (2 * n * d + 2 * d + 2 * n * d) * T + 4 * r + 16 * n * T, T)
+    del srcs, dsrc16, dout, dout16, saved, out
     return res
 
 

@@ -97,6 +97,18 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
                          const float* q, void* out, int64_t out_ld, float* alpha,
                          int64_t alpha_ld, int32_t variant, void* stream);
 
+/* lrar_forward that also saves, for the backward, each source's normalization and softmax
+ * statistics (LR-AttnRes paper App. I, "Implementation": the fused kernel keeps them for its
+ * backward): per row t, saved[t][i] = z_i (the score) and saved[t][n + i] = 1 / rho_i (the
+ * reciprocal RMS of the key), both float64.
+ *   saved, saved_ld : device float64 [T, saved_ld >= 2n]; overlaps no other buffer.
+ * Other arguments as for lrar_forward (no weights output). lrar_backward_saved takes the
+ * buffer. */
+lrar_status lrar_forward_save(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                              int32_t n, const void* const* src, const int64_t* src_ld,
+                              const float* q, void* out, int64_t out_ld, double* saved,
+                              int64_t saved_ld, int32_t variant, void* stream);
+
 /* The full-width-RMS control read (LR-AttnRes paper §4.4, Eq. 13 "control"; App. B.1): the
  * key of source i is its last r coordinates divided by the RMS of the whole row,
  *     kbar_i = tail_r(o_i) / sqrt(||o_i||^2 / d + eps),   z_i = q . kbar_i,
@@ -222,6 +234,20 @@ lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar
                                int64_t dout_ld, void* const* dsrc, const int64_t* dsrc_ld,
                                int32_t accumulate, float* dq, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* lrar_backward_grad from the statistics lrar_forward_save kept (LR-AttnRes paper App. I,
+ * "Implementation"; App. B.3): the scores z_i and reciprocal RMS 1 / rho_i are read from
+ * `saved` (device float64 [T, saved_ld >= 2n], as lrar_forward_save wrote it for the same
+ * sources, q and eps) instead of being recomputed from the keys, so the key pass reduces only
+ * s_i = <g, o_i>. eps enters through the saved 1 / rho_i and is not an argument. A weights array
+ * alone would not do: the key columns' gradient needs z_i and rho_i themselves. Other
+ * arguments, limits and the workspace as for lrar_backward_grad. */
+lrar_status lrar_backward_saved(int64_t T, int32_t d, int32_t r, lrar_dtype io, int32_t n,
+                                const void* const* src, const int64_t* src_ld, const float* q,
+                                const double* saved, int64_t saved_ld, lrar_dtype grad_dtype,
+                                const void* dout, int64_t dout_ld, void* const* dsrc,
+                                const int64_t* dsrc_ld, int32_t accumulate, float* dq,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* lrar_backward_grad with no workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

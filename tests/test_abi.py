@@ -371,3 +371,41 @@ def test_backward_noalloc_checks_before_device_work(L):
     assert bwd_noalloc(L, T=2048, d=big, r=big, n=1, ld=big, dsrc=[FAKE * 5000],
                        dout=FAKE * 9000, dq=FAKE * 20000) == lrar.LRAR_ERR_UNSUPPORTED
     assert "scratch" in L.lrar_last_error().decode()
+
+
+def fwd_save(L, T=4, d=8, r=4, n=2, ld=8, out=FAKE * 2, saved=FAKE * 30, saved_ld=4):
+    p, l = _src(n, ld)
+    return L.lrar_forward_save(T, d, r, 1e-6, 1, n, p, l, FAKE * 3, out, 8, saved, saved_ld, 0,
+                               None)
+
+
+def bwd_saved(L, T=4, d=8, r=4, n=2, saved=FAKE * 30, saved_ld=4, dsrc=None):
+    p, ld = _src(n, 8)
+    dsrc = dsrc if dsrc is not None else [FAKE * (10 + i) for i in range(n)]
+    dp = (ctypes.c_void_p * n)(*dsrc)
+    dl = (ctypes.c_int64 * n)(*([8] * n))
+    return L.lrar_backward_saved(T, d, r, 1, n, p, ld, FAKE * 2, saved, saved_ld, 0, FAKE * 7, 8,
+                                 dp, dl, 0, FAKE * 8, FAKE * 9, 1 << 30, None)
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(saved=None), "saved is null"), (dict(saved_ld=3), "saved_ld"),
+    (dict(saved=FAKE * 2 + 8), "saved overlaps out"), (dict(saved=FAKE + 8), "saved overlaps src"),
+])
+def test_forward_save_rejects(L, kw, what):
+    assert fwd_save(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(saved=None), "saved is null"), (dict(saved_ld=3), "saved_ld"),
+    (dict(dsrc=[FAKE * 30 + 16, FAKE * 11]), "dsrc[0] overlaps saved"),
+])
+def test_backward_saved_rejects(L, kw, what):
+    assert bwd_saved(L, **kw) == lrar.LRAR_ERR_INVALID
+    assert what in L.lrar_last_error().decode()
+
+
+def test_saved_entry_points_empty(L):
+    assert fwd_save(L, T=0, saved=None) == lrar.LRAR_OK
+    assert bwd_saved(L, T=0, saved=None) == lrar.LRAR_OK

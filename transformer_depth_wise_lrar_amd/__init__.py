@@ -61,6 +61,11 @@ def lib():
                 raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
             L.lrar_forward.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
                                        _vp, _i64, _vp, _i64, _i32, _vp]
+            L.lrar_forward_save.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p, _vp,
+                                            _vp, _i64, _vp, _i64, _i32, _vp]
+            L.lrar_backward_saved.argtypes = [_i64, _i32, _i32, _i32, _i32, _vpp, _i64p, _vp, _vp,
+                                              _i64, _i32, _vp, _i64, _vpp, _i64p, _i32, _vp, _vp,
+                                              ctypes.c_size_t, _vp]
             L.lrar_forward_fullrms.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
                                                _vp, _vp, _i64, _vp, _i64, _vp]
             L.lrar_forward_keys.argtypes = [_i64, _i32, _i32, _f64, _i32, _i32, _vpp, _i64p,
@@ -88,7 +93,8 @@ def lib():
             L.lrar_read_stream.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
             L.lrar_read_stream_sink_bytes.argtypes = []
             L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
-            for fn in ("lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys",
+            for fn in ("lrar_forward", "lrar_forward_save", "lrar_backward_saved",
+                       "lrar_forward_fullrms", "lrar_forward_keys",
                        "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
                        "lrar_backward", "lrar_backward_grad", "lrar_backward_noalloc",
                        "lrar_copy", "lrar_read_stream"):
@@ -103,7 +109,8 @@ def lib():
 
 def exported_symbols() -> list[str]:
     """The C entry points this binding expects the library to export."""
-    return ["lrar_forward", "lrar_forward_fullrms", "lrar_forward_keys", "lrar_forward_stats",
+    return ["lrar_forward", "lrar_forward_save", "lrar_backward_saved", "lrar_forward_fullrms",
+            "lrar_forward_keys", "lrar_forward_stats",
             "lrar_merge", "lrar_merge_accumulate", "lrar_backward", "lrar_backward_grad",
             "lrar_backward_noalloc", "lrar_backward_workspace_size", "lrar_copy", "lrar_read_stream",
             "lrar_read_stream_sink_bytes", "lrar_status_string", "lrar_last_error",
@@ -236,6 +243,27 @@ def lrar_forward(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, alpha=N
     args = (T, d, r, float(eps), io, len(srcs), ptrs, lds, q.data_ptr(), op, old, ap, ald,
             VARIANTS[variant], _stream(stream))
     return _run(lib().lrar_forward, args, (out, alpha), (srcs, q, out, alpha), prepare)
+
+
+def lrar_forward_save(srcs: Sequence, q, r: int, eps: float = 1e-6, out=None, saved=None,
+                      variant: str = "auto", stream=None, prepare: bool = False):
+    """lrar_forward that also writes the statistics the backward reuses: saved [T, 2n] float64,
+    the scores z_i in columns 0..n-1 and 1 / rho_i in columns n..2n-1. Returns (out, saved)."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, None)
+    n = len(srcs)
+    _query(q, r)
+    if out is None:
+        out = torch.empty((T, d), dtype=srcs[0].dtype, device=srcs[0].device)
+    _need(out, (T, d), srcs[0].dtype, "out")
+    if saved is None:
+        saved = torch.empty((T, 2 * n), dtype=torch.float64, device=srcs[0].device)
+    _need(saved, (T, 2 * n), torch.float64, "saved")
+    op, old = _rows(out, "out")
+    sp, sld = _rows(saved, "saved")
+    args = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr(), op, old, sp, sld,
+            VARIANTS[variant], _stream(stream))
+    return _run(lib().lrar_forward_save, args, (out, saved), (srcs, q, out, saved), prepare)
 
 
 def _read_outputs(srcs, T, d, out, alpha):
@@ -405,7 +433,7 @@ def lrar_backward_workspace_size(T: int, d: int, r: int, n: int) -> int:
 
 
 def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, workspace, stream,
-              prepare, noalloc=False):
+              prepare, noalloc=False, saved=None):
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, None)
     n = len(srcs)
@@ -427,9 +455,14 @@ def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, worksp
         dq = torch.empty((r,), dtype=torch.float32, device=dev)
     _need(dq, (r,), torch.float32, "dq")
     gp, gld = _rows(dout, "dout")
-    head = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr())
-    if grad_code is not None:
-        head = head + (grad_code,)
+    if saved is not None:
+        _need(saved, (T, 2 * n), torch.float64, "saved")
+        sp, sld = _rows(saved, "saved")
+        head = (T, d, r, io, n, ptrs, lds, q.data_ptr(), sp, sld, grad_code)
+    else:
+        head = (T, d, r, float(eps), io, n, ptrs, lds, q.data_ptr())
+        if grad_code is not None:
+            head = head + (grad_code,)
     if noalloc:
         args = head + (gp, gld, dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
                        _stream(stream))
@@ -440,7 +473,7 @@ def _backward(fn, grad_code, srcs, q, dout, r, eps, dsrc, accumulate, dq, worksp
     args = head + (gp, gld, dptrs, dlds, int(bool(accumulate)), dq.data_ptr(),
                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                    _stream(stream))
-    return _run(fn, args, (dsrc, dq), (srcs, q, dout, dsrc, dq, workspace), prepare)
+    return _run(fn, args, (dsrc, dq), (srcs, q, dout, dsrc, dq, workspace, saved), prepare)
 
 
 def lrar_backward(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,
@@ -462,6 +495,15 @@ def lrar_backward_grad(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=
     that dtype (bf16 rounded once, after the optional accumulation); dq stays fp32 [r]."""
     return _backward(lib().lrar_backward_grad, _dtype_code(dout), srcs, q, dout, r, eps, dsrc,
                      accumulate, dq, workspace, stream, prepare)
+
+
+def lrar_backward_saved(srcs: Sequence, q, saved, dout, r: int, dsrc=None,
+                        accumulate: bool = False, dq=None, workspace=None, stream=None,
+                        prepare: bool = False):
+    """lrar_backward_grad from the statistics lrar_forward_save wrote (saved [T, 2n] float64):
+    the keys are not scored again. Gradients in dout's dtype; returns (dsrc, dq)."""
+    return _backward(lib().lrar_backward_saved, _dtype_code(dout), srcs, q, dout, r, 0.0, dsrc,
+                     accumulate, dq, workspace, stream, prepare, saved=saved)
 
 
 def lrar_backward_noalloc(srcs: Sequence, q, dout, r: int, eps: float = 1e-6, dsrc=None,

@@ -248,18 +248,24 @@ bool row_fits_tile(int32_t d, int use_vec) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
-                         const void* const* src, const int64_t* src_ld, const float* q, void* out,
-                         int64_t out_ld, float* alpha, int64_t alpha_ld, int32_t variant,
+// lrar_forward, and with saved != nullptr lrar_forward_save.
+lrar_status forward_impl(const char* fn, int64_t T, int32_t d, int32_t r, double eps,
+                         lrar_dtype io, int32_t n, const void* const* src, const int64_t* src_ld,
+                         const float* q, void* out, int64_t out_ld, float* alpha,
+                         int64_t alpha_ld, double* saved, int64_t saved_ld, int32_t variant,
                          void* stream) {
-  const char* fn = "lrar_forward";
   lrar::ReadParams p;
   int use_vec = 1;
   lrar_status st = check_read(fn, T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
                               alpha_ld, p, use_vec);
   if (st != LRAR_OK) return st;
+  if (saved != nullptr && saved_ld < 2 * static_cast<int64_t>(n))
+    return fail(LRAR_ERR_INVALID, "%s: saved_ld = %lld < 2 n = %d", fn, (long long)saved_ld,
+                2 * n);
+  p.saved = saved;
+  p.saved_ld = saved_ld;
   if (variant < LRAR_VARIANT_AUTO || variant > LRAR_VARIANT_ONLINE)
     return fail(LRAR_ERR_INVALID, "%s: unknown variant %d", fn, variant);
   const bool tile_fits = row_fits_tile(d, use_vec);
@@ -278,12 +284,35 @@ lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype
   if (T == 0) return LRAR_OK;
   Regions R;
   read_regions(R, p, io);
+  if (saved != nullptr) R.output(rows_region(saved, T, saved_ld, 2 * n, 8, "saved"));
   st = check_disjoint(fn, R);
   if (st != LRAR_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = tile_fits ? lrar::launch_tile(p, kind, io == LRAR_BF16, use_vec, 0, hs)
                                  : lrar::launch_read(p, kind, io == LRAR_BF16, use_vec, 0, hs);
   return device_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+lrar_status lrar_forward(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io, int32_t n,
+                         const void* const* src, const int64_t* src_ld, const float* q, void* out,
+                         int64_t out_ld, float* alpha, int64_t alpha_ld, int32_t variant,
+                         void* stream) {
+  return forward_impl("lrar_forward", T, d, r, eps, io, n, src, src_ld, q, out, out_ld, alpha,
+                      alpha_ld, nullptr, 0, variant, stream);
+}
+
+lrar_status lrar_forward_save(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
+                              int32_t n, const void* const* src, const int64_t* src_ld,
+                              const float* q, void* out, int64_t out_ld, double* saved,
+                              int64_t saved_ld, int32_t variant, void* stream) {
+  if (saved == nullptr && T > 0)
+    return fail(LRAR_ERR_INVALID, "lrar_forward_save: saved is null");
+  return forward_impl("lrar_forward_save", T, d, r, eps, io, n, src, src_ld, q, out, out_ld,
+                      nullptr, 0, saved, saved_ld, variant, stream);
 }
 
 lrar_status lrar_forward_fullrms(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,
@@ -633,7 +662,8 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
                           const int64_t* src_ld, const float* q, lrar_dtype grad,
                           const void* dout, int64_t dout_ld, void* const* dsrc,
                           const int64_t* dsrc_ld, int32_t accumulate, float* dq, void* workspace,
-                          size_t workspace_bytes, void* stream, bool use_scratch = false) {
+                          size_t workspace_bytes, void* stream, bool use_scratch = false,
+                          const double* saved = nullptr, int64_t saved_ld = 0) {
   lrar_status st = check_shape(fn, T, d, r, eps, io);
   if (st != LRAR_OK) return st;
   if (!dtype_ok(grad)) return fail(LRAR_ERR_INVALID, "%s: unknown gradient dtype %d", fn, (int)grad);
@@ -646,6 +676,9 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
   if (st != LRAR_OK) return st;
   if (accumulate != 0 && accumulate != 1)
     return fail(LRAR_ERR_INVALID, "%s: accumulate must be 0 or 1", fn);
+  if (saved != nullptr && saved_ld < 2 * static_cast<int64_t>(n))
+    return fail(LRAR_ERR_INVALID, "%s: saved_ld = %lld < 2 n = %d", fn, (long long)saved_ld,
+                2 * n);
   if (dout_ld < d) return fail(LRAR_ERR_INVALID, "%s: dout_ld = %lld < d", fn, (long long)dout_ld);
   if (dsrc == nullptr || dsrc_ld == nullptr) return fail(LRAR_ERR_INVALID, "%s: null dsrc table", fn);
   if (T > 0 && (q == nullptr || dout == nullptr || dq == nullptr))
@@ -691,6 +724,7 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
     add_sources(R, p.src, n, T, d, esize(io), "src");
     R.input(span_region(q, static_cast<int64_t>(r) * 4, "q"));
     R.input(rows_region(dout, T, dout_ld, d, esize(grad), "dout"));
+    if (saved != nullptr) R.input(rows_region(saved, T, saved_ld, 2 * n, 8, "saved"));
     for (int i = 0; i < n; ++i)
       R.output(rows_region(dsrc[i], T, dsrc_ld[i], d, esize(grad), "dsrc", i));
     R.output(span_region(dq, static_cast<int64_t>(r) * 4, "dq"));
@@ -710,6 +744,8 @@ lrar_status backward_impl(const char* fn, int64_t T, int32_t d, int32_t r, doubl
   p.q = q;
   p.dout = dout;
   p.dout_ld = dout_ld;
+  p.saved = saved;
+  p.saved_ld = saved_ld;
   p.accumulate = accumulate;
   p.dq = dq;
   p.workspace = workspace;
@@ -741,6 +777,20 @@ lrar_status lrar_backward_grad(int64_t T, int32_t d, int32_t r, double eps, lrar
   return backward_impl("lrar_backward_grad", T, d, r, eps, io, n, src, src_ld, q, grad_dtype,
                        dout, dout_ld, dsrc, dsrc_ld, accumulate, dq, workspace, workspace_bytes,
                        stream);
+}
+
+lrar_status lrar_backward_saved(int64_t T, int32_t d, int32_t r, lrar_dtype io, int32_t n,
+                                const void* const* src, const int64_t* src_ld, const float* q,
+                                const double* saved, int64_t saved_ld, lrar_dtype grad_dtype,
+                                const void* dout, int64_t dout_ld, void* const* dsrc,
+                                const int64_t* dsrc_ld, int32_t accumulate, float* dq,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (saved == nullptr && T > 0)
+    return fail(LRAR_ERR_INVALID, "lrar_backward_saved: saved is null");
+  // eps only enters through the saved reciprocal RMS; 0 passes the shape check
+  return backward_impl("lrar_backward_saved", T, d, r, 0.0, io, n, src, src_ld, q, grad_dtype,
+                       dout, dout_ld, dsrc, dsrc_ld, accumulate, dq, workspace, workspace_bytes,
+                       stream, false, saved, saved_ld);
 }
 
 lrar_status lrar_backward_noalloc(int64_t T, int32_t d, int32_t r, double eps, lrar_dtype io,

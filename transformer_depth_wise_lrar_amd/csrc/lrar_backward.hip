@@ -7,7 +7,8 @@
 // than a tile.
 //
 // k_backward, one wavefront per token row:
-//   1. key pass (float64): z_i, rho_i, alpha_i of every source, as in the forward;
+//   1. key pass (float64): z_i, rho_i, alpha_i of every source, as in the forward (or z_i and
+//      rho_i from the forward's saved statistics);
 //   2. s_i = <g, o_i> over all d (float64 sums of exact products), streaming g = dL/dh and the
 //      source rows in column chunks (g is read again from the cache for every source); then
 //      dz_i = alpha_i (s_i - sum_j alpha_j s_j), which equals alpha_i <g, o_i - h>;
@@ -58,9 +59,16 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
 
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; row < p.T;
        row += step) {
-    // 1. weights
-    double z, rho;
-    row_scores<IO, VEC>(p.src, p.n, row, p.d, p.r, p.eps, p.q, lane, z, rho);
+    // 1. weights (the scores and key RMS from the forward's saved statistics when given)
+    double z = 0.0, rho = 1.0;
+    if (p.saved != nullptr) {
+      if (lane < p.n) {
+        z = p.saved[row * p.saved_ld + lane];
+        rho = 1.0 / p.saved[row * p.saved_ld + p.n + lane];
+      }
+    } else {
+      row_scores<IO, VEC>(p.src, p.n, row, p.d, p.r, p.eps, p.q, lane, z, rho);
+    }
     const double m = wave_max((lane < p.n) ? z : -INFINITY);
     const double ex = (lane < p.n) ? exp(z - m) : 0.0;
     const double a = ex / wave_sum(ex);

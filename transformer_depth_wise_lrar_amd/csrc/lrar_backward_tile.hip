@@ -9,7 +9,8 @@
 //   pass A  the upstream gradient g of the row is loaded once into registers; the sources
 //           stream through a prefetch ring and, from each row, the float64 sums q . k, k . k
 //           and s_i = <g, o_i> are reduced (DPP, then across the row's waves through LDS in a
-//           fixed order); lane i keeps z_i, rho_i, s_i;
+//           fixed order); lane i keeps z_i, rho_i, s_i. With the forward's saved statistics
+//           (SAVED) z_i and rho_i are read from them and only s_i is reduced;
 //   then    alpha = softmax(z), sbar = sum_j alpha_j s_j, dz_i = alpha_i (s_i - sbar), which
 //           equals alpha_i <g, o_i - h>;
 //   pass B  dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns
@@ -28,7 +29,7 @@
 
 namespace lrar {
 
-template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR>
+template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR, bool SAVED>
 __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* __restrict__ block_dq) {
   static_assert(kWavesPerBlock % WPR == 0, "a workgroup holds whole row groups");
   constexpr int PF = 2;
@@ -90,10 +91,17 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
 
     // ---- pass A: z_i, rho_i, s_i (lane i)
     double zi = 0.0, rhoi = 1.0, si = 0.0;
+    if constexpr (SAVED) {
+      if (lane < n) {
+        const double* srow = p.saved + row * p.saved_ld;
+        zi = srow[lane];
+        rhoi = 1.0 / srow[n + lane];
+      }
+    }
     Stage<IO, VEC, NU, 1, 0> ring[PF + 1];
     const auto fold_a = [&](const Stage<IO, VEC, NU, 1, 0>& st, int i) {
-      double red[3];
-      key_partial_units<TU>(st.t.u[0], qst, g, red[0], red[1]);
+      double red[3] = {0.0, 0.0, 0.0};
+      if constexpr (!SAVED) key_partial_units<TU>(st.t.u[0], qst, g, red[0], red[1]);
       double s = 0.0;
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
@@ -109,34 +117,54 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         }
       }
       red[2] = s;
-      // The three sums (q . k, k . k, g . o) by the transposed butterfly, as a fourth zero
-      // value: lane l < 4 then holds sum v4[transposed_index<2>(l)].
-      const double v4[4] = {red[0], red[1], red[2], 0.0};
-      const double x = wave_sums_transposed<2>(v4, lane);
-      if constexpr (WPR == 1) {
-        // transposed_index<2>: lane 0 holds q . k, lane 2 k . k, lane 1 g . o
-        red[0] = lane_f64(x, 0);
-        red[1] = lane_f64(x, 2);
-        red[2] = lane_f64(x, 1);
-      } else {
-        const int idx = transposed_index<2>(lane);
-        if (lane < 4 && idx < 3) xch[parity][wib][idx] = x;
-        __syncthreads();
-        const int base = wib - g.w;
+      if constexpr (SAVED) {
+        // only g . o: the transposed butterfly of two values (the second zero) leaves it in
+        // lane 0 (transposed_index<1>(0) = 0)
+        const double v2[2] = {s, 0.0};
+        const double x = wave_sums_transposed<1>(v2, lane);
+        if constexpr (WPR == 1) {
+          red[2] = lane_f64(x, 0);
+        } else {
+          if (lane == 0) xch[parity][wib][2] = x;
+          __syncthreads();
+          const int base = wib - g.w;
+          double t = xch[parity][base][2];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          double t = xch[parity][base][j];
-#pragma unroll
-          for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][j];
-          red[j] = t;
+          for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][2];
+          red[2] = t;
+          parity ^= 1;
         }
-        parity ^= 1;
-      }
-      const double rho = sqrt(red[1] / p.r + p.eps);
-      if (lane == i) {
-        zi = red[0] / rho;
-        rhoi = rho;
-        si = red[2];
+        if (lane == i) si = red[2];
+      } else {
+        // The three sums (q . k, k . k, g . o) by the transposed butterfly, as a fourth zero
+        // value: lane l < 4 then holds sum v4[transposed_index<2>(l)].
+        const double v4[4] = {red[0], red[1], red[2], 0.0};
+        const double x = wave_sums_transposed<2>(v4, lane);
+        if constexpr (WPR == 1) {
+          // transposed_index<2>: lane 0 holds q . k, lane 2 k . k, lane 1 g . o
+          red[0] = lane_f64(x, 0);
+          red[1] = lane_f64(x, 2);
+          red[2] = lane_f64(x, 1);
+        } else {
+          const int idx = transposed_index<2>(lane);
+          if (lane < 4 && idx < 3) xch[parity][wib][idx] = x;
+          __syncthreads();
+          const int base = wib - g.w;
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            double t = xch[parity][base][j];
+#pragma unroll
+            for (int v = 1; v < WPR; ++v) t += xch[parity][base + v][j];
+            red[j] = t;
+          }
+          parity ^= 1;
+        }
+        const double rho = sqrt(red[1] / p.r + p.eps);
+        if (lane == i) {
+          zi = red[0] / rho;
+          rhoi = rho;
+          si = red[2];
+        }
       }
       if (stash != nullptr) {
 #pragma unroll
@@ -338,7 +366,8 @@ size_t stash_bytes(const BwdParams& p, int wpr) {
 template <typename IO, typename GIO, int VEC, int NU, int TU, int WPR>
 hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_blocks, int* grid_out,
                              hipStream_t s) {
-  auto kern = k_backward_tile<IO, GIO, VEC, NU, TU, WPR>;
+  auto kern = p.saved != nullptr ? k_backward_tile<IO, GIO, VEC, NU, TU, WPR, true>
+                                 : k_backward_tile<IO, GIO, VEC, NU, TU, WPR, false>;
   BwdParams pk = p;
   pk.key_stash = stash_bytes<IO, VEC>(p, WPR) <= kStashMaxBytes ? 1 : 0;
   const int ub = (p.d - p.r) / VEC;
@@ -347,7 +376,9 @@ hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_block
                      (pk.key_stash ? stash_bytes<IO, VEC>(p, WPR) : 0);
   static thread_local size_t cached_lds = ~size_t(0);
   static thread_local int cached_per_cu = 0;
-  if (cached_lds != lds) {
+  static thread_local bool cached_saved = false;
+  if (cached_lds != lds || cached_saved != (p.saved != nullptr)) {
+    cached_saved = p.saved != nullptr;
     int per = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kBlock, lds) != hipSuccess ||
         per < 1)

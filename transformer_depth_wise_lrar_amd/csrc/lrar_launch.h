@@ -22,6 +22,9 @@ struct ReadParams {
   int64_t out_ld;
   float* alpha;  // nullable
   int64_t alpha_ld;
+  // nullable: per row the scores z_i (columns 0..n-1) and 1 / rho_i (columns n..2n-1)
+  double* saved;
+  int64_t saved_ld;
   // merge only
   const float* m_in;
   const float* l_in;
@@ -76,6 +79,10 @@ struct BwdParams {
   const void* dout;  // float32 or bf16, the gradient type
   int64_t dout_ld;
   int accumulate;
+  // nullable: the forward's saved statistics (z_i, then 1 / rho_i, per row); when given, the
+  // key pass does not score the keys again
+  const double* saved;
+  int64_t saved_ld;
   float* dq;
   void* workspace;  // [grid + reduce groups][r] float64 dq partials
   int key_stash;    // set by the row-tile launcher: pass B reads the key units from LDS

@@ -69,6 +69,11 @@ __global__ __launch_bounds__(kBlock) void k_read_two_pass(ReadParams p, SrcList 
     float w, w_prior, m_f, l_f;
     row_weights<PRIOR>(p, row, lane, z, w, w_prior, m_f, l_f);
     if (p.alpha != nullptr && lane < p.n) p.alpha[row * p.alpha_ld + lane] = w;
+    if (p.saved != nullptr && lane < p.n) {
+      double* srow = p.saved + row * p.saved_ld;
+      srow[lane] = z;
+      srow[p.n + lane] = 1.0 / rho;
+    }
     if constexpr (PRIOR) {
       if (lane == 0) {
         if (p.m_out) p.m_out[row] = m_f;

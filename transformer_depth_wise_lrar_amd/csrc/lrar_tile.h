@@ -386,16 +386,21 @@ __device__ __forceinline__ void key_partial_spread(const KeyPiece<IO, KS>& kp,
   }
 }
 
+// A source's score z and the reciprocal 1 / rho of its key's RMS.
+struct Score {
+  double z, rinv;
+};
+
 // z = dot / sqrt(ss / r + eps) as dot * rsq(ss / r + eps): the hardware reciprocal square root
 // refined by two Newton steps y <- y (3 - a y^2) / 2, each of which squares the relative error,
 // so the result is good to a few float64 ulp. A zero key with eps = 0 gives 0 * inf = NaN, as
 // the division does.
-__device__ __forceinline__ double score_from_sums(double dot, double ss, int r, double eps) {
+__device__ __forceinline__ Score score_from_sums(double dot, double ss, int r, double eps) {
   const double a = ss / r + eps;
   double y = __builtin_amdgcn_rsq(a);
   y = y * fma(-0.5 * a, y * y, 1.5);
   y = y * fma(-0.5 * a, y * y, 1.5);
-  return dot * y;
+  return Score{dot * y, y};
 }
 
 // e^x for x <= kLazyRescale, accurate to about 2^-31 relative (the weights it feeds are
@@ -466,7 +471,7 @@ __device__ __forceinline__ double half_sums_transposed(const double (&red)[2 * R
 // The score of row j (< R) in lane j from transposed (dot, ss) sums: the ss of row j sits R
 // lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1).
 template <int R>
-__device__ __forceinline__ double score_from_transposed(double x, int r, double eps) {
+__device__ __forceinline__ Score score_from_transposed(double x, int r, double eps) {
   const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
   return score_from_sums(x, ss, r, eps);
 }
@@ -474,7 +479,7 @@ __device__ __forceinline__ double score_from_transposed(double x, int r, double 
 // Row-local sums for R = 1 or 2 tile rows when the spread key sits in lanes 0..31: the sums of
 // the wave's first half are the rows' sums. Lane j (< R) returns row j's score.
 template <int R>
-__device__ __forceinline__ double row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
                                                       double eps) {
   return score_from_transposed<R>(half_sums_transposed<R>(red, lane), r, eps);
 }
@@ -531,7 +536,7 @@ __device__ __forceinline__ int transposed_index(int lane) {
 // wave_sums_transposed. Lane j (< R) returns row j's score; other lanes return values of no
 // meaning.
 template <int R>
-__device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_wave(const double (&red)[2 * R], int lane, int r,
                                                   double eps) {
   return score_from_transposed<R>(wave_sums_transposed<R>(red, lane), r, eps);
 }
@@ -540,7 +545,7 @@ __device__ __forceinline__ double row_scores_wave(const double (&red)[2 * R], in
 // lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
 // division run once for all rows.
 template <int R>
-__device__ __forceinline__ double row_scores_to_lanes(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_to_lanes(const double (&red)[2 * R], int lane, int r,
                                                       double eps) {
   double dot = red[0], ss = red[1];
 #pragma unroll

@@ -130,6 +130,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 
   float acc[R][NU][VEC];
   double zk[R];  // lane i: score (two-pass: weight) of source i in row j
+  double rk[R];  // lane i: 1 / rho of source i in row j (kept only for the saved statistics)
+  const bool keep_scores = p.alpha != nullptr || p.saved != nullptr;
   // Online-softmax state of row j, held in lane j: reference mref, running sum lsum of
   // e^{z - mref}, running maximum mtop. One vector exp then serves all R rows.
   double mref = -INFINITY, lsum = 0.0, mtop = -INFINITY;
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       zk[j] = 0.0;
+      rk[j] = 0.0;
 #pragma unroll
       for (int k = 0; k < NU; ++k)
 #pragma unroll
@@ -202,8 +205,23 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     }
   };
 
+  // Writes the saved statistics of a tile's rows: z_i and 1 / rho_i of source i in lane i.
+  const auto save_scores = [&](const TileGeom& t) {
+    if (p.saved != nullptr && t.w == 0 && lane < n) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (j < t.nrow) {
+          double* srow = p.saved + (t.r0 + j) * p.saved_ld;
+          srow[lane] = zk[j];
+          srow[n + lane] = rk[j];
+        }
+      }
+    }
+  };
+
   // Normalises and writes a tile's h (and the weights / merged statistics).
   const auto finish_tile = [&](const TileGeom& t) {
+    if constexpr (MODE != kTileTwoPass) save_scores(t);
     const float inv = static_cast<float>(1.0 / lsum);  // lane j: row j (online and merge)
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -241,7 +259,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   };
 
   // Scores of one stage's rows; lane j returns row j's.
-  const auto stage_scores = [&](const Stage<IO, VEC, NU, R, KS>& st, const TileGeom& t) {
+  const auto stage_scores = [&](const Stage<IO, VEC, NU, R, KS>& st,
+                                const TileGeom& t) -> Score {
     double red[2 * R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -299,16 +318,29 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     return row_scores_to_lanes<R>(red, lane, nrm, p.eps);
   };
 
-  // Scores source i's stage and folds its rows into the online-softmax accumulators.
-  const auto fold_source = [&](const Stage<IO, VEC, NU, R, KS>& st, const TileGeom& t, int i) {
-    const double z = stage_scores(st, t);  // lane j: row j
-    if (p.alpha != nullptr) {  // the scores are kept only to write the weights
+  // Keeps the scores (and reciprocal RMS) of source i for the weights and saved statistics.
+  const auto keep_source = [&](const Score& sc, int i) {
+    if (keep_scores) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
-        const double zj = lane_f64(z, j);
+        const double zj = lane_f64(sc.z, j);
         if (lane == i) zk[j] = zj;
       }
     }
+    if (p.saved != nullptr) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const double rj = lane_f64(sc.rinv, j);
+        if (lane == i) rk[j] = rj;
+      }
+    }
+  };
+
+  // Scores source i's stage and folds its rows into the online-softmax accumulators.
+  const auto fold_source = [&](const Stage<IO, VEC, NU, R, KS>& st, const TileGeom& t, int i) {
+    const Score sc = stage_scores(st, t);  // lane j: row j
+    const double z = sc.z;
+    keep_source(sc, i);
     if constexpr (kMerge) mtop = fmax(mtop, z);  // only the merge reports the maximum
     // Rescale a row only when its score passes the reference by more than kLazyRescale
     // (always on its first source, whose reference is -inf).
@@ -363,15 +395,23 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
           load_stage_as<true, false, kExact>(ring[(b + PF) % (PF + 1)], src_base(ia),
                                              p.src.ld[ia], t, kNoKeys, 0, i + PF < n);
           if (i < n) {
-            const double z = stage_scores(ring[b], t);
+            const Score sc = stage_scores(ring[b], t);
 #pragma unroll
             for (int j = 0; j < R; ++j) {
-              const double zj = lane_f64(z, j);
+              const double zj = lane_f64(sc.z, j);
               if (lane == i) zk[j] = zj;
+            }
+            if (p.saved != nullptr) {
+#pragma unroll
+              for (int j = 0; j < R; ++j) {
+                const double rj = lane_f64(sc.rinv, j);
+                if (lane == i) rk[j] = rj;
+              }
             }
           }
         }
       }
+      save_scores(t);
       // softmax once per row (lanes = sources)
       float w[R];
 #pragma unroll
