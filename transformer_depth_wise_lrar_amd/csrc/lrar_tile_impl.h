@@ -707,12 +707,30 @@ hipError_t launch_tile_units(const ReadParams& p, const KeyTable<MODE>& kt, hipS
   }
 }
 
-// Key path. Spread pieces of KS elements when the key is short: preferably KS = r / 32 rounded
-// up to a power of two, so the key fits lanes 0..31 (row-local sums), else 1 or 2 elements over
-// up to 64 lanes; a piece size must divide r and keep the loads aligned. Otherwise the row
-// units, with TU = 1 when every key chunk lands in a wave's last slot. The full-width-RMS
-// control always sums the row units (TU = NU); the separate-key read takes the piece the host
-// chose (p.key_piece, see tile_keys_piece).
+// The spread key piece a read of the value row's last r columns takes (see launch_tile_key):
+// key_piece_code(KS, row-local), or 0 when the key is read from the row units. Preferably
+// KS = r / 32 rounded up to a power of two, so the key fits lanes 0..31 (row-local sums), else 1
+// or 2 elements over up to 64 lanes; a piece size must divide r and keep the loads aligned.
+// Pieces of 16 elements (r up to 512) measured 2 % faster than the row units at r = 512,
+// d = 2048.
+inline int spread_piece(const ReadParams& p, int vec) {
+  if (vec == 1) return 0;
+  const int c0 = p.d - p.r;
+  const auto fits = [&](int ks) { return p.r % ks == 0 && c0 % (ks < vec ? ks : vec) == 0; };
+  if (p.r <= 32 && fits(1)) return key_piece_code(1, true);
+  if (p.r <= 64 && fits(2)) return key_piece_code(2, true);
+  if (p.r <= 128 && fits(4)) return key_piece_code(4, true);
+  if (p.r <= 256 && fits(8)) return key_piece_code(8, true);
+  if (p.r <= 512 && fits(16)) return key_piece_code(16, true);
+  if (p.r <= kWave) return key_piece_code(1, false);
+  if (p.r <= 2 * kWave && fits(2)) return key_piece_code(2, false);
+  return 0;
+}
+
+// Key path. Spread pieces (spread_piece) when the key is short; otherwise the row units, with
+// TU = 1 when every key chunk lands in a wave's last slot. The full-width-RMS control always
+// sums the row units (TU = NU); the separate-key read takes the piece the host chose
+// (p.key_piece, see tile_keys_piece).
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr (MODE == kTileFullRms) {
@@ -757,18 +775,23 @@ hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStr
   } else {
     const int c0 = p.d - p.r;
     if constexpr (VEC > 1) {
-      const auto fits = [&](int ks) { return p.r % ks == 0 && c0 % (ks < VEC ? ks : VEC) == 0; };
-      if (p.r <= 32 && fits(1))
-        return launch_tile_spread<IO, VEC, NU, 1, true, WPR, MODE, ACC>(p, kt, s);
-      if (p.r <= 64 && fits(2))
-        return launch_tile_spread<IO, VEC, NU, 2, true, WPR, MODE, ACC>(p, kt, s);
-      if (p.r <= 128 && fits(4))
-        return launch_tile_spread<IO, VEC, NU, 4, true, WPR, MODE, ACC>(p, kt, s);
-      if (p.r <= 256 && fits(8))
-        return launch_tile_spread<IO, VEC, NU, 8, true, WPR, MODE, ACC>(p, kt, s);
-      if (p.r <= kWave) return launch_tile_spread<IO, VEC, NU, 1, false, WPR, MODE, ACC>(p, kt, s);
-      if (p.r <= 2 * kWave && fits(2))
-        return launch_tile_spread<IO, VEC, NU, 2, false, WPR, MODE, ACC>(p, kt, s);
+      switch (spread_piece(p, VEC)) {
+        case key_piece_code(1, true):
+          return launch_tile_spread<IO, VEC, NU, 1, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(2, true):
+          return launch_tile_spread<IO, VEC, NU, 2, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(4, true):
+          return launch_tile_spread<IO, VEC, NU, 4, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(8, true):
+          return launch_tile_spread<IO, VEC, NU, 8, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(16, true):
+          return launch_tile_spread<IO, VEC, NU, 16, true, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(1, false):
+          return launch_tile_spread<IO, VEC, NU, 1, false, WPR, MODE, ACC>(p, kt, s);
+        case key_piece_code(2, false):
+          return launch_tile_spread<IO, VEC, NU, 2, false, WPR, MODE, ACC>(p, kt, s);
+        default: break;
+      }
     }
     const int first_key_chunk = (c0 / VEC) / kWave;
     if constexpr (NU > 1) {
@@ -780,7 +803,12 @@ hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStr
 }
 
 // Rows of up to 4 chunks of 64 units are held by one wave; wider rows by the 4 waves of a
-// workgroup, each taking every fourth chunk.
+// workgroup, each taking every fourth chunk. The one-pass reads of 9 to 16 chunks whose key,
+// read from the row units, spans at most a quarter of the row take two waves of 8 slots per row
+// instead: one exchange of key sums between two waves per source instead of four. That
+// measured 6 % faster at r = 1792, d = 7168, but 4 % slower at r = d = 7168 (the key fills
+// every slot, and the 256 registers of the two-wave tile leave one wave per SIMD for that
+// float64 work) and 3 % slower for spread keys (r = 64), whose sums need no exchange.
 template <typename IO, int VEC, int MODE, typename ACC>
 hipError_t launch_tile_nu(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   const int nur = (p.d + VEC - 1) / VEC;
@@ -789,6 +817,10 @@ hipError_t launch_tile_nu(const ReadParams& p, const KeyTable<MODE>& kt, hipStre
   if (chunks <= 2) return launch_tile_key<IO, VEC, 2, 1, MODE, ACC>(p, kt, s);
   if (chunks <= 4) return launch_tile_key<IO, VEC, 4, 1, MODE, ACC>(p, kt, s);
   if (chunks <= 8) return launch_tile_key<IO, VEC, 2, 4, MODE, ACC>(p, kt, s);
+  if constexpr (VEC > 1 && (MODE == kTileOnline || MODE == kTileTwoPass)) {
+    if (chunks <= 16 && spread_piece(p, VEC) == 0 && 4 * p.r <= p.d)
+      return launch_tile_key<IO, VEC, 8, 2, MODE, ACC>(p, kt, s);
+  }
   if (chunks <= 16) return launch_tile_key<IO, VEC, 4, 4, MODE, ACC>(p, kt, s);
   if (chunks <= 32) return launch_tile_key<IO, VEC, 8, 4, MODE, ACC>(p, kt, s);
   return hipErrorInvalidValue;
