@@ -9,8 +9,8 @@
 //   pass A  the upstream gradient g of the row is loaded once into registers; the sources
 //           stream through a prefetch ring and, from each row, the float64 sums q . k, k . k
 //           and s_i = <g, o_i> are reduced (DPP, then across the row's waves through LDS in a
-//           fixed order); lane i keeps z_i, rho_i, s_i. With the forward's saved statistics
-//           (SAVED) z_i and rho_i are read from them and only s_i is reduced;
+//           fixed order); lane i keeps z_i, 1 / rho_i, s_i. With the forward's saved statistics
+//           (SAVED) z_i and 1 / rho_i are read from them and only s_i is reduced;
 //   then    alpha = softmax(z), sbar = sum_j alpha_j s_j, dz_i = alpha_i (s_i - sbar), which
 //           equals alpha_i <g, o_i - h>;
 //   pass B  dsrc_i = alpha_i g, plus dz_i (q - z_i k_i / (r rho_i)) / rho_i on the key columns
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
   g.c0 = p.d - p.r;
   g.ub = g.c0 / VEC;
   g.r = p.r;
+  const double rinv_r = 1.0 / static_cast<double>(p.r);
   const int rq = p.d - g.ub * VEC;  // staged query columns
   QStage qst;
   qst.base = q_lds;
@@ -89,13 +90,13 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
       }
     }
 
-    // ---- pass A: z_i, rho_i, s_i (lane i)
-    double zi = 0.0, rhoi = 1.0, si = 0.0;
+    // ---- pass A: z_i, 1 / rho_i, s_i (lane i)
+    double zi = 0.0, rinvi = 1.0, si = 0.0;
     if constexpr (SAVED) {
       if (lane < n) {
         const double* srow = p.saved + row * p.saved_ld;
         zi = srow[lane];
-        rhoi = 1.0 / srow[n + lane];
+        rinvi = srow[n + lane];
       }
     }
     Stage<IO, VEC, NU, 1, 0> ring[PF + 1];
@@ -159,10 +160,10 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
           }
           parity ^= 1;
         }
-        const double rho = sqrt(red[1] / p.r + p.eps);
+        const Score sc = score_from_sums(red[0], red[1], rinv_r, p.eps);
         if (lane == i) {
-          zi = red[0] / rho;
-          rhoi = rho;
+          zi = sc.z;
+          rinvi = sc.rinv;
           si = red[2];
         }
       }
@@ -196,8 +197,8 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
     const double sbar = wave_sum_dpp(lane < n ? a * si : 0.0);
     const double dz = a * (si - sbar);
     const float af = static_cast<float>(a);
-    const float c1f = static_cast<float>(dz / rhoi);                          // dz / rho
-    const float c2f = static_cast<float>(dz * zi / (p.r * rhoi * rhoi));      // dz z / (r rho^2)
+    const float c1f = static_cast<float>(dz * rinvi);                         // dz / rho
+    const float c2f = static_cast<float>(dz * zi * (rinvi * rinvi) * rinv_r);  // dz z / (r rho^2)
 
     // ---- pass B: source gradients (the key units from the LDS stash, or streamed through the
     // ring again when the stash would be too large)

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
   const int nur = (p.d + VEC - 1) / VEC;
   const int nslot = (nur + kWave - 1) / kWave;  // unit slots per lane
   const int c0 = p.d - p.r;
+  const double rinv_r = 1.0 / static_cast<double>(p.r);
   const int ub = c0 / VEC;
   const int rq = p.d - ub * VEC;  // staged query columns
   const int k_lo = ub / kWave;    // first slot that can hold key units
@@ -157,11 +158,11 @@ __global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q
         for (int s = 0; s < 16; ++s) v16[s] = s <= kStatsMaxQ ? red[s] : 0.0;
         double u[4];
         wave_sums_transposed16(v16, lane, u);
-        const double rho = sqrt(lane_f64(u[0], 3) / p.r + p.eps);
+        const double rinv = score_from_sums(0.0, lane_f64(u[0], 3), rinv_r, p.eps).rinv;
         const int s0 = 8 * (lane & 1) + 4 * ((lane >> 1) & 1);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (lane < 4 && s0 + k < nqg) z_lds[wv][s0 + k][i] = u[k] / rho;
+          if (lane < 4 && s0 + k < nqg) z_lds[wv][s0 + k][i] = u[k] * rinv;
 #pragma unroll
         for (int s = 0; s <= kStatsMaxQ; ++s) red[s] = 0.0;
         ++i;

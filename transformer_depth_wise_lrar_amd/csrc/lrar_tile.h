@@ -391,14 +391,14 @@ struct Score {
   double z, rinv;
 };
 
-// z = dot / sqrt(ss / r + eps) as dot * rsq(ss / r + eps): the hardware reciprocal square root
-// refined by two Newton steps y <- y (3 - a y^2) / 2, each of which squares the relative error,
-// so the result is good to a few float64 ulp. A zero key with eps = 0 gives 0 * inf = NaN, as
-// the division does.
-__device__ __forceinline__ Score score_from_sums(double dot, double ss, int r, double eps) {
-  const double a = ss / r + eps;
+// z = dot / sqrt(ss / r + eps) as dot * rsq(ss / r + eps), with 1 / r passed in (rinv_r,
+// computed once per kernel). The hardware reciprocal square root is good to about 2^-23
+// relative; one Newton step y <- y (3 - a y^2) / 2 squares that error, to about 2^-45. A zero key
+// with eps = 0 gives 0 * inf = NaN, as the division does.
+__device__ __forceinline__ Score score_from_sums(double dot, double ss, double rinv_r,
+                                                 double eps) {
+  const double a = fma(ss, rinv_r, eps);
   double y = __builtin_amdgcn_rsq(a);
-  y = y * fma(-0.5 * a, y * y, 1.5);
   y = y * fma(-0.5 * a, y * y, 1.5);
   return Score{dot * y, y};
 }
@@ -453,17 +453,17 @@ __device__ __forceinline__ double half_sums_transposed(const double (&red)[2 * R
     // 2 b0 + b1: lane 0 dot0, lane 1 dot1, lane 2 ss0, lane 3 ss1.
     const double keep0 = b0 ? red[2] : red[0], send0 = b0 ? red[0] : red[2];
     const double keep1 = b0 ? red[3] : red[1], send1 = b0 ? red[1] : red[3];
-    const double w0 = keep0 + dpp_f64<kDppXor1>(send0, 0.0);
-    const double w1 = keep1 + dpp_f64<kDppXor1>(send1, 0.0);
+    const double w0 = keep0 + dpp_f64_all<kDppXor1>(send0);
+    const double w1 = keep1 + dpp_f64_all<kDppXor1>(send1);
     const bool b1 = (lane & 2) != 0;
-    x = (b1 ? w1 : w0) + dpp_f64<kDppXor2>(b1 ? w0 : w1, 0.0);
+    x = (b1 ? w1 : w0) + dpp_f64_all<kDppXor2>(b1 ? w0 : w1);
   } else {
     // values 0, 1 = dot, ss; lane 0 ends with dot, lane 1 with ss
-    x = (b0 ? red[1] : red[0]) + dpp_f64<kDppXor1>(b0 ? red[0] : red[1], 0.0);
-    x += dpp_f64<kDppXor2>(x, 0.0);
+    x = (b0 ? red[1] : red[0]) + dpp_f64_all<kDppXor1>(b0 ? red[0] : red[1]);
+    x += dpp_f64_all<kDppXor2>(x);
   }
-  x += dpp_f64<kRor4>(x, 0.0);
-  x += dpp_f64<kRor8>(x, 0.0);
+  x += dpp_f64_all<kRor4>(x);
+  x += dpp_f64_all<kRor8>(x);
   x += swizzle_xor16_f64(x);
   return x;
 }
@@ -471,17 +471,18 @@ __device__ __forceinline__ double half_sums_transposed(const double (&red)[2 * R
 // The score of row j (< R) in lane j from transposed (dot, ss) sums: the ss of row j sits R
 // lanes after its dot (quad_perm [2,3,2,3] for R = 2, [1,1,3,3] for R = 1).
 template <int R>
-__device__ __forceinline__ Score score_from_transposed(double x, int r, double eps) {
-  const double ss = dpp_f64<R == 2 ? 0xEE : 0xF5>(x, 0.0);
-  return score_from_sums(x, ss, r, eps);
+__device__ __forceinline__ Score score_from_transposed(double x, double rinv_r, double eps) {
+  const double ss = dpp_f64_all<R == 2 ? 0xEE : 0xF5>(x);
+  return score_from_sums(x, ss, rinv_r, eps);
 }
 
 // Row-local sums for R = 1 or 2 tile rows when the spread key sits in lanes 0..31: the sums of
 // the wave's first half are the rows' sums. Lane j (< R) returns row j's score.
 template <int R>
-__device__ __forceinline__ Score row_scores_rowlocal(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_rowlocal(const double (&red)[2 * R], int lane,
+                                                      double rinv_r,
                                                       double eps) {
-  return score_from_transposed<R>(half_sums_transposed<R>(red, lane), r, eps);
+  return score_from_transposed<R>(half_sums_transposed<R>(red, lane), rinv_r, eps);
 }
 
 // Sums over the whole wave of R = 1 or 2 rows' (q . k, k . k) pairs: the halves' transposed
@@ -508,17 +509,17 @@ __device__ __forceinline__ void wave_sums_transposed16(const double (&v)[16], in
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const double keep = b0 ? v[8 + k] : v[k], send = b0 ? v[k] : v[8 + k];
-    w[k] = keep + dpp_f64<kDppXor1>(send, 0.0);
+    w[k] = keep + dpp_f64_all<kDppXor1>(send);
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const double keep = b1 ? w[4 + k] : w[k], send = b1 ? w[k] : w[4 + k];
-    u[k] = keep + dpp_f64<kDppXor2>(send, 0.0);
+    u[k] = keep + dpp_f64_all<kDppXor2>(send);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) u[k] += dpp_f64<kRor4>(u[k], 0.0);
+  for (int k = 0; k < 4; ++k) u[k] += dpp_f64_all<kRor4>(u[k]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) u[k] += dpp_f64<kRor8>(u[k], 0.0);
+  for (int k = 0; k < 4; ++k) u[k] += dpp_f64_all<kRor8>(u[k]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) u[k] += swizzle_xor16_f64(u[k]);
 #pragma unroll
@@ -536,16 +537,18 @@ __device__ __forceinline__ int transposed_index(int lane) {
 // wave_sums_transposed. Lane j (< R) returns row j's score; other lanes return values of no
 // meaning.
 template <int R>
-__device__ __forceinline__ Score row_scores_wave(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_wave(const double (&red)[2 * R], int lane,
+                                                  double rinv_r,
                                                   double eps) {
-  return score_from_transposed<R>(wave_sums_transposed<R>(red, lane), r, eps);
+  return score_from_transposed<R>(wave_sums_transposed<R>(red, lane), rinv_r, eps);
 }
 
 // Scores of the R rows of a tile from their reduced (q . k, k . k) pairs, one row per lane:
 // lane j < R returns z of row j (lanes >= R return row 0's), so the square root and the
 // division run once for all rows.
 template <int R>
-__device__ __forceinline__ Score row_scores_to_lanes(const double (&red)[2 * R], int lane, int r,
+__device__ __forceinline__ Score row_scores_to_lanes(const double (&red)[2 * R], int lane,
+                                                      double rinv_r,
                                                       double eps) {
   double dot = red[0], ss = red[1];
 #pragma unroll
@@ -555,7 +558,7 @@ __device__ __forceinline__ Score row_scores_to_lanes(const double (&red)[2 * R],
       ss = red[2 * j + 1];
     }
   }
-  return score_from_sums(dot, ss, r, eps);
+  return score_from_sums(dot, ss, rinv_r, eps);
 }
 
 template <typename IO, int VEC, int NU>

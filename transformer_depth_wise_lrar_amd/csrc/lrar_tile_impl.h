@@ -119,8 +119,9 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     if constexpr (kSep) return keys.ld[i];
     else return 0;
   };
-  // Width of the mean of squares in the key's RMS: the key, or the whole row for the control.
-  const int nrm = MODE == kTileFullRms ? p.d : p.r;
+  // 1 / width of the mean of squares in the key's RMS: the key, or the whole row for the
+  // control.
+  const double rinv_nrm = 1.0 / static_cast<double>(MODE == kTileFullRms ? p.d : p.r);
   constexpr bool kMerge = MODE == kTileMerge || MODE == kTileMergeAcc;
   const auto set_tile = [&](TileGeom& t, int64_t tile) {
     t = g;
@@ -273,11 +274,11 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
     }
     if constexpr (KS > 0 && ROWRED && R <= 2) {
       // the spread key sits in lanes 0..31 of every wave of the row
-      return row_scores_rowlocal<R>(red, lane, nrm, p.eps);
+      return row_scores_rowlocal<R>(red, lane, rinv_nrm, p.eps);
     } else if constexpr (KS > 0) {
       lanes_sums_dpp(red, gp);  // every wave of the row holds the whole spread key
     } else if constexpr (WPR == 1 && R <= 2) {
-      return row_scores_wave<R>(red, lane, nrm, p.eps);
+      return row_scores_wave<R>(red, lane, rinv_nrm, p.eps);
     } else if constexpr (R <= 2) {
       // the row's waves each reduce their own sums, then add all waves' in a fixed order (so
       // every wave of the row gets bitwise the same score)
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
         parity ^= 1;
       }
     }
-    return row_scores_to_lanes<R>(red, lane, nrm, p.eps);
+    return row_scores_to_lanes<R>(red, lane, rinv_nrm, p.eps);
   };
 
   // Keeps the scores (and reciprocal RMS) of source i for the weights and saved statistics.
@@ -624,10 +625,13 @@ constexpr int deep_min_sources(int nu, int mode) {
 // Tiles per row group in one launch of a one-pass spread-key read. Over a long launch the waves
 // drift apart, the window of rows they read together widens, and HBM serves it more slowly:
 // at 64 tiles per group such reads measured 4-7 % slower than the same reads cut into
-// launches of 16 tiles per group (d = 1024 to 7168, 9 sources). Reads with the key taken from
-// the row units, the two-pass read and the merges measured 2-10 % slower cut at 12 tiles per
-// group, and reads with the key in the row units -3 to +2 % at 16, so they run as one launch.
-constexpr int64_t kMaxTilesPerGroup = 16;
+// launches of 16 tiles per group (d = 1024 to 7168, 9 sources). Launches of 8 tiles per group
+// measured 1-2 % faster again for key pieces of up to 8 elements (d = 2048, r = 16 and 64, 9 and
+// 10 sources; d = 7168, r = 64) but 1-2 % slower for the 16-element pieces (r = 512), and 4
+// slower for both. Reads with the key taken from the row units, the two-pass read and the
+// merges measured 2-10 % slower cut at 12 tiles per group, and reads with the key in the row
+// units -3 to +2 % at 16, so they run as one launch.
+constexpr int64_t max_tiles_per_group(int ks) { return ks >= 16 ? 16 : 8; }
 constexpr bool cut_into_launches(int mode, int ks) {
   return ks > 0 && (mode == kTileOnline || mode == kTileKeys);
 }
@@ -655,15 +659,17 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   const int per_cu = cached_per_cu;
   // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
   // each launch runs in one round and the groups' tile counts differ by at most one. A
-  // one-pass spread-key read is cut into launches of at most kMaxTilesPerGroup tiles per group
-  // (see there); any other read is one launch.
+  // one-pass spread-key read is cut into launches of at most max_tiles_per_group tiles per
+  // group (see there), every launch but the last giving each resident group the same count;
+  // any other read is one launch.
   const int64_t resident = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock / WPR;
   const int64_t tiles = (p.T + R - 1) / R;
+  const int64_t per_group_all = (tiles + resident - 1) / resident;
   const int64_t launches =
       cut_into_launches(MODE, KS)
-          ? ((tiles + resident - 1) / resident + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup
+          ? (per_group_all + max_tiles_per_group(KS) - 1) / max_tiles_per_group(KS)
           : 1;
-  const int64_t per_launch = (tiles + launches - 1) / launches;
+  const int64_t per_launch = ((per_group_all + launches - 1) / launches) * resident;
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
   ReadParams pc = p;
   for (int64_t t0 = 0; t0 < tiles; t0 += per_launch) {
