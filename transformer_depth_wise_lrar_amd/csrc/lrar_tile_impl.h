@@ -622,25 +622,33 @@ constexpr int deep_min_sources(int nu, int mode) {
   return nu <= 2 && mode != kTileKeys ? kDeepMinSourcesNarrow : kDeepMinSources;
 }
 
-// Tiles per row group in one launch of a one-pass spread-key read. Over a long launch the waves
-// drift apart, the window of rows they read together widens, and HBM serves it more slowly:
-// at 64 tiles per group such reads measured 4-7 % slower than the same reads cut into
-// launches of 16 tiles per group (d = 1024 to 7168, 9 sources). Launches of 8 tiles per group
-// measured 1-2 % faster again for key pieces of up to 8 elements (d = 2048, r = 16 and 64, 9 and
-// 10 sources; d = 7168, r = 64) but 1-2 % slower for the 16-element pieces (r = 512), and 4
-// slower for both. Reads with the key taken from the row units, the two-pass read and the
-// merges measured 2-10 % slower cut at 12 tiles per group, and reads with the key in the row
-// units -3 to +2 % at 16, so they run as one launch.
-constexpr int64_t max_tiles_per_group(int ks) { return ks >= 16 ? 16 : 8; }
-constexpr bool cut_into_launches(int mode, int ks) {
-  return ks > 0 && (mode == kTileOnline || mode == kTileKeys);
+// Reads of 16-element spread key pieces (r = 257..512) keep one source in flight: their
+// per-source float64 scoring covers the load latency, and a deeper ring only adds requests
+// that HBM then serves less efficiently (r = 512, d = 2048, 10 sources: 6 % faster than three
+// ahead, 4 % faster than two). Pieces of 4 and 8 elements measured 4-5 % slower with one.
+constexpr bool spread_single(int ks, int mode) { return ks >= 16 && mode == kTileOnline; }
+
+// Tiles per row group in one launch of a one-pass read. Over a long launch the waves drift
+// apart, the window of rows they read together widens, and HBM serves it more slowly. Spread-key
+// reads: at 64 tiles per group they measured 4-7 % slower than cut into launches of 16 tiles per
+// group (d = 1024 to 7168, 9 sources), and 8 tiles per group measured 1-2 % faster again (d =
+// 2048, r = 16 and 64; d = 7168, r = 64); 4 was slower. Keys read from the row units of one
+// wave (rows of up to 4 chunks): 8 tiles per group measured 4 % faster than one launch (r = d =
+// 2048); where several waves share a row (d = 7168) such cuts measured 3-7 % slower, as did
+// the two-pass read and the merges (2-10 % at 12 tiles per group), so those run as one launch.
+constexpr int64_t kMaxTilesPerGroup = 8;
+constexpr bool cut_into_launches(int mode, int ks, int wpr) {
+  return (ks > 0 && (mode == kTileOnline || mode == kTileKeys)) ||
+         (ks == 0 && mode == kTileOnline && wpr == 1);
 }
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, int MODE,
           typename ACC, bool DEEP = false, bool KA = false>
 hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
-  constexpr int PF = DEEP ? kDeepPrefetch : (key_fills_slots(KS, TU, NU) ? 1 : tile_prefetch(NU));
+  constexpr int PF = spread_single(KS, MODE) || key_fills_slots(KS, TU, NU)
+                         ? 1
+                         : (DEEP ? kDeepPrefetch : tile_prefetch(NU));
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC, KA>;
   const int ub = (p.d - p.r) / VEC;
   const int nur = (p.d + VEC - 1) / VEC;
@@ -658,16 +666,16 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   }
   const int per_cu = cached_per_cu;
   // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
-  // each launch runs in one round and the groups' tile counts differ by at most one. A
-  // one-pass spread-key read is cut into launches of at most max_tiles_per_group tiles per
-  // group (see there), every launch but the last giving each resident group the same count;
-  // any other read is one launch.
+  // each launch runs in one round and the groups' tile counts differ by at most one. The reads
+  // of cut_into_launches are cut into launches of at most kMaxTilesPerGroup tiles per group,
+  // every launch but the last giving each resident group the same count; any other read is one
+  // launch.
   const int64_t resident = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock / WPR;
   const int64_t tiles = (p.T + R - 1) / R;
   const int64_t per_group_all = (tiles + resident - 1) / resident;
   const int64_t launches =
-      cut_into_launches(MODE, KS)
-          ? (per_group_all + max_tiles_per_group(KS) - 1) / max_tiles_per_group(KS)
+      cut_into_launches(MODE, KS, WPR)
+          ? (per_group_all + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup
           : 1;
   const int64_t per_launch = ((per_group_all + launches - 1) / launches) * resident;
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
@@ -690,7 +698,7 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
 template <typename IO, int VEC, int NU, int KS, bool ROWRED, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_spread(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr ((MODE == kTileOnline || MODE == kTileKeys || MODE == kTileTwoPass) && NU >= 2 &&
-                NU <= 4) {
+                NU <= 4 && !spread_single(KS, MODE)) {
     if (p.n >= deep_min_sources(NU, MODE))
       return launch_tile_t<IO, VEC, NU, 1, KS, ROWRED, WPR, MODE, ACC, true>(p, kt, s);
   }
