@@ -370,9 +370,11 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
   // Ring of PF + 1 stages: the item PF ahead is loading while the current one is folded in.
   // Loops over the ring are unrolled by PF + 1 so that every stage index is a constant and no
   // stage is copied (a copy would wait for its loads). Exact loads (see load_stage_exact) for
-  // keys read from the row units and for the two-deep ring; spread keys through the three-deep
-  // ring keep the branchy loads.
-  constexpr bool kExact = KS == 0 || PF < 3;
+  // keys read from the row units and for the one- and two-deep rings; spread keys through the
+  // three-deep ring, and the drained one-ahead reads of short pieces (spread_drained, the only
+  // one-deep ring over 4 slots with such pieces), keep the branchy loads.
+  constexpr bool kDrained = MODE == kTileOnline && KS > 0 && KS < 16 && NU == 4 && PF == 1;
+  constexpr bool kExact = !kDrained && (KS == 0 || PF < 3);
   Stage<IO, VEC, NU, R, KS> ring[PF + 1];
 
   if constexpr (MODE == kTileTwoPass) {
@@ -622,21 +624,35 @@ constexpr int deep_min_sources(int nu, int mode) {
   return nu <= 2 && mode != kTileKeys ? kDeepMinSourcesNarrow : kDeepMinSources;
 }
 
-// Reads of 16-element spread key pieces (r = 257..512) keep one source in flight: their
-// per-source float64 scoring covers the load latency, and a deeper ring only adds requests
-// that HBM then serves less efficiently (r = 512, d = 2048, 10 sources: 6 % faster than three
-// ahead, 4 % faster than two). Pieces of 4 and 8 elements measured 4-5 % slower with one.
+// How much a read keeps in flight matters beyond covering the load latency: a plain stream of
+// the same traffic (10 sources, d = 2048) ran 0.81 of peak with one source in flight per wave
+// and short launches, 0.75 with three. HBM serves fewer, better-ordered requests faster.
+//
+// Reads of 16-element spread key pieces (r = 257..512) keep one source in flight, loaded exactly:
+// their per-source float64 scoring covers the load latency (r = 512, d = 2048, 10 sources: 6 %
+// faster than three ahead, 4 % faster than two; 9 % faster than the same ring with branchy
+// loads). Pieces of 4 and 8 elements measured 4-5 % slower that way.
 constexpr bool spread_single(int ks, int mode) { return ks >= 16 && mode == kTileOnline; }
+// One-pass reads of many sources whose short pieces (up to 8 elements) sit on rows of 4 or more
+// unit slots fetch one source ahead with branchy loads, whose wait for the oldest stage is a
+// wait for every load in flight: each source is drained before it is folded, the pattern of the
+// plain stream above. Against the three-deep ring: 1-2 % faster at d = 2048 (r = 16, 64; 9 and 10
+// sources) and 3 % at d = 7168 (r = 64, 9 sources). Rows of 1-2 slots (d <= 1024) measured
+// 2-6 % slower that way and keep their rings.
+constexpr bool spread_drained(int ks, int nu, int mode, bool deep) {
+  return mode == kTileOnline && deep && ks > 0 && ks < 16 && nu == 4;
+}
 
 // Tiles per row group in one launch of a one-pass read. Over a long launch the waves drift
 // apart, the window of rows they read together widens, and HBM serves it more slowly. Spread-key
 // reads: at 64 tiles per group they measured 4-7 % slower than cut into launches of 16 tiles per
 // group (d = 1024 to 7168, 9 sources), and 8 tiles per group measured 1-2 % faster again (d =
-// 2048, r = 16 and 64; d = 7168, r = 64); 4 was slower. Keys read from the row units of one
-// wave (rows of up to 4 chunks): 8 tiles per group measured 4 % faster than one launch (r = d =
-// 2048); where several waves share a row (d = 7168) such cuts measured 3-7 % slower, as did
-// the two-pass read and the merges (2-10 % at 12 tiles per group), so those run as one launch.
-constexpr int64_t kMaxTilesPerGroup = 8;
+// 2048, r = 16 and 64; d = 7168, r = 64); the drained reads above take 4 (as did the plain
+// stream). Keys read from the row units of one wave (rows of up to 4 chunks): 8 tiles per group
+// measured 4 % faster than one launch (r = d = 2048) and 3 % faster than 4; where several waves
+// share a row (d = 7168) such cuts measured 3-7 % slower, as did the two-pass read and the
+// merges (2-10 % at 12 tiles per group), so those run as one launch.
+constexpr int64_t max_tiles_per_group(bool drained) { return drained ? 4 : 8; }
 constexpr bool cut_into_launches(int mode, int ks, int wpr) {
   return (ks > 0 && (mode == kTileOnline || mode == kTileKeys)) ||
          (ks == 0 && mode == kTileOnline && wpr == 1);
@@ -646,7 +662,8 @@ template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, in
           typename ACC, bool DEEP = false, bool KA = false>
 hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
-  constexpr int PF = spread_single(KS, MODE) || key_fills_slots(KS, TU, NU)
+  constexpr bool kDrained = spread_drained(KS, NU, MODE, DEEP);
+  constexpr int PF = spread_single(KS, MODE) || key_fills_slots(KS, TU, NU) || kDrained
                          ? 1
                          : (DEEP ? kDeepPrefetch : tile_prefetch(NU));
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC, KA>;
@@ -667,7 +684,7 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   const int per_cu = cached_per_cu;
   // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
   // each launch runs in one round and the groups' tile counts differ by at most one. The reads
-  // of cut_into_launches are cut into launches of at most kMaxTilesPerGroup tiles per group,
+  // of cut_into_launches are cut into launches of at most max_tiles_per_group tiles per group,
   // every launch but the last giving each resident group the same count; any other read is one
   // launch.
   const int64_t resident = static_cast<int64_t>(per_cu) * device_cus() * kWavesPerBlock / WPR;
@@ -675,7 +692,7 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   const int64_t per_group_all = (tiles + resident - 1) / resident;
   const int64_t launches =
       cut_into_launches(MODE, KS, WPR)
-          ? (per_group_all + kMaxTilesPerGroup - 1) / kMaxTilesPerGroup
+          ? (per_group_all + max_tiles_per_group(kDrained) - 1) / max_tiles_per_group(kDrained)
           : 1;
   const int64_t per_launch = ((per_group_all + launches - 1) / launches) * resident;
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
