@@ -24,8 +24,11 @@ until two consecutive windows of six launches agree (the LR-AttnRes paper's App.
 rule: coefficient of variation <= 1 % in each window, medians within 0.5 %, at most 30
 windows); `rooflines_wide` prices the bf16 forward at d >= 2048 the same way as `roofline`;
 `ceilings` holds a plain streaming read and copy measured the same way, and the write rate
-and per-read mix ceilings derived from them; `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workload.
+and per-read mix ceilings derived from them, and `ceilings.streams` the same-traffic streams
+(lrar_mix_stream: the read's n rows in and one out per token with next to no arithmetic, in the
+fastest of a sweep of launch shapes) that each d >= 2048 row and the headline's largest site are
+also priced against; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -469,6 +472,61 @@ def ceilings(torch, lrar, ev):
     return dict(read=read, copy=copy, write_GBps_derived=round(W, 1) if W else None)
 
 
+# Shapes of the same-traffic streams: the headline's largest site and the bf16 forward at
+# d >= 2048 (T, d, n).
+STREAM_SHAPES = ((16 * 1024, 1024, 49), (16 * 4096, 2048, 10), (16 * 4096, 2048, 9),
+                 (32768, 7168, 9))
+STREAM_LAUNCHES = [(w, p, c) for w in (4, 8, 12) for p in (1, 2) for c in (0, 2, 4, 8)]
+
+
+def stream_slots(d):
+    """Units a lane for the same-traffic stream of width d: whole rows in one group up to 16 units
+    a lane (d <= 8192), else groups of 4."""
+    nur = d // 8
+    for u in (2, 4, 8, 16):
+        if nur <= 64 * u:
+            return (u,) if u <= 4 else (4, u)
+    return (4,)
+
+
+def stream_ceilings(torch, lrar, ev):
+    """The read's traffic as a plain stream (lrar_mix_stream: n bf16 rows in, one out per
+    token, next to no arithmetic) for each shape of STREAM_SHAPES: every launch shape of
+    STREAM_LAUNCHES (waves per CU, sources loaded together, rows per wave per launch), with the
+    units a lane of stream_slots, is timed
+    over 4 launches, and the fastest is then timed like the rows. What HBM gives this mix of
+    reads and writes, measured rather than derived."""
+    out = {}
+    for T, d, n in STREAM_SHAPES:
+        srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=9000 + d + n, dtype=torch.bfloat16)
+        dst = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        nbytes = fwd_bytes(T, d, n, 2)
+        best = None
+        shapes = [(w, pdep, u, c) for w, pdep, c in STREAM_LAUNCHES for u in stream_slots(d)
+                  if pdep * u <= 16]
+        for w, pdep, u, c in shapes:
+            call = lrar.lrar_mix_stream(srcs, out=dst, waves_per_cu=w, depth=pdep, slots=u,
+                                        rows_per_wave=c, prepare=True)
+            tm = Timer(torch)
+            ev()
+            call()
+            for _ in range(4):
+                ev()
+                tm.run(call)
+            ms = _median(tm.collect_ms())
+            if best is None or ms < best[0]:
+                best = (ms, w, pdep, u, c)
+        _, w, pdep, u, c = best
+        ms = time_calls(torch, ev, lrar.lrar_mix_stream(srcs, out=dst, waves_per_cu=w, depth=pdep,
+                                                        slots=u, rows_per_wave=c, prepare=True))
+        e = row_entry(ms, nbytes)
+        e["launch"] = dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c)
+        out[f"d{d}_n{n}"] = e
+        del srcs, dst
+        torch.cuda.empty_cache()
+    return out
+
+
 def mix_ceiling(ceil, n):
     """Streaming ceiling of a read of n sources that writes one row per n rows read."""
     if not ceil:
@@ -519,13 +577,17 @@ def wide_rooflines(rows, ceil, digest):
         ms = e.get("mean_ms", e["ms"])
         achieved = nbytes / (ms * 1e-3) / 1e9
         mix = mix_ceiling(ceil, n) if ceil else None
+        st = (ceil or {}).get("streams", {}).get(f"d{d}_n{n}")
+        sg = st["GBps"] if st else None
         out.append(dict(workload=f"{group.replace('_', ' ')}: T={T} d={d} r={r} n={n}, bf16",
                         row=f"{group}/{key}", bound="hbm", achieved=round(achieved, 1),
                         peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
                         traffic=traffic_entry(digest, f"{group}/{key}"),
                         algorithmic_bytes_per_launch=nbytes, avg_launch_us=round(ms * 1e3, 3),
                         mix_ceiling_GBps=round(mix, 1) if mix else None,
-                        frac_of_mix_ceiling=round(achieved / mix, 4) if mix else None))
+                        frac_of_mix_ceiling=round(achieved / mix, 4) if mix else None,
+                        stream_ceiling_GBps=sg,
+                        frac_of_stream_ceiling=round(achieved / sg, 4) if sg else None))
     return out
 
 
@@ -574,6 +636,9 @@ def main():
         ceil = ceilings(torch, lrar, ev)
         log(f"bench: ceilings read {ceil['read']['GBps']:.0f} GB/s, copy "
             f"{ceil['copy']['GBps']:.0f} GB/s, write (derived) {ceil['write_GBps_derived']} GB/s")
+        ceil["streams"] = stream_ceilings(torch, lrar, ev)
+        log("bench: same-traffic streams " + ", ".join(
+            f"{k} {v['GBps']:.0f} GB/s" for k, v in ceil["streams"].items()))
     rows = {}
     want = None if args.rows is None else set(args.rows.split(","))
     if not args.no_rows:
@@ -601,6 +666,12 @@ def main():
                         algorithmic_bytes_per_launch=round(bytes_launch),
                         avg_launch_us=round(avg_launch_s * 1e6, 3),
                         launches_per_step=len(deep))
+        st49 = (ceil or {}).get("streams", {}).get(f"d{FULL['d']}_n{h['S']}")
+        if st49:
+            site49 = h["sites"].get(str(h["S"]), {}).get("GBps")
+            roofline["stream_ceiling_n49_GBps"] = st49["GBps"]
+            roofline["site_n49_frac_of_stream_ceiling"] = (
+                round(site49 / st49["GBps"], 4) if site49 else None)
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")

@@ -332,6 +332,29 @@ def test_read_stream_rejects(L):
     assert L.lrar_read_stream(FAKE, 0, None, None) == lrar.LRAR_OK
 
 
+def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=4, rows=4,
+        ptr=FAKE):
+    p = (ctypes.c_void_p * max(n, 1))(*([ptr] * max(n, 1)))
+    l = (ctypes.c_int64 * max(n, 1))(*([ld] * max(n, 1)))
+    return L.lrar_mix_stream(T, d, n, p, l, out, out_ld, waves, depth, slots, rows, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=-1), dict(d=0), dict(d=12, ld=16, out_ld=16), dict(n=0), dict(n=65), dict(ld=4),
+    dict(ld=12, d=8), dict(ptr=FAKE + 8), dict(out=None), dict(out_ld=4), dict(out=FAKE * 2 + 8),
+    dict(out_ld=12), dict(waves=0), dict(waves=3), dict(waves=36), dict(depth=0), dict(depth=3),
+    dict(depth=8), dict(rows=-1), dict(out=FAKE), dict(out=FAKE + 16, T=4), dict(slots=0),
+    dict(slots=3), dict(slots=32), dict(slots=16, depth=2), dict(slots=8, depth=4),
+])
+def test_mix_stream_rejects(L, kw):
+    assert mix(L, **kw) == lrar.LRAR_ERR_INVALID, kw
+
+
+def test_mix_stream_empty_is_ok(L):
+    assert mix(L, T=0) == lrar.LRAR_OK
+    assert mix(L, T=0, out=None) == lrar.LRAR_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lrar, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(lrar, "_lib", None)

@@ -1,6 +1,7 @@
-"""Reads of many rows: the one-pass spread-key reads are cut into several launches over
-consecutive row ranges (at most a fixed number of tiles per row group each); reads with the
-key in the row units and merges run as one launch over the same rows.
+"""Reads of many rows: the one-pass spread-key reads, and the one-pass reads whose key comes
+from the row units of one wave, are cut into several launches over consecutive row ranges (at
+most a fixed number of tiles per row group each); other reads and merges run as one launch over
+the same rows.
 
 These tests fill the outputs with NaN first and then check that every row was written, that
 every row's weights sum to 1, and that rows on both sides of the launch boundaries (and the

@@ -91,13 +91,15 @@ def lib():
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
             L.lrar_read_stream.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+            L.lrar_mix_stream.argtypes = [_i64, _i32, _i32, _vpp, _i64p, _vp, _i64, _i32, _i32,
+                                          _i32, _i32, _vp]
             L.lrar_read_stream_sink_bytes.argtypes = []
             L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
             for fn in ("lrar_forward", "lrar_forward_save", "lrar_backward_saved",
                        "lrar_forward_fullrms", "lrar_forward_keys",
                        "lrar_forward_stats", "lrar_merge", "lrar_merge_accumulate",
                        "lrar_backward", "lrar_backward_grad", "lrar_backward_noalloc",
-                       "lrar_copy", "lrar_read_stream"):
+                       "lrar_copy", "lrar_read_stream", "lrar_mix_stream"):
                 getattr(L, fn).restype = ctypes.c_int
             L.lrar_status_string.argtypes = [ctypes.c_int]
             L.lrar_status_string.restype = ctypes.c_char_p
@@ -113,8 +115,8 @@ def exported_symbols() -> list[str]:
             "lrar_forward_keys", "lrar_forward_stats",
             "lrar_merge", "lrar_merge_accumulate", "lrar_backward", "lrar_backward_grad",
             "lrar_backward_noalloc", "lrar_backward_workspace_size", "lrar_copy", "lrar_read_stream",
-            "lrar_read_stream_sink_bytes", "lrar_status_string", "lrar_last_error",
-            "lrar_version"]
+            "lrar_read_stream_sink_bytes", "lrar_mix_stream", "lrar_status_string",
+            "lrar_last_error", "lrar_version"]
 
 
 class Prepared:
@@ -522,6 +524,23 @@ def lrar_copy(dst, src, stream=None, prepare: bool = False):
         raise ValueError("dst and src must have the same byte size")
     args = (dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream))
     return _run(lib().lrar_copy, args, dst, (dst, src), prepare)
+
+
+def lrar_mix_stream(srcs: Sequence, out=None, waves_per_cu: int = 8, depth: int = 1,
+                    slots: int = 4, rows_per_wave: int = 4, stream=None, prepare: bool = False):
+    """A plain stream with the traffic of a bf16 read of srcs (n bf16 tensors [T, d]): writes their
+    mean, rounded to bf16, to out [T, d]. The reference kernel for the same-traffic bandwidth
+    ceiling; the launch shape (waves per CU, sources loaded together, 16-byte units a lane,
+    rows per wave per launch) is the caller's. Returns out."""
+    torch = _torch()
+    ptrs, lds, io, T, d = _src_table(srcs, LRAR_BF16)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=srcs[0].device)
+    _need(out, (T, d), torch.bfloat16, "out")
+    op, old = _rows(out, "out")
+    args = (T, d, len(srcs), ptrs, lds, op, old, int(waves_per_cu), int(depth), int(slots),
+            int(rows_per_wave), _stream(stream))
+    return _run(lib().lrar_mix_stream, args, out, (srcs, out), prepare)
 
 
 def lrar_read_stream(src, sink=None, stream=None, prepare: bool = False):

@@ -832,6 +832,45 @@ lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* st
                        fn);
 }
 
+lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
+                            const int64_t* src_ld, void* out, int64_t out_ld, int32_t waves_per_cu,
+                            int32_t depth, int32_t slots, int32_t rows_per_wave, void* stream) {
+  const char* fn = "lrar_mix_stream";
+  if (T < 0) return fail(LRAR_ERR_INVALID, "%s: T = %lld < 0", fn, (long long)T);
+  if (d < 8 || d % 8 != 0)
+    return fail(LRAR_ERR_INVALID, "%s: d = %d must be a positive multiple of 8", fn, d);
+  if (waves_per_cu < 4 || waves_per_cu > 32 || waves_per_cu % 4 != 0)
+    return fail(LRAR_ERR_INVALID, "%s: waves_per_cu = %d must be 4, 8, ..., 32", fn, waves_per_cu);
+  if (depth != 1 && depth != 2 && depth != 4)
+    return fail(LRAR_ERR_INVALID, "%s: depth = %d must be 1, 2 or 4", fn, depth);
+  if (slots != 2 && slots != 4 && slots != 8 && slots != 16)
+    return fail(LRAR_ERR_INVALID, "%s: slots = %d must be 2, 4, 8 or 16", fn, slots);
+  if (depth * slots > 16)
+    return fail(LRAR_ERR_INVALID, "%s: depth x slots = %d exceeds 16 units a lane", fn,
+                depth * slots);
+  if (rows_per_wave < 0)
+    return fail(LRAR_ERR_INVALID, "%s: rows_per_wave = %d < 0", fn, rows_per_wave);
+  lrar::SrcList S;
+  bool vec_ok = true;
+  lrar_status st = check_sources(fn, T, d, LRAR_BF16, n, 1, src, src_ld, S, vec_ok);
+  if (st != LRAR_OK) return st;
+  if (T == 0) return LRAR_OK;
+  if (out == nullptr) return fail(LRAR_ERR_INVALID, "%s: out is null", fn);
+  if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
+  if (!stride_ok(out_ld, 2)) return stride_fail(fn, "out_ld", out_ld);
+  if (!vec_ok || !aligned16(out) || out_ld % 8 != 0)
+    return fail(LRAR_ERR_INVALID,
+                "%s: every row start must be 16-byte aligned (pointers, and strides in 8s)", fn);
+  Regions R;
+  add_sources(R, S, n, T, d, 2, "src");
+  R.output(rows_region(out, T, out_ld, d, 2, "out"));
+  st = check_disjoint(fn, R);
+  if (st != LRAR_OK) return st;
+  return device_status(lrar::launch_mix_stream(S, n, T, d, out, out_ld, waves_per_cu, depth, slots,
+                                               rows_per_wave, static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
 const char* lrar_status_string(lrar_status s) {
   switch (s) {
     case LRAR_OK: return "ok";
@@ -903,6 +942,104 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
   hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
                      static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
   return hipGetLastError();
+}
+
+// The read's traffic with next to no arithmetic: for the rows [r0, r1), the n bf16 source rows
+// are read and their mean (float32 sums in source order, rounded to nearest even) written as
+// one bf16 row. A wave takes rows in bands (row r0 + w + k * waves, as the read's tiles) and a
+// row in groups of up to NU chunks of 64 16-byte units, NU units a lane; DEPTH sources are loaded
+// before any is added, and the loads are waited for together.
+template <int DEPTH, int NU>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NU >= 16 ? 2 : 1)))
+void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1,
+                                                       int nur, u32x4* __restrict__ out,
+                                                       int64_t out_ld16, float w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block();
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  for (int64_t row = r0 + wave; row < r1; row += waves) {
+    for (int g = 0; g < nur; g += NU * kWave) {
+      float acc[NU][8];
+#pragma unroll
+      for (int k = 0; k < NU; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+      for (int i0 = 0; i0 < n; i0 += DEPTH) {
+        Unit<bf16_bits, 8> v[DEPTH][NU];
+#pragma unroll
+        for (int b = 0; b < DEPTH; ++b) {
+          const int i = i0 + b < n ? i0 + b : n - 1;
+          const bf16_bits* rp = static_cast<const bf16_bits*>(src.ptr[i]) + row * src.ld[i];
+#pragma unroll
+          for (int k = 0; k < NU; ++k) {
+            const int u = g + k * kWave + lane;
+            if (u < nur) v[b][k].load(rp + static_cast<int64_t>(u) * 8);
+            else v[b][k].zero();
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < DEPTH; ++b) {
+          const float wb = i0 + b < n ? w : 0.f;
+#pragma unroll
+          for (int k = 0; k < NU; ++k) {
+            float x[8];
+            v[b][k].get(x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][e] = fmaf(wb, x[e], acc[k][e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = g + k * kWave + lane;
+        if (u < nur) {
+          Unit<bf16_bits, 8> y;
+          y.set(acc[k]);
+          __builtin_nontemporal_store(y.raw, out + row * out_ld16 + u);
+        }
+      }
+    }
+  }
+}
+
+template <int DEPTH, int NU>
+void launch_mix_stream_t(const SrcList& src, int n, int64_t r0, int64_t r1, int nur, void* out,
+                         int64_t out_ld, float w, unsigned blocks, hipStream_t s) {
+  hipLaunchKernelGGL((k_mix_stream<DEPTH, NU>), dim3(blocks), dim3(kBlock), 0, s, src, n, r0, r1,
+                     nur, static_cast<u32x4*>(out), out_ld / 8, w);
+}
+
+hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, void* out,
+                             int64_t out_ld, int waves_per_cu, int depth, int slots,
+                             int rows_per_wave, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = static_cast<int64_t>(cus) * waves_per_cu / kWavesPerBlock;
+  const int64_t span = rows_per_wave > 0 ? blocks * kWavesPerBlock * rows_per_wave : T;
+  const int nur = d / 8;
+  const float w = 1.0f / static_cast<float>(n);
+  const unsigned g = static_cast<unsigned>(blocks);
+  for (int64_t r0 = 0; r0 < T; r0 += span) {
+    const int64_t r1 = r0 + span < T ? r0 + span : T;
+    const int key = 10 * depth + slots;
+    switch (key) {
+      case 12: launch_mix_stream_t<1, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 14: launch_mix_stream_t<1, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 18: launch_mix_stream_t<1, 8>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 26: launch_mix_stream_t<1, 16>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 22: launch_mix_stream_t<2, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 24: launch_mix_stream_t<2, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 28: launch_mix_stream_t<2, 8>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 42: launch_mix_stream_t<4, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 44: launch_mix_stream_t<4, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStream_t s) {
