@@ -23,6 +23,8 @@
 // of the workspace; the reduction kernels of lrar_backward.hip then sum the workgroups' rows in
 // a fixed order, so dq is bitwise reproducible.
 
+#include <type_traits>
+
 #include "lrar_device.h"
 #include "lrar_launch.h"
 #include "lrar_tile.h"
@@ -388,7 +390,12 @@ hipError_t launch_bwd_tile_t(const BwdParams& p, double* block_dq, int max_block
     cached_lds = lds;
   }
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
-  int64_t blocks = static_cast<int64_t>(cached_per_cu) * device_cus_bwd();
+  // float32 gradients write twice the bytes they read: with at most 2 workgroups (8 waves) per
+  // CU, fewer write streams are open at once, which measured 2 % faster than the 3 that fit
+  // (d = 4096, r = 1024, 10 sources); bf16 gradients measured 8 % slower so capped, and 1
+  // workgroup per CU was 24-37 % slower for both.
+  const int per_cu = std::is_same<GIO, float>::value && cached_per_cu > 2 ? 2 : cached_per_cu;
+  int64_t blocks = static_cast<int64_t>(per_cu) * device_cus_bwd();
   const int64_t need = (p.T + kGroupsPerBlock - 1) / kGroupsPerBlock;
   if (blocks > need) blocks = need;
   if (blocks > max_blocks) blocks = max_blocks;
