@@ -174,7 +174,7 @@ def headline(torch, lrar, args, ev):
     gbps = bytes_step / (step_ms * 1e-3) / 1e9
     sites = {str(n): dict(ms=round(site_ms[n - 1], 5),
                           GBps=round(fwd_bytes(T, d, n, 2) / (site_ms[n - 1] * 1e-3) / 1e9, 1))
-             for n in (1, 2, 5, 9, 13, 25, 37, 49)}
+             for n in SAMPLED_SITES}
     del srcs, calls
     return dict(step_ms=step_ms, step_cv=step_cv, wall_ms=wall * 1e3 / args.steps, gbps=gbps,
                 T=T, S=S,
@@ -472,10 +472,11 @@ def ceilings(torch, lrar, ev):
     return dict(read=read, copy=copy, write_GBps_derived=round(W, 1) if W else None)
 
 
-# Shapes of the same-traffic streams: the headline's largest site and the bf16 forward at
+# Shapes of the same-traffic streams: the headline's sampled sites and the bf16 forward at
 # d >= 2048 (T, d, n).
-STREAM_SHAPES = ((16 * 1024, 1024, 49), (16 * 4096, 2048, 10), (16 * 4096, 2048, 9),
-                 (32768, 7168, 9))
+SAMPLED_SITES = (1, 2, 5, 9, 13, 25, 37, 49)
+STREAM_SHAPES = tuple((16 * 1024, 1024, n) for n in SAMPLED_SITES) + (
+    (16 * 4096, 2048, 10), (16 * 4096, 2048, 9), (32768, 7168, 9))
 STREAM_LAUNCHES = [(w, p, c) for w in (4, 8, 12) for p in (1, 2) for c in (0, 2, 4, 8)]
 
 
@@ -696,6 +697,12 @@ def main():
             "sites": h["sites"],
             "mix_ceiling_n49_GBps": round(mix_ceiling(ceil, 49), 1) if ceil else None,
         })
+    if h is not None and ceil is not None:
+        for n, e in h["sites"].items():
+            st = ceil.get("streams", {}).get(f"d{FULL['d']}_n{n}")
+            if st:
+                e["stream_ceiling_GBps"] = st["GBps"]
+                e["frac_of_stream_ceiling"] = round(e["GBps"] / st["GBps"], 4)
     line.update({
         "roofline": roofline,
         "rooflines_wide": wide_rooflines(rows, ceil, digest),
