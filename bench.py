@@ -1,7 +1,7 @@
 """Throughput of the LR-AttnRes depth-mix read on one MI355X (gfx950).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
-                    [--rows NAME,...] [--fixed-reps K]
+                    [--rows NAME,...] [--fixed-reps K] [--no-streams]
 
 One step is the depth mix of one forward pass of the full-routing model shape of the
 LR-AttnRes paper's 0.5B runs (§4.1: d = 1024, 24 layers = 48 sub-layer writes, so 49
@@ -604,6 +604,8 @@ def main():
                     help="skip the headline step (profiling runs of single rows)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the streaming ceilings (profiling runs of single rows)")
+    ap.add_argument("--no-streams", action="store_true",
+                    help="skip the sweep of same-traffic streams (profiling runs)")
     ap.add_argument("--rows", default=None,
                     help="comma-separated row groups to run (default: all): "
                          + ", ".join(n for n, _ in ROW_GROUPS))
@@ -637,9 +639,10 @@ def main():
         ceil = ceilings(torch, lrar, ev)
         log(f"bench: ceilings read {ceil['read']['GBps']:.0f} GB/s, copy "
             f"{ceil['copy']['GBps']:.0f} GB/s, write (derived) {ceil['write_GBps_derived']} GB/s")
-        ceil["streams"] = stream_ceilings(torch, lrar, ev)
-        log("bench: same-traffic streams " + ", ".join(
-            f"{k} {v['GBps']:.0f} GB/s" for k, v in ceil["streams"].items()))
+        if not args.no_streams:
+            ceil["streams"] = stream_ceilings(torch, lrar, ev)
+            log("bench: same-traffic streams " + ", ".join(
+                f"{k} {v['GBps']:.0f} GB/s" for k, v in ceil["streams"].items()))
     rows = {}
     want = None if args.rows is None else set(args.rows.split(","))
     if not args.no_rows:
