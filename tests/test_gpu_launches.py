@@ -36,11 +36,13 @@ def rows64(t, rows):
 
 
 @pytest.mark.parametrize("d,r,n,T", [
-    (2048, 64, 9, 65536 + 37),     # cut: one wave per row, spread key, three-deep ring
+    (2048, 64, 9, 65536 + 37),     # cut: one wave per row, short spread key, drained one ahead
     (2048, 64, 1, 65536 + 37),     # cut: one source, the two-stage tile alternation
-    (7168, 64, 3, 32768 + 5),      # cut: four waves per row
-    (2048, 512, 3, 65536 + 37),    # one launch: key from the row units
-    (7168, 1792, 3, 32768 + 5),    # one launch: the row's four waves exchange key sums
+    (7168, 64, 3, 32768 + 5),      # cut: four waves per row, two-deep ring
+    (7168, 64, 9, 32768 + 5),      # cut: four waves per row, drained one ahead
+    (2048, 512, 3, 65536 + 37),    # cut: 16-element key pieces, one source ahead
+    (2048, 2048, 3, 65536 + 37),   # cut: key from the row units of one wave
+    (7168, 1792, 3, 32768 + 5),    # one launch: the row's two waves exchange key sums
 ])
 def test_every_row_written(d, r, n, T):
     eps = 1e-6
@@ -79,7 +81,8 @@ def test_merge_every_row_written():
     parity.assert_read(rows64(out, rows), h_ref, a_ref, s64, "bf16", f"merge T={T}")
 
 
-@pytest.mark.parametrize("d,r,n,T", [(2048, 64, 9, 65536 + 37), (7168, 64, 3, 32768 + 5)])
+@pytest.mark.parametrize("d,r,n,T", [(2048, 64, 9, 65536 + 37), (7168, 64, 3, 32768 + 5),
+                                     (2048, 2048, 3, 65536 + 37)])
 def test_cut_read_matches_uncut_slices(d, r, n, T):
     """Each row's result depends on that row alone: rows of a read cut into several launches
     are bitwise equal to the same rows read on their own (a slice short enough for one
