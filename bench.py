@@ -592,6 +592,36 @@ def wide_rooflines(rows, ceil, digest):
     return out
 
 
+def block_schedules(rows):
+    """The largest block of the production-width shape (d = 7168, 12 read sites, each reading the
+    8 cached sources and the intra-block partial sum) under both schedules, from the measured
+    rows: single-pass, 12 reads of 9 sources; two-phase, one Phase 1 of the 12 site queries
+    against the 8 cached sources, then 12 Phase-2 merges with the partial sum (fp32 or bf16
+    accumulators). Bytes are algorithmic; times the rows' medians."""
+    pr = rows.get("production_d7168")
+    if not pr:
+        return None
+    T, d, S = 32768, 7168, 12
+    out = {}
+    for r in (1792,):
+        sp = pr.get(f"single_pass_r{r}_n9_online")
+        if sp is None:
+            continue
+        e = {"single_pass": dict(ms=round(S * sp["ms"], 4),
+                                 GB=round(S * fwd_bytes(T, d, 9, 2) / 1e9, 2))}
+        for acc, ae in (("f32", 4), ("bf16", 2)):
+            p1 = pr.get(f"phase1_r{r}_ninter8_q{S}_acc{acc}")
+            p2 = pr.get(f"phase2_r{r}_acc{acc}")
+            if p1 is None or p2 is None:
+                continue
+            b1 = 2 * 8 * d * T + S * (ae * d + 8) * T
+            b2 = (ae * d + 8 + 2 * d + 2 * d) * T
+            e[f"two_phase_acc{acc}"] = dict(ms=round(p1["ms"] + S * p2["ms"], 4),
+                                            GB=round((b1 + S * b2) / 1e9, 2))
+        out[f"d{d}_r{r}_block_of_{S}_sites"] = e
+    return out
+
+
 def main():
     global FIXED_REPS
     ap = argparse.ArgumentParser()
@@ -706,6 +736,7 @@ def main():
             if st:
                 e["stream_ceiling_GBps"] = st["GBps"]
                 e["frac_of_stream_ceiling"] = round(e["GBps"] / st["GBps"], 4)
+    line.update({"schedules": block_schedules(rows)})
     line.update({
         "roofline": roofline,
         "rooflines_wide": wide_rooflines(rows, ceil, digest),
