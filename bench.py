@@ -37,6 +37,7 @@ import concurrent.futures as cf
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,13 +60,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(text: str) -> str:
+    """A HIP source without its comments and blank lines, each line stripped: what compiles."""
+    def keep(m):
+        t = m.group(0)
+        return "" if t.startswith("/") else t
+    lines = (ln.strip() for ln in _TOKENS.sub(keep, text).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest() -> str:
-    """sha256 over the HIP sources: counter figures taken on other sources are stale."""
+    """sha256 over the code of the HIP sources (comments and layout left out): counter figures
+    taken on other code are stale."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

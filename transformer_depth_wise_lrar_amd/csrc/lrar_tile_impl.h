@@ -607,11 +607,13 @@ constexpr int tile_prefetch(int nu) { return nu <= 4 ? 2 : 1; }
 // r = 1792 at d = 7168) but 4 % slower for a key in the last slot alone (r = 512, d = 2048).
 constexpr bool key_fills_slots(int ks, int tu, int nu) { return ks == 0 && nu == 4 && tu == nu; }
 
-// Reads of many sources keep one more source in flight: three sources ahead measured 8 %
+// Reads of many sources (DEEP) keep one more source in flight: three sources ahead measured 8 %
 // (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two for spread keys, in
 // both variants, and 9 % for the full-width-RMS control, at the price of a third wave per
-// SIMD. Reads of few sources, and slice keys taken from the row units (whose float64 scoring
-// already keeps the vector unit busy), keep the shallower ring.
+// SIMD. One-pass reads of short pieces on 4-slot rows now take the drained one-ahead ring
+// instead (spread_drained, below), which beat three ahead. Reads of few sources, and slice
+// keys taken from the row units (whose float64 scoring already keeps the vector unit busy),
+// keep the shallower ring.
 constexpr int kDeepPrefetch = 3;
 constexpr int kDeepMinSources = 8;
 // Reads with the key in the row's last columns, spread over the lanes, and two units per lane
@@ -633,8 +635,9 @@ constexpr int deep_min_sources(int nu, int mode) {
 // faster than three ahead, 4 % faster than two; 9 % faster than the same ring with branchy
 // loads). Pieces of 4 and 8 elements measured 4-5 % slower that way.
 constexpr bool spread_single(int ks, int mode) { return ks >= 16 && mode == kTileOnline; }
-// One-pass reads of many sources whose short pieces (up to 8 elements) sit on rows of 4 or more
-// unit slots fetch one source ahead with branchy loads, whose wait for the oldest stage is a
+// One-pass reads of many sources whose short pieces (up to 8 elements) sit on rows of 4 unit
+// slots (d = 1536..2048 per wave, and the 4-wave rows up to d = 8192) fetch one source ahead
+// with branchy loads, whose wait for the oldest stage is a
 // wait for every load in flight: each source is drained before it is folded, the pattern of the
 // plain stream above. Against the three-deep ring: 1-2 % faster at d = 2048 (r = 16, 64; 9 and 10
 // sources) and 3 % at d = 7168 (r = 64, 9 sources). Rows of 1-2 slots (d <= 1024) measured
