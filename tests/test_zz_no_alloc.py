@@ -67,6 +67,17 @@ def test_noalloc_wide_key_fewer_workgroups():
     check(*b, "f32", bitwise_dq=True)
 
 
+@pytest.mark.parametrize("grad", ["f32", "bf16"])
+def test_noalloc_element_path_twice(grad):
+    """Rows the element path serves (an unaligned width, and a width past a register tile with
+    an odd row stride): the one-wave-per-row backward with the scratch, twice in a row, equal to
+    the workspace entry point bit for bit."""
+    a = run_pair(257, 513, 200, 3, grad, False, seed=960)
+    check(*a, grad, bitwise_dq=True)
+    b = run_pair(70, 2561, 640, 2, grad, True, seed=970)
+    check(*b, grad, bitwise_dq=True)
+
+
 def test_noalloc_rejects_a_key_beyond_the_scratch():
     srcs = sources(1, 2048, 16384, "bf16", seed=940)
     q = query(16384, seed=941)
