@@ -609,11 +609,12 @@ constexpr bool key_fills_slots(int ks, int tu, int nu) { return ks == 0 && nu ==
 
 // Reads of many sources (DEEP) keep one more source in flight: three sources ahead measured 8 %
 // (d = 1024, 49 sources) and 5 % (d = 2048, 9 sources) faster than two for spread keys, in
-// both variants, and 9 % for the full-width-RMS control, at the price of a third wave per
-// SIMD. One-pass reads of short pieces on 4-slot rows now take the drained one-ahead ring
-// instead (spread_drained, below), which beat three ahead. Reads of few sources, and slice
-// keys taken from the row units (whose float64 scoring already keeps the vector unit busy),
-// keep the shallower ring.
+// both variants, at the price of a third wave per SIMD. One-pass reads of short pieces on
+// 4-slot rows now take the drained one-ahead ring instead (spread_drained, below), which beat
+// three ahead. Reads of few sources, and slice keys taken from the row units (whose float64
+// scoring already keeps the vector unit busy), keep the shallower ring. The full-width-RMS
+// control, which scores every column of the row in float64, keeps one source ahead: 7 % (13
+// sources) and 3 % (25) faster than three ahead, level at 49 (d = 1024).
 constexpr int kDeepPrefetch = 3;
 constexpr int kDeepMinSources = 8;
 // Reads with the key in the row's last columns, spread over the lanes, and two units per lane
@@ -666,7 +667,8 @@ template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int WPR, in
 hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   constexpr int R = tile_rows(NU);
   constexpr bool kDrained = spread_drained(KS, NU, MODE, DEEP);
-  constexpr int PF = spread_single(KS, MODE) || key_fills_slots(KS, TU, NU) || kDrained
+  constexpr int PF = MODE == kTileFullRms || spread_single(KS, MODE) ||
+                             key_fills_slots(KS, TU, NU) || kDrained
                          ? 1
                          : (DEEP ? kDeepPrefetch : tile_prefetch(NU));
   auto kern = k_read_tile<IO, VEC, NU, TU, KS, ROWRED, R, PF, WPR, MODE, ACC, KA>;
@@ -768,10 +770,6 @@ inline int spread_piece(const ReadParams& p, int vec) {
 template <typename IO, int VEC, int NU, int WPR, int MODE, typename ACC>
 hipError_t launch_tile_key(const ReadParams& p, const KeyTable<MODE>& kt, hipStream_t s) {
   if constexpr (MODE == kTileFullRms) {
-    if constexpr (NU >= 2 && NU <= 4) {
-      if (p.n >= kDeepMinSources)
-        return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC, true>(p, kt, s);
-    }
     return launch_tile_units<IO, VEC, NU, NU, WPR, MODE, ACC>(p, kt, s);
   } else if constexpr (MODE == kTileMergeAcc) {
     const int first_key_chunk = ((p.d - p.r) / VEC) / kWave;
