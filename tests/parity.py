@@ -136,14 +136,25 @@ def assert_dsrc_bf16(g64, g_ref, where="dsrc"):
 
 
 def dq_bound(srcs64, q, dout64, alpha, h, r, eps):
-    """sum_t sum_i |dz_ti| * max_j |kbar_tij| from oracle outputs alpha, h (for the dq tol)."""
+    """The dq tolerance in units of the 1e-5 bar (assert_dq takes 1e-5 times this; sums over row
+    chunks add): sum_t sum_i |dz_ti| max_j |kbar_tij|, plus 1e5 times the absolute error of
+    dz_ti = alpha_ti (s_ti - sbar_t) that float64 leaves on either side, where the two sides sum
+    s_ti = g_t . o_ti (d exact products) and sbar_t in different orders: at most
+    alpha_ti (d + 2) 2^-53 (S_ti + sum_j alpha_tj S_tj) with S_ti = sum_c |g_tc o_tic|. That term
+    only matters when the softmax saturates, where s_ti - sbar_t cancels to almost nothing and
+    dq is rounding noise (LR-AttnRes paper, App. B.3, Lemma 2)."""
     d = srcs64[0].shape[1]
     total = 0.0
+    gamma = (d + 2) * 2.0 ** -53
+    big = [np.sum(np.abs(dout64 * o), axis=1) for o in srcs64]        # S_ti
+    sbar_mag = sum(alpha[:, j] * big[j] for j in range(len(srcs64)))   # sum_j alpha_tj S_tj
     for i, o in enumerate(srcs64):
         dz = alpha[:, i] * np.sum(dout64 * (o - h), axis=1)
         k = o[:, d - r:]
         rho = np.sqrt(np.mean(k * k, axis=1) + eps)
-        total += float(np.sum(np.abs(dz) * np.max(np.abs(k), axis=1) / rho))
+        kmax = np.max(np.abs(k), axis=1) / rho
+        cancel = alpha[:, i] * gamma * (big[i] + sbar_mag)
+        total += float(np.sum((np.abs(dz) + 1e5 * cancel) * kmax))
     return total
 
 

@@ -79,3 +79,25 @@ def test_backward_wide_rows(d, r, io):
     """Rows shared by the four waves of a workgroup, up to the widest tile (32 chunks)."""
     srcs = sources(3, 19, d, io, seed=250, scale=(0.5, 4.0))
     check_backward(srcs, query(r, seed=251), r, 1e-6, False, f"wide d{d} r{r} {io}", seed=252)
+
+
+@pytest.mark.parametrize("d,io", [(4096, "bf16"), (8192, "f32"), (8200, "f32"), (16392, "bf16")])
+@pytest.mark.parametrize("r", [1, 2, 16])
+def test_backward_key_term_cancellation(d, r, io):
+    """Small keys parallel to the query: d z / d k_j = (q_j - (z / r) kbar_j) / rho is then
+    q_j eps / (|k|^2 / r + eps) / rho, a small difference of two large terms (LR-AttnRes paper,
+    App. B.3, Lemma 2; at r = 1 every key is parallel to q). With |k| / sqrt(r) in [0.01, 0.05]
+    and eps = 1e-6 the terms are 400-25000 times their difference, which float32 coefficients
+    of the two terms (one rounding each) do not resolve to the 1e-5 bar. Row tiles (up to 8192
+    fp32 / 16384 bf16 columns) and the one-wave-per-row path past them."""
+    T, n = 40, 4
+    qt = synth.queries(1, r, 1.0, 261, device="cpu")[0]
+    srcs = []
+    for i, s in enumerate(synth.values(n, T, d, io, 260 + d + r, scale=(0.5, 4.0), device="cpu")):
+        g = torch.Generator().manual_seed(270 + i)
+        mag = 0.01 + 0.04 * torch.rand((T, 1), generator=g)
+        sign = torch.where(torch.rand((T, 1), generator=g) < 0.5, -1.0, 1.0)
+        s[:, d - r:] = (mag * sign * (r ** 0.5) * qt / qt.norm()).to(s.dtype)
+        srcs.append(s.cuda())
+    check_backward(srcs, qt.cuda(), r, 1e-6, False, f"parallel small keys d{d} r{r} {io}",
+                   seed=262)

@@ -96,14 +96,21 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
     const double sbar = wave_sum((lane < p.n) ? a * s_mine : 0.0);
     const double dz = a * (s_mine - sbar);
     const float af = static_cast<float>(a);
-    const float c1f = static_cast<float>(dz / rho);                       // dz / rho
-    const float c2f = static_cast<float>(dz * z / (p.r * rho * rho));     // dz z / (r rho^2)
+    // d z / d k_j = (q_j - w k_j) / rho with w = z / (r rho). The difference cancels when r is
+    // small (at r = 1 it is q (1 - kbar^2), about q eps / k^2), so w is held as two floats
+    // w = wh + wl: q_j - wh k_j is taken by one fused multiply-add, whose single rounding
+    // falls on the small result, and (dz / rho) wl k_j is taken off the gradient after it.
+    const float c1f = static_cast<float>(dz / rho);  // dz / rho
+    const double wd = z / (p.r * rho);
+    const float whf = static_cast<float>(wd);
+    const float c1wlf = static_cast<float>(static_cast<double>(c1f) * (wd - static_cast<double>(whf)));
 
     // 3./4. source gradients and dq partials
     for (int i = 0; i < p.n; ++i) {
       const float ai = lane_f32(af, i);
       const float c1 = lane_f32(c1f, i);
-      const float c2 = lane_f32(c2f, i);
+      const float wh = lane_f32(whf, i);
+      const float c1wl = lane_f32(c1wlf, i);
       const IO* orow = static_cast<const IO*>(p.src.ptr[i]) + row * p.src.ld[i];
       GIO* drow = static_cast<GIO*>(p.dsrc.ptr[i]) + row * p.dsrc.ld[i];
       // columns before the key window: alpha_i g only
@@ -140,7 +147,8 @@ __global__ __launch_bounds__(kBlock) void k_backward(BwdParams p, double* __rest
               const int col = u * VEC + e;
               if (col >= c0) {
                 const float qv = p.q[col - c0];
-                v[e] += c1 * qv - c2 * x[e];
+                v[e] = fmaf(c1, fmaf(-wh, x[e], qv), v[e]);
+                v[e] = fmaf(-c1wl, x[e], v[e]);
                 dqa[t][e] = fmaf(c1, x[e], dqa[t][e]);
               }
             }

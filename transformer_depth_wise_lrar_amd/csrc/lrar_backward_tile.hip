@@ -199,15 +199,22 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
     const double sbar = wave_sum_dpp(lane < n ? a * si : 0.0);
     const double dz = a * (si - sbar);
     const float af = static_cast<float>(a);
-    const float c1f = static_cast<float>(dz * rinvi);                         // dz / rho
-    const float c2f = static_cast<float>(dz * zi * (rinvi * rinvi) * rinv_r);  // dz z / (r rho^2)
+    // d z / d k_j = (q_j - w k_j) / rho with w = z / (r rho). The difference cancels when r is
+    // small (at r = 1 it is q (1 - kbar^2), about q eps / k^2), so w is held as two floats
+    // w = wh + wl: q_j - wh k_j is taken by one fused multiply-add, whose single rounding
+    // falls on the small result, and (dz / rho) wl k_j is taken off the gradient after it.
+    const float c1f = static_cast<float>(dz * rinvi);  // dz / rho
+    const double wd = zi * rinvi * rinv_r;
+    const float whf = static_cast<float>(wd);
+    const float c1wlf = static_cast<float>(static_cast<double>(c1f) * (wd - static_cast<double>(whf)));
 
     // ---- pass B: source gradients (the key units from the LDS stash, or streamed through the
     // ring again when the stash would be too large)
     const auto store_b = [&](const Unit<IO, VEC> (&ku)[NU], int i) {
       const float ai = lane_f32(af, i);
       const float c1 = lane_f32(c1f, i);
-      const float c2 = lane_f32(c2f, i);
+      const float wh = lane_f32(whf, i);
+      const float c1wl = lane_f32(c1wlf, i);
       GIO* drow = static_cast<GIO*>(p.dsrc.ptr[i]) + row * p.dsrc.ld[i];
 #pragma unroll
       for (int k = 0; k < NU; ++k) {
@@ -218,14 +225,20 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
         if (k >= K0 && u >= g.ub && u < g.nur) {
           float x[VEC];
           ku[k].get(x);
+          if (u * VEC < g.c0) {
+            // the one unit that straddles the window's first column: the staged query is 0
+            // before it, so zeroing those source values leaves their columns alpha_i g alone
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+              if (u * VEC + e < g.c0) x[e] = 0.f;
+          }
           float qv[VEC];
           qst.get<VEC>(u - g.ub, qv);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            if (u * VEC + e >= g.c0) {
-              v[e] += c1 * qv[e] - c2 * x[e];
-              dqa[k >= K0 ? k - K0 : 0][e] = fmaf(c1, x[e], dqa[k >= K0 ? k - K0 : 0][e]);
-            }
+            v[e] = fmaf(c1, fmaf(-wh, x[e], qv[e]), v[e]);
+            v[e] = fmaf(-c1wl, x[e], v[e]);
+            dqa[k >= K0 ? k - K0 : 0][e] = fmaf(c1, x[e], dqa[k >= K0 ? k - K0 : 0][e]);
           }
         }
         if constexpr (kRunStores) {
