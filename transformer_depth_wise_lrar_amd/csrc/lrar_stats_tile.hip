@@ -4,9 +4,10 @@
 // valid).
 //
 // For up to kStatsMaxSrc cached sources and a group of up to kStatsMaxQ site queries:
-//   * one 768-thread workgroup per CU (12 wavefronts) shares one LDS copy of the group's
-//     queries, laid out from the first key unit's column (columns of that unit before the key
-//     hold zero), so each key element is dotted with every query of the group from LDS;
+//   * one workgroup per CU (12 wavefronts, or 16 for bf16 sources with bf16 accumulators)
+//     shares one LDS copy of the group's queries, laid out from the first key unit's column
+//     (columns of that unit before the key hold zero), so each key element is dotted with
+//     every query of the group from LDS;
 //   * each wave takes one token row at a time, rows dealt out in bands over all waves;
 //   * score pass: per source, the key units are taken kStatsKeySlots slots at a time; float64
 //     partial sums of q_s . k for every query s and of k . k accumulate per lane, and the
@@ -39,21 +40,28 @@ namespace lrar {
 
 namespace {
 
-constexpr int kStatsBlock = 768;
-constexpr int kStatsWaves = kStatsBlock / kWave;
+// Waves per workgroup (one workgroup per CU: the staged queries take most of the LDS). bf16
+// sources with bf16 accumulators fit 4 waves per SIMD (at most 128 registers) and run 16,
+// 3-6 % faster than 12 at d = 7168, r = 1792, 8 sources x 12 queries, and 32768 rows split
+// evenly over the 4096 waves; float32 accumulators of bf16 sources need more registers than
+// 4 waves allow, and float32 sources measured no faster with 16.
+constexpr int kStatsWavesMax = 16;
 static_assert(kStatsMaxQ <= 16 && kStatsMaxSrc % 4 == 0,
               "a query group fills at most the 16 rows of a matrix product, sources come in fours");
 // LDS a workgroup holds besides the staged queries (z_lds, w_lds)
 constexpr size_t kStatsStaticLds =
-    kStatsWaves * kStatsMaxQ * kStatsMaxSrc * (sizeof(double) + sizeof(float));
+    kStatsWavesMax * kStatsMaxQ * kStatsMaxSrc * (sizeof(double) + sizeof(float));
 
 }  // namespace
 
 // FULLQ: the group holds kStatsMaxQ queries, so no pass or store depends on the group's size
 // (with a smaller group, those branches leave the compiler unsure how many stores are in flight
 // and its waits for loads then also wait for stores).
-template <typename IO, int VEC, typename ACC, bool FULLQ>
-__global__ __launch_bounds__(kStatsBlock) void k_stats_tile(StatsParams p, int q0, int nq_arg) {
+template <typename IO, int VEC, typename ACC, bool FULLQ, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void k_stats_tile(StatsParams p, int q0, int nq_arg) {
+  constexpr int kStatsWaves = WAVES;
+  constexpr int kStatsBlock = WAVES * kWave;
+  static_assert(WAVES <= kStatsWavesMax, "the query group's LDS budget counts kStatsWavesMax");
   extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [nqg][rq]
   const int nqg = FULLQ ? kStatsMaxQ : nq_arg;
   // Scores of the wave's current row: z[s][i] for query s, source i; and their weights.
@@ -347,14 +355,16 @@ size_t lds_limit() {
   return lim;
 }
 
-template <typename IO, int VEC, typename ACC>
+template <typename IO, int VEC, typename ACC, int WAVES>
 hipError_t launch_stats_tile_t(const StatsParams& p, int qg, hipStream_t s) {
+  constexpr int kStatsWaves = WAVES;
+  constexpr int kStatsBlock = WAVES * kWave;
   const int ub = (p.d - p.r) / VEC;
   const int rq = p.d - ub * VEC;
   for (int q0 = 0; q0 < p.nq; q0 += qg) {
     const int nqg = (p.nq - q0) < qg ? (p.nq - q0) : qg;
-    auto kern = nqg == kStatsMaxQ ? k_stats_tile<IO, VEC, ACC, true>
-                                  : k_stats_tile<IO, VEC, ACC, false>;
+    auto kern = nqg == kStatsMaxQ ? k_stats_tile<IO, VEC, ACC, true, WAVES>
+                                  : k_stats_tile<IO, VEC, ACC, false, WAVES>;
     const size_t lds = static_cast<size_t>(nqg) * rq * sizeof(float);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStatsBlock, lds) !=
@@ -385,10 +395,10 @@ int stats_tile_query_group(int d, int r, int vec) {
 
 hipError_t launch_stats_tile(const StatsParams& p, int io_bf16, int acc_bf16, int qg,
                              hipStream_t s) {
-  if (io_bf16) return acc_bf16 ? launch_stats_tile_t<bf16_bits, 8, bf16_bits>(p, qg, s)
-                               : launch_stats_tile_t<bf16_bits, 8, float>(p, qg, s);
-  return acc_bf16 ? launch_stats_tile_t<float, 4, bf16_bits>(p, qg, s)
-                  : launch_stats_tile_t<float, 4, float>(p, qg, s);
+  if (io_bf16) return acc_bf16 ? launch_stats_tile_t<bf16_bits, 8, bf16_bits, 16>(p, qg, s)
+                               : launch_stats_tile_t<bf16_bits, 8, float, 12>(p, qg, s);
+  return acc_bf16 ? launch_stats_tile_t<float, 4, bf16_bits, 12>(p, qg, s)
+                  : launch_stats_tile_t<float, 4, float, 12>(p, qg, s);
 }
 
 }  // namespace lrar
