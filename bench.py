@@ -25,10 +25,10 @@ rule: coefficient of variation <= 1 % in each window, medians within 0.5 %, at m
 windows); `rooflines_wide` prices the bf16 forward at d >= 2048 the same way as `roofline`;
 `ceilings` holds a plain streaming read and copy measured the same way, and the write rate
 and per-read mix ceilings derived from them, and `ceilings.streams` the same-traffic streams
-(lrar_mix_stream: the read's n rows in and one out per token with next to no arithmetic, in the
-fastest of a sweep of launch shapes) that each d >= 2048 row and the headline's largest site are
-also priced against; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+(lrar_mix_stream: a kernel's rows in and out per token with next to no arithmetic, in the
+fastest of a sweep of launch shapes) that each d >= 2048 read, the headline's sites, Phase 1,
+the merges and the backward are also priced against (`frac_of_stream_ceiling`); `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -487,11 +487,35 @@ def ceilings(torch, lrar, ev):
 
 
 # Shapes of the same-traffic streams: the headline's sampled sites and the bf16 forward at
-# d >= 2048 (T, d, n).
+# d >= 2048 (T, d, n), one bf16 row out per n read.
 SAMPLED_SITES = (1, 2, 5, 9, 13, 25, 37, 49)
 STREAM_SHAPES = tuple((16 * 1024, 1024, n) for n in SAMPLED_SITES) + (
     (16 * 4096, 2048, 10), (16 * 4096, 2048, 9), (32768, 7168, 9))
 STREAM_LAUNCHES = [(w, p, c) for w in (4, 8, 12) for p in (1, 2) for c in (0, 2, 4, 8)]
+# The other kernels' traffic as streams: name -> (T, d, bf16 rows in, rows out, out dtype, the
+# rows it prices). A float32 row read counts as two bf16 rows (Phase 2's fp32 accumulator, the
+# backward's fp32 upstream gradient); Phase 1's m and l (8 bytes per query and row) and the
+# backward's dq are left out (under 0.03 % of the bytes).
+KERNEL_STREAMS = {
+    "phase1_d7168_8in_12f32out": (32768, 7168, 8, 12, "f32", [
+        ("production_d7168", "phase1_r1792_ninter8_q12_accf32")]),
+    "phase1_d7168_8in_12bf16out": (32768, 7168, 8, 12, "bf16", [
+        ("production_d7168", "phase1_r1792_ninter8_q12_accbf16")]),
+    "merge_d7168_3in_1out": (32768, 7168, 3, 1, "bf16", [
+        ("production_d7168", "phase2_r1792_accf32")]),
+    "merge_d7168_2in_1out": (32768, 7168, 2, 1, "bf16", [
+        ("production_d7168", "phase2_r1792_accbf16")]),
+    "fused_update_d7168_4in_2out": (32768, 7168, 4, 2, "bf16", [
+        ("production_d7168", "phase2_fused_update_r1792_accf32")]),
+    "fused_update_d7168_3in_2out": (32768, 7168, 3, 2, "bf16", [
+        ("production_d7168", "phase2_fused_update_r1792_accbf16")]),
+    "backward_d4096_12in_10f32out": (16384, 4096, 12, 10, "f32", [
+        ("backward_d4096", "backward_r1024_n10"), ("backward_d4096", "backward_saved_r1024_n10")]),
+    "backward_d4096_11in_10bf16out": (16384, 4096, 11, 10, "bf16", [
+        ("backward_d4096", "backward_bf16_grads_r1024_n10"),
+        ("backward_d4096", "backward_saved_bf16_grads_r1024_n10")]),
+}
+KERNEL_STREAM_LAUNCHES = [(w, p, c) for w in (4, 8, 12, 16, 24, 32) for p in (1, 2) for c in (0, 2, 4)]
 
 
 def stream_slots(d):
@@ -504,23 +528,16 @@ def stream_slots(d):
     return (4,)
 
 
-def stream_ceilings(torch, lrar, ev):
-    """The read's traffic as a plain stream (lrar_mix_stream: n bf16 rows in, one out per
-    token, next to no arithmetic) for each shape of STREAM_SHAPES: every launch shape of
-    STREAM_LAUNCHES (waves per CU, sources loaded together, rows per wave per launch), with the
-    units a lane of stream_slots, is timed
-    over 4 launches, and the fastest is then timed like the rows. What HBM gives this mix of
-    reads and writes, measured rather than derived."""
-    out = {}
-    for T, d, n in STREAM_SHAPES:
-        srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=9000 + d + n, dtype=torch.bfloat16)
-        dst = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
-        nbytes = fwd_bytes(T, d, n, 2)
-        best = None
-        shapes = [(w, pdep, u, c) for w, pdep, c in STREAM_LAUNCHES for u in stream_slots(d)
-                  if pdep * u <= 16]
-        for w, pdep, u, c in shapes:
-            call = lrar.lrar_mix_stream(srcs, out=dst, waves_per_cu=w, depth=pdep, slots=u,
+def best_stream(torch, lrar, ev, srcs, outs, launches, slots):
+    """Times lrar_mix_stream over every launch shape (waves per CU, sources loaded together,
+    rows per wave per launch) and units a lane, 4 launches each, then the fastest like the
+    rows: (its timing, its launch shape)."""
+    best = None
+    for w, pdep, c in launches:
+        for u in slots:
+            if pdep * u > 16:
+                continue
+            call = lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep, slots=u,
                                         rows_per_wave=c, prepare=True)
             tm = Timer(torch)
             ev()
@@ -531,15 +548,55 @@ def stream_ceilings(torch, lrar, ev):
             ms = _median(tm.collect_ms())
             if best is None or ms < best[0]:
                 best = (ms, w, pdep, u, c)
-        _, w, pdep, u, c = best
-        ms = time_calls(torch, ev, lrar.lrar_mix_stream(srcs, out=dst, waves_per_cu=w, depth=pdep,
-                                                        slots=u, rows_per_wave=c, prepare=True))
-        e = row_entry(ms, nbytes)
-        e["launch"] = dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c)
+    _, w, pdep, u, c = best
+    ms = time_calls(torch, ev, lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep,
+                                                    slots=u, rows_per_wave=c, prepare=True))
+    return ms, dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c)
+
+
+def stream_ceilings(torch, lrar, ev):
+    """Each kernel's traffic as a plain stream (lrar_mix_stream: n bf16 rows in and one or more
+    rows out per token, next to no arithmetic), in the fastest of a sweep of launch shapes:
+    what HBM gives that mix of reads and writes, measured rather than derived. The read's
+    mixes (STREAM_SHAPES: n rows in, one bf16 row out) sweep STREAM_LAUNCHES; Phase 1's, the
+    merges' and the backward's (KERNEL_STREAMS) sweep KERNEL_STREAM_LAUNCHES."""
+    out = {}
+    for T, d, n in STREAM_SHAPES:
+        srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=9000 + d + n, dtype=torch.bfloat16)
+        dst = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        ms, launch = best_stream(torch, lrar, ev, srcs, dst, STREAM_LAUNCHES, stream_slots(d))
+        e = row_entry(ms, fwd_bytes(T, d, n, 2))
+        e["launch"] = launch
         out[f"d{d}_n{n}"] = e
         del srcs, dst
         torch.cuda.empty_cache()
+    for name, (T, d, n, nout, odt, _) in KERNEL_STREAMS.items():
+        srcs = gen_sources(torch, n, T, d, (0.5, 4.0), seed=9100 + d + n, dtype=torch.bfloat16)
+        tdt, oe = (torch.float32, 4) if odt == "f32" else (torch.bfloat16, 2)
+        outs = [torch.empty((T, d), dtype=tdt, device="cuda") for _ in range(nout)]
+        ms, launch = best_stream(torch, lrar, ev, srcs, outs, KERNEL_STREAM_LAUNCHES,
+                                 stream_slots(d))
+        e = row_entry(ms, (2 * n + oe * nout) * d * T)
+        e["launch"] = launch
+        out[name] = e
+        del srcs, outs
+        torch.cuda.empty_cache()
     return out
+
+
+def kernel_stream_fractions(rows, ceil):
+    """Each priced row's GB/s as a share of its kernel stream's."""
+    streams = (ceil or {}).get("streams", {})
+    for name, (_, _, _, _, _, priced) in KERNEL_STREAMS.items():
+        st = streams.get(name)
+        if not st:
+            continue
+        for group, key in priced:
+            e = rows.get(group, {}).get(key)
+            if e is not None:
+                e["stream"] = name
+                e["stream_ceiling_GBps"] = st["GBps"]
+                e["frac_of_stream_ceiling"] = round(e["GBps"] / st["GBps"], 4)
 
 
 def mix_ceiling(ceil, n):
@@ -750,6 +807,7 @@ def main():
             if st:
                 e["stream_ceiling_GBps"] = st["GBps"]
                 e["frac_of_stream_ceiling"] = round(e["GBps"] / st["GBps"], 4)
+    kernel_stream_fractions(rows, ceil)
     line.update({"schedules": block_schedules(rows)})
     line.update({
         "roofline": roofline,

@@ -284,18 +284,24 @@ lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* st
 /* Bytes of the sink lrar_read_stream writes. */
 size_t lrar_read_stream_sink_bytes(void);
 
-/* A plain stream with the traffic of a bf16 read: for each of T rows, reads the n bf16 source
- * rows of d columns (src as for lrar_forward, n in [1, LRAR_MAX_SOURCES]) and writes their mean,
- * summed in float32 in source order and rounded to nearest even, to out [T, out_ld] (bf16).
- * Not part of the read: it is the reference kernel for the same-traffic bandwidth ceiling a read
- * is measured against. d, every src_ld and out_ld are multiples of 8 and every pointer is
- * 16-byte aligned; out may not overlap a source. The launch shape is the caller's:
- * waves_per_cu (4, 8, ..., 32) waves per compute unit; slots (2, 4, 8 or 16) 16-byte units a
- * lane, so a wave takes a row in groups of 64 x slots units; depth (1, 2 or 4, with
- * depth x slots <= 16) sources loaded together before any is added; and rows_per_wave (> 0:
- * launches of that many rows per wave; 0: one launch). Errors as for lrar_forward. */
+/* A plain stream with a kernel's traffic: for each of T rows, reads the n bf16 source rows of d
+ * columns (src as for lrar_forward, n in [1, LRAR_MAX_SOURCES]) and writes their mean, summed
+ * in float32 in source order, to each of nout output rows: out[j] is a device [T, out_ld[j]]
+ * matrix of out_dtype (LRAR_F32: the float32 sum; LRAR_BF16: rounded to nearest even),
+ * 1 <= nout <= LRAR_MAX_SOURCES; out and out_ld are HOST arrays of nout entries. One bf16
+ * output gives a read's traffic; more outputs or float32 ones give the write-heavy mixes of
+ * Phase 1 (8 rows in, 12 accumulator rows out per token) and the backward. Not part of the
+ * read: it is the reference kernel for the same-traffic bandwidth ceiling a kernel is measured
+ * against. d and every src_ld are multiples of 8, every out_ld a multiple of 16 bytes, and
+ * every pointer is 16-byte aligned; no output may overlap a source or another output. The
+ * launch shape is the caller's: waves_per_cu (4, 8, ..., 32) waves per compute unit; slots
+ * (2, 4, 8 or 16) 16-byte units a lane, so a wave takes a row in groups of 64 x slots units;
+ * depth (1, 2 or 4, with depth x slots <= 16) sources loaded together before any is added; and
+ * rows_per_wave (> 0: launches of that many rows per wave; 0: one launch). Errors as for
+ * lrar_forward. */
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
-                            const int64_t* src_ld, void* out, int64_t out_ld, int32_t waves_per_cu,
+                            const int64_t* src_ld, int32_t nout, void* const* out,
+                            const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
                             int32_t depth, int32_t slots, int32_t rows_per_wave, void* stream);
 
 /* Static description of a status code. */

@@ -333,10 +333,17 @@ def test_read_stream_rejects(L):
 
 
 def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=4, rows=4,
-        ptr=FAKE):
+        ptr=FAKE, odt=lrar.LRAR_BF16, nout=None, table=True):
+    """lrar_mix_stream through ctypes; out and out_ld may be one value or a list per output."""
     p = (ctypes.c_void_p * max(n, 1))(*([ptr] * max(n, 1)))
     l = (ctypes.c_int64 * max(n, 1))(*([ld] * max(n, 1)))
-    return L.lrar_mix_stream(T, d, n, p, l, out, out_ld, waves, depth, slots, rows, None)
+    outs = out if isinstance(out, list) else [out]
+    lds = out_ld if isinstance(out_ld, list) else [out_ld] * len(outs)
+    o = (ctypes.c_void_p * len(outs))(*outs)
+    ol = (ctypes.c_int64 * len(outs))(*lds)
+    k = len(outs) if nout is None else nout
+    return L.lrar_mix_stream(T, d, n, p, l, k, o if table else None, ol if table else None, odt,
+                             waves, depth, slots, rows, None)
 
 
 @pytest.mark.parametrize("kw", [
@@ -345,6 +352,13 @@ def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=
     dict(out_ld=12), dict(waves=0), dict(waves=3), dict(waves=36), dict(depth=0), dict(depth=3),
     dict(depth=8), dict(rows=-1), dict(out=FAKE), dict(out=FAKE + 16, T=4), dict(slots=0),
     dict(slots=3), dict(slots=32), dict(slots=16, depth=2), dict(slots=8, depth=4),
+    dict(nout=0), dict(nout=65), dict(odt=2), dict(table=False),
+    dict(odt=lrar.LRAR_F32, out_ld=10),                         # 40-byte rows: not in 16s
+    dict(odt=lrar.LRAR_F32, d=16, ld=16, out_ld=18),            # 72-byte rows: not in 16s
+    dict(out=[FAKE * 2, FAKE * 2 + 16]),                        # two outputs overlap
+    dict(out=[FAKE * 2, FAKE * 3], odt=lrar.LRAR_F32, out_ld=[8, 8], T=4,
+         ptr=FAKE * 3 + 16),                                    # an output overlaps a source
+    dict(out=[FAKE * 2, None]),
 ])
 def test_mix_stream_rejects(L, kw):
     assert mix(L, **kw) == lrar.LRAR_ERR_INVALID, kw
@@ -352,7 +366,9 @@ def test_mix_stream_rejects(L, kw):
 
 def test_mix_stream_empty_is_ok(L):
     assert mix(L, T=0) == lrar.LRAR_OK
+    assert mix(L, T=0, odt=lrar.LRAR_F32, out_ld=12) == lrar.LRAR_OK
     assert mix(L, T=0, out=None) == lrar.LRAR_OK
+    assert mix(L, T=0, table=False) == lrar.LRAR_OK
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -91,8 +91,8 @@ def lib():
             L.lrar_backward_workspace_size.restype = ctypes.c_size_t
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
             L.lrar_read_stream.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
-            L.lrar_mix_stream.argtypes = [_i64, _i32, _i32, _vpp, _i64p, _vp, _i64, _i32, _i32,
-                                          _i32, _i32, _vp]
+            L.lrar_mix_stream.argtypes = [_i64, _i32, _i32, _vpp, _i64p, _i32, _vpp, _i64p,
+                                          _i32, _i32, _i32, _i32, _i32, _vp]
             L.lrar_read_stream_sink_bytes.argtypes = []
             L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
             for fn in ("lrar_forward", "lrar_forward_save", "lrar_backward_saved",
@@ -528,19 +528,30 @@ def lrar_copy(dst, src, stream=None, prepare: bool = False):
 
 def lrar_mix_stream(srcs: Sequence, out=None, waves_per_cu: int = 8, depth: int = 1,
                     slots: int = 4, rows_per_wave: int = 4, stream=None, prepare: bool = False):
-    """A plain stream with the traffic of a bf16 read of srcs (n bf16 tensors [T, d]): writes their
-    mean, rounded to bf16, to out [T, d]. The reference kernel for the same-traffic bandwidth
+    """A plain stream with a kernel's traffic: reads srcs (n bf16 tensors [T, d]) and writes
+    their mean to each tensor of out (a tensor [T, d], or a list of them, all float32 or all
+    bf16; default one bf16 tensor). The reference kernel for the same-traffic bandwidth
     ceiling; the launch shape (waves per CU, sources loaded together, 16-byte units a lane,
     rows per wave per launch) is the caller's. Returns out."""
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, LRAR_BF16)
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=srcs[0].device)
-    _need(out, (T, d), torch.bfloat16, "out")
-    op, old = _rows(out, "out")
-    args = (T, d, len(srcs), ptrs, lds, op, old, int(waves_per_cu), int(depth), int(slots),
-            int(rows_per_wave), _stream(stream))
-    return _run(lib().lrar_mix_stream, args, out, (srcs, out), prepare)
+    outs = list(out) if isinstance(out, (list, tuple)) else [out]
+    if not outs or len(outs) > MAX_SOURCES:
+        raise ValueError(f"1 to {MAX_SOURCES} outputs")
+    odt = outs[0].dtype
+    if odt not in (torch.float32, torch.bfloat16):
+        raise TypeError("outputs must be float32 or bfloat16")
+    optrs = (ctypes.c_void_p * len(outs))()
+    olds = (ctypes.c_int64 * len(outs))()
+    for j, o in enumerate(outs):
+        _need(o, (T, d), odt, f"out[{j}]")
+        optrs[j], olds[j] = _rows(o, f"out[{j}]")
+    args = (T, d, len(srcs), ptrs, lds, len(outs), optrs, olds,
+            LRAR_F32 if odt == torch.float32 else LRAR_BF16, int(waves_per_cu), int(depth),
+            int(slots), int(rows_per_wave), _stream(stream))
+    return _run(lib().lrar_mix_stream, args, out, (srcs, outs), prepare)
 
 
 def lrar_read_stream(src, sink=None, stream=None, prepare: bool = False):

@@ -833,7 +833,8 @@ lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* st
 }
 
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
-                            const int64_t* src_ld, void* out, int64_t out_ld, int32_t waves_per_cu,
+                            const int64_t* src_ld, int32_t nout, void* const* out,
+                            const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
                             int32_t depth, int32_t slots, int32_t rows_per_wave, void* stream) {
   const char* fn = "lrar_mix_stream";
   if (T < 0) return fail(LRAR_ERR_INVALID, "%s: T = %lld < 0", fn, (long long)T);
@@ -850,24 +851,40 @@ lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* 
                 depth * slots);
   if (rows_per_wave < 0)
     return fail(LRAR_ERR_INVALID, "%s: rows_per_wave = %d < 0", fn, rows_per_wave);
+  if (nout < 1 || nout > LRAR_MAX_SOURCES)
+    return fail(LRAR_ERR_INVALID, "%s: nout = %d outside [1, %d]", fn, nout, LRAR_MAX_SOURCES);
+  if (!dtype_ok(out_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown out dtype", fn);
   lrar::SrcList S;
   bool vec_ok = true;
   lrar_status st = check_sources(fn, T, d, LRAR_BF16, n, 1, src, src_ld, S, vec_ok);
   if (st != LRAR_OK) return st;
   if (T == 0) return LRAR_OK;
-  if (out == nullptr) return fail(LRAR_ERR_INVALID, "%s: out is null", fn);
-  if (out_ld < d) return fail(LRAR_ERR_INVALID, "%s: out_ld = %lld < d", fn, (long long)out_ld);
-  if (!stride_ok(out_ld, 2)) return stride_fail(fn, "out_ld", out_ld);
-  if (!vec_ok || !aligned16(out) || out_ld % 8 != 0)
-    return fail(LRAR_ERR_INVALID,
-                "%s: every row start must be 16-byte aligned (pointers, and strides in 8s)", fn);
+  if (out == nullptr || out_ld == nullptr)
+    return fail(LRAR_ERR_INVALID, "%s: null out table", fn);
+  const size_t oe = esize(out_dtype);
+  const int64_t per16 = static_cast<int64_t>(16 / oe);
+  lrar::DstList O;
   Regions R;
   add_sources(R, S, n, T, d, 2, "src");
-  R.output(rows_region(out, T, out_ld, d, 2, "out"));
+  for (int j = 0; j < nout; ++j) {
+    if (out[j] == nullptr) return fail(LRAR_ERR_INVALID, "%s: out[%d] is null", fn, j);
+    if (out_ld[j] < d)
+      return fail(LRAR_ERR_INVALID, "%s: out_ld[%d] = %lld < d", fn, j, (long long)out_ld[j]);
+    if (!stride_ok(out_ld[j], oe)) return stride_fail(fn, "out_ld", out_ld[j]);
+    if (!aligned16(out[j]) || out_ld[j] % per16 != 0) vec_ok = false;
+    O.ptr[j] = out[j];
+    O.ld[j] = out_ld[j];
+    R.output(rows_region(out[j], T, out_ld[j], d, oe, "out", j));
+  }
+  if (!vec_ok)
+    return fail(LRAR_ERR_INVALID,
+                "%s: every row start must be 16-byte aligned (pointers, and strides in 16 bytes)",
+                fn);
   st = check_disjoint(fn, R);
   if (st != LRAR_OK) return st;
-  return device_status(lrar::launch_mix_stream(S, n, T, d, out, out_ld, waves_per_cu, depth, slots,
-                                               rows_per_wave, static_cast<hipStream_t>(stream)),
+  return device_status(lrar::launch_mix_stream(S, n, T, d, O, nout, out_dtype == LRAR_F32,
+                                               waves_per_cu, depth, slots, rows_per_wave,
+                                               static_cast<hipStream_t>(stream)),
                        fn);
 }
 
@@ -944,16 +961,17 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
   return hipGetLastError();
 }
 
-// The read's traffic with next to no arithmetic: for the rows [r0, r1), the n bf16 source rows
-// are read and their mean (float32 sums in source order, rounded to nearest even) written as
-// one bf16 row. A wave takes rows in bands (row r0 + w + k * waves, as the read's tiles) and a
-// row in groups of up to NU chunks of 64 16-byte units, NU units a lane; DEPTH sources are loaded
-// before any is added, and the loads are waited for together.
-template <int DEPTH, int NU>
+// A kernel's traffic with next to no arithmetic: for the rows [r0, r1), the n bf16 source rows
+// are read and their mean (float32 sums in source order) written to each of the nout output
+// rows, as float32 (F32OUT) or rounded to nearest-even bf16. A wave takes rows in bands (row
+// r0 + w + k * waves, as the read's tiles) and a row in groups of up to NU chunks of 64 16-byte
+// units, NU units a lane; DEPTH sources are loaded before any is added, and the loads are
+// waited for together. One bf16 output is a read's traffic; more outputs, or float32 ones,
+// give the write-heavy mixes of Phase 1 and the backward.
+template <int DEPTH, int NU, bool F32OUT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NU >= 16 ? 2 : 1)))
-void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1,
-                                                       int nur, u32x4* __restrict__ out,
-                                                       int64_t out_ld16, float w) {
+void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList out, int nout,
+                  float w) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block();
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -972,9 +990,23 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1,
           const bf16_bits* rp = static_cast<const bf16_bits*>(src.ptr[i]) + row * src.ld[i];
 #pragma unroll
           for (int k = 0; k < NU; ++k) {
-            const int u = g + k * kWave + lane;
-            if (u < nur) v[b][k].load(rp + static_cast<int64_t>(u) * 8);
-            else v[b][k].zero();
+            if constexpr (F32OUT) {
+              // two runs of 4 columns, 256 apart: each 16-byte float32 store then lands next
+              // to its neighbour lanes' (1 KiB a store instruction). d is a multiple of 8, so
+              // a run lies wholly inside the row or wholly past it.
+              const int c0 = (g + k * kWave) * 8 + 4 * lane;
+              const u32x2 lo = c0 < nur * 8
+                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + c0))
+                  : u32x2{0u, 0u};
+              const u32x2 hi = c0 + 256 < nur * 8
+                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + c0 + 256))
+                  : u32x2{0u, 0u};
+              v[b][k].raw = u32x4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+              const int u = g + k * kWave + lane;
+              if (u < nur) v[b][k].load(rp + static_cast<int64_t>(u) * 8);
+              else v[b][k].zero();
+            }
           }
         }
 #pragma unroll
@@ -989,13 +1021,27 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1,
           }
         }
       }
+      for (int j = 0; j < nout; ++j) {
 #pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = g + k * kWave + lane;
-        if (u < nur) {
-          Unit<bf16_bits, 8> y;
-          y.set(acc[k]);
-          __builtin_nontemporal_store(y.raw, out + row * out_ld16 + u);
+        for (int k = 0; k < NU; ++k) {
+          if constexpr (F32OUT) {
+            const int c0 = (g + k * kWave) * 8 + 4 * lane;
+            float* op = static_cast<float*>(out.ptr[j]) + row * out.ld[j] + c0;
+            if (c0 < nur * 8)
+              out_store(f32x4{acc[k][0], acc[k][1], acc[k][2], acc[k][3]},
+                        reinterpret_cast<f32x4*>(op));
+            if (c0 + 256 < nur * 8)
+              out_store(f32x4{acc[k][4], acc[k][5], acc[k][6], acc[k][7]},
+                        reinterpret_cast<f32x4*>(op + 256));
+          } else {
+            const int u = g + k * kWave + lane;
+            if (u < nur) {
+              Unit<bf16_bits, 8> y;
+              y.set(acc[k]);
+              y.store(static_cast<bf16_bits*>(out.ptr[j]) + row * out.ld[j] +
+                      static_cast<int64_t>(u) * 8);
+            }
+          }
         }
       }
     }
@@ -1003,14 +1049,19 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1,
 }
 
 template <int DEPTH, int NU>
-void launch_mix_stream_t(const SrcList& src, int n, int64_t r0, int64_t r1, int nur, void* out,
-                         int64_t out_ld, float w, unsigned blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_mix_stream<DEPTH, NU>), dim3(blocks), dim3(kBlock), 0, s, src, n, r0, r1,
-                     nur, static_cast<u32x4*>(out), out_ld / 8, w);
+void launch_mix_stream_t(const SrcList& src, int n, int64_t r0, int64_t r1, int nur,
+                         const DstList& out, int nout, bool f32_out, float w, unsigned blocks,
+                         hipStream_t s) {
+  if (f32_out)
+    hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, true>), dim3(blocks), dim3(kBlock), 0, s, src, n,
+                       r0, r1, nur, out, nout, w);
+  else
+    hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, false>), dim3(blocks), dim3(kBlock), 0, s, src,
+                       n, r0, r1, nur, out, nout, w);
 }
 
-hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, void* out,
-                             int64_t out_ld, int waves_per_cu, int depth, int slots,
+hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const DstList& out,
+                             int nout, bool f32_out, int waves_per_cu, int depth, int slots,
                              int rows_per_wave, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1024,18 +1075,20 @@ hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, void* 
   for (int64_t r0 = 0; r0 < T; r0 += span) {
     const int64_t r1 = r0 + span < T ? r0 + span : T;
     const int key = 10 * depth + slots;
+#define LRAR_MIX(D, U) launch_mix_stream_t<D, U>(src, n, r0, r1, nur, out, nout, f32_out, w, g, s)
     switch (key) {
-      case 12: launch_mix_stream_t<1, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 14: launch_mix_stream_t<1, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 18: launch_mix_stream_t<1, 8>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 26: launch_mix_stream_t<1, 16>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 22: launch_mix_stream_t<2, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 24: launch_mix_stream_t<2, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 28: launch_mix_stream_t<2, 8>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 42: launch_mix_stream_t<4, 2>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
-      case 44: launch_mix_stream_t<4, 4>(src, n, r0, r1, nur, out, out_ld, w, g, s); break;
+      case 12: LRAR_MIX(1, 2); break;
+      case 14: LRAR_MIX(1, 4); break;
+      case 18: LRAR_MIX(1, 8); break;
+      case 26: LRAR_MIX(1, 16); break;
+      case 22: LRAR_MIX(2, 2); break;
+      case 24: LRAR_MIX(2, 4); break;
+      case 28: LRAR_MIX(2, 8); break;
+      case 42: LRAR_MIX(4, 2); break;
+      case 44: LRAR_MIX(4, 4); break;
       default: return hipErrorInvalidValue;
     }
+#undef LRAR_MIX
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
