@@ -1,9 +1,11 @@
-"""Seeded random shapes across the dispatch boundaries of the read and the backward, against the
-oracle element by element. The widths straddle the register-tile limits (one to four chunks of 64
+"""Seeded random shapes across the dispatch boundaries of every entry point (the read, Phase 1,
+the merge, the fused update, the full-width-RMS and separate-key reads, and the backward),
+against the oracle element by element. The widths straddle the register-tile limits (one to four chunks of 64
 units per wave, rows shared by two or four waves, rows past the widest tile), the key widths map to
 every spread-piece size, to the row units and to keys that start inside a unit, unaligned widths
 and odd row strides take the element path, and every case draws its element type, 1 to 20
-sources and 1 to 300 rows (ragged tiles)."""
+sources and 1 to 300 rows (ragged tiles); Phase 1 also draws 1 to 20 site queries and the
+accumulators' type and row padding, the merges their prior sources and extra sources."""
 import numpy as np
 import pytest
 import torch
@@ -89,3 +91,156 @@ def test_random_backward(d, r, io, n, T, ld):
     h, al = oracle.forward(s64, f64(q), r, eps)
     parity.assert_dq(f64(dq), dq_ref, parity.dq_bound(s64, f64(q), g64, al, h, r, eps),
                      f"{where} dq")
+
+
+def draw_keyed(rng):
+    d, r, io, n, T, ld = draw(rng, WIDTHS)
+    return d, r, io, n, T, ld, int(rng.integers(0, 1 << 30))
+
+
+STATS = [draw_keyed(np.random.default_rng(7003 + i)) for i in range(20)]
+MERGE = [draw_keyed(np.random.default_rng(7103 + i)) for i in range(16)]
+MACC = [draw_keyed(np.random.default_rng(7203 + i)) for i in range(16)]
+FULL = cases(7004, 16, WIDTHS)
+KEYS = [draw_keyed(np.random.default_rng(7303 + i)) for i in range(16)]
+
+
+def kids(cs):
+    return [f"d{d}-r{r}-{io}-n{n}-T{T}-ld{ld}-k{k % 1000}" for d, r, io, n, T, ld, k in cs]
+
+
+def stats_rounded(inter64, q64, r, eps, acc_dtype):
+    """The oracle's Phase-1 statistics of one query, rounded to their storage types."""
+    m_o, l_o, acc_o = oracle.stats(inter64, q64[None, :], r, eps)
+    m = torch.tensor(m_o[0], dtype=torch.float32, device="cuda")
+    l = torch.tensor(l_o[0], dtype=torch.float32, device="cuda")
+    acc = torch.tensor(acc_o[0], dtype=torch.float32).to(acc_dtype).cuda()
+    return m, l, acc
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld,k", STATS, ids=kids(STATS))
+def test_random_stats(d, r, io, n, T, ld, k):
+    rng = np.random.default_rng(k)
+    nq = int(rng.integers(1, 21))
+    n = min(n, 12)
+    acc_dtype = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+    pad = int(rng.choice([0, 8]))
+    eps = 1e-6
+    srcs = sources(n, T, d, io, seed=k % 9973, scale=(0.5, 4.0), row_stride=ld)
+    qs = query(r, seed=k % 997, nq=nq)
+    acc = torch.full((nq, T, d + pad), float("nan"), dtype=acc_dtype, device="cuda")[:, :, :d]
+    m = torch.empty((nq, T), dtype=torch.float32, device="cuda")
+    l = torch.empty((nq, T), dtype=torch.float32, device="cuda")
+    where = f"d={d} r={r} {io} n={n} nq={nq} T={T} ld={ld} acc={acc_dtype} pad={pad}"
+    say(f"[random] stats {where}")
+    lrar.lrar_forward_stats(srcs, qs, r, eps, m=m, l=l, acc=acc)
+    torch.cuda.synchronize()
+    s64 = [f64(s) for s in srcs]
+    q64 = f64(qs)
+    m_o, l_o, acc_o = oracle.stats(s64, q64, r, eps)
+    m_g, l_g, acc_g = f64(m), f64(l), f64(acc)
+    for qi in range(nq):
+        z_o, _ = oracle.scores(s64, q64[qi], r, eps)
+        parity.assert_stats(m_g[qi], l_g[qi], acc_g[qi], m_o[qi], l_o[qi], acc_o[qi], z_o, s64,
+                            "bf16" if acc_dtype == torch.bfloat16 else "f32",
+                            f"{where} query {qi}")
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld,k", MERGE, ids=kids(MERGE))
+def test_random_merge(d, r, io, n, T, ld, k):
+    rng = np.random.default_rng(k)
+    n_inter = int(rng.integers(1, 9))
+    n_extra = int(rng.integers(0, 4))
+    acc_dtype = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+    eps = 1e-6
+    inter = sources(n_inter, T, d, io, seed=k % 9973, scale=(0.5, 4.0))
+    extra = (sources(n_extra, T, d, io, seed=k % 9967, scale=(0.5, 4.0), row_stride=ld)
+             if n_extra else [])
+    q = query(r, seed=k % 991)
+    m, l, acc = stats_rounded([f64(s) for s in inter], f64(q), r, eps, acc_dtype)
+    where = f"d={d} r={r} {io} inter={n_inter} extra={n_extra} T={T} ld={ld} acc={acc_dtype}"
+    say(f"[random] merge {where}")
+    out_dtype = torch.bfloat16 if io == "bf16" else torch.float32
+    out, m2, l2 = lrar.lrar_merge(m, l, acc, extra, q, r, eps, stats_out=True, io_dtype=out_dtype)
+    torch.cuda.synchronize()
+    e64 = [f64(s) for s in extra]
+    m_in, l_in, acc_in = f64(m), f64(l), f64(acc)
+    h_ref, m_ref, l_ref = oracle.merge(m_in, l_in, acc_in, e64, f64(q), r, eps)
+    if e64:
+        z_e, _ = oracle.scores(e64, f64(q), r, eps)
+        w_extra = np.exp(z_e - m_ref[:, None]) / l_ref[:, None]
+    else:
+        w_extra = np.zeros((T, 0))
+    w_prior = l_in * np.exp(m_in - m_ref) / l_ref
+    parity.assert_merge(f64(out), h_ref, w_prior, acc_in / l_in[:, None], w_extra, e64, io,
+                        where + " h")
+    m2g = f64(m2)
+    assert np.all(np.abs(m2g - m_ref) <= 2.0 ** -23 * np.abs(m_ref) + 1e-12), where + " m'"
+    l_resc = l_ref * np.exp(m_ref - m2g)
+    assert np.all(np.abs(f64(l2) - l_resc) <= 4 * parity.U * l_resc), where + " l'"
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld,k", MACC, ids=kids(MACC))
+def test_random_merge_accumulate(d, r, io, n, T, ld, k):
+    rng = np.random.default_rng(k)
+    n_inter = int(rng.integers(1, 9))
+    with_b = bool(rng.integers(0, 2))
+    acc_dtype = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+    eps = 1e-6
+    inter = sources(n_inter, T, d, io, seed=k % 9973, scale=(0.5, 4.0))
+    b, o = sources(2, T, d, io, seed=k % 9967, scale=(0.5, 4.0), row_stride=ld)
+    q = query(r, seed=k % 991)
+    m, l, acc = stats_rounded([f64(s) for s in inter], f64(q), r, eps, acc_dtype)
+    where = f"d={d} r={r} {io} inter={n_inter} b={with_b} T={T} ld={ld} acc={acc_dtype}"
+    say(f"[random] merge_accumulate {where}")
+    out, b2, m2, l2 = lrar.lrar_merge_accumulate(m, l, acc, b if with_b else None, o, q, r, eps,
+                                                 stats_out=True)
+    torch.cuda.synchronize()
+    m_in, l_in, acc_in = f64(m), f64(l), f64(acc)
+    h_ref, bref, m_ref, l_ref = oracle.merge_accumulate(
+        m_in, l_in, acc_in, f64(b) if with_b else None, f64(o), f64(q), r, eps,
+        8 if io == "bf16" else 24)
+    assert np.array_equal(f64(b2), bref), where + " b_out differs from round(b + o)"
+    z_e, _ = oracle.scores([bref], f64(q), r, eps)
+    w_extra = np.exp(z_e - m_ref[:, None]) / l_ref[:, None]
+    w_prior = l_in * np.exp(m_in - m_ref) / l_ref
+    parity.assert_merge(f64(out), h_ref, w_prior, acc_in / l_in[:, None], w_extra, [bref], io,
+                        where + " h")
+    m2g = f64(m2)
+    assert np.all(np.abs(m2g - m_ref) <= 2.0 ** -23 * np.abs(m_ref) + 1e-12), where + " m'"
+    l_resc = l_ref * np.exp(m_ref - m2g)
+    assert np.all(np.abs(f64(l2) - l_resc) <= 4 * parity.U * l_resc), where + " l'"
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld", FULL, ids=ids(FULL))
+def test_random_fullrms(d, r, io, n, T, ld):
+    eps = 1e-6
+    srcs = sources(n, T, d, io, seed=d + 5 * r + n, scale=(0.5, 4.0), row_stride=ld)
+    q = query(r, seed=r + 17)
+    where = f"d={d} r={r} {io} n={n} T={T} ld={ld}"
+    say(f"[random] fullrms {where}")
+    out, alpha = lrar.lrar_forward_fullrms(srcs, q, r, eps, alpha=True)
+    torch.cuda.synchronize()
+    s64 = [f64(s) for s in srcs]
+    h_ref, a_ref = oracle.forward_fullrms(s64, f64(q), r, eps)
+    parity.assert_weights(f64(alpha), a_ref, where + " alpha")
+    parity.assert_read(f64(out), h_ref, a_ref, s64, io, where + " h")
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld,k", KEYS, ids=kids(KEYS))
+def test_random_keys(d, r, io, n, T, ld, k):
+    rng = np.random.default_rng(k)
+    key_pad = int(rng.choice([0, 8, 1]))
+    eps = 1e-6
+    srcs = sources(n, T, d, io, seed=k % 9973, scale=(0.5, 4.0), row_stride=ld)
+    full = synth.values(n, T, r + key_pad, io, k % 9967, scale=(0.5, 2.0), device="cpu")
+    keys = [x.cuda()[:, :r] for x in full]
+    q = query(r, seed=k % 991)
+    where = f"d={d} r={r} {io} n={n} T={T} ld={ld} key_ld={r + key_pad}"
+    say(f"[random] keys {where}")
+    out, alpha = lrar.lrar_forward_keys(srcs, keys, q, r, eps, alpha=True)
+    torch.cuda.synchronize()
+    s64 = [f64(s) for s in srcs]
+    h_ref, a_ref = oracle.forward_keys(s64, [f64(x) for x in keys], f64(q), r, eps)
+    parity.assert_weights(f64(alpha), a_ref, where + " alpha")
+    parity.assert_read(f64(out), h_ref, a_ref, s64, io, where + " h")
