@@ -52,6 +52,8 @@ namespace lrar {
 // Sources in flight ahead of the one being folded for reads of many sources (the three-deep
 // ring; the launchers below say when it is used).
 constexpr int kDeepPrefetch = 3;
+// Reads through the shallower rings keep their one-wave rows in lockstep from this many sources.
+constexpr int kLockMinSources = 8;
 
 template <typename IO, int VEC, int NU, int TU, int KS, bool ROWRED, int R, int PF, int WPR,
           int MODE, typename ACC, bool KA>
@@ -554,14 +556,17 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       }
     }
   } else {
-    // Rows held by one wave and read through the three-deep ring meet at a workgroup barrier
-    // once per ring cycle, so the workgroup's waves stream the same sources together, which
-    // HBM serves best (d = 1024, sites of 20..49 sources: +2.7 to +3.6 %; the separate-key read
-    // of 49 sources: +3 %). A barrier per source or per tile gained less, and one per source
-    // for the shallower rings lost 1-1.5 %. It is taken only in the steps where every row group
-    // of the workgroup has a tile, a condition that is the same for all of its waves, so they
-    // all meet the same barriers.
-    constexpr bool kLockstep = WPR == 1 && PF == kDeepPrefetch;
+    // Rows held by one wave meet at a workgroup barrier, so the workgroup's waves stream the
+    // same sources together, which HBM serves best: once per ring cycle through the three-deep
+    // ring (d = 1024, sites of 20..49 sources: +2.7 to +3.6 %; the separate-key read of 49
+    // sources: +3 %; per source or per tile gained less), once per tile through the shallower
+    // rings of reads of 8 or more sources (d = 2048: +0.6 to +2.5 %; d = 1024, 9 and 13
+    // sources: +2 %; 5 sources lost 1 %, and a barrier per source or per ring cycle lost up to
+    // 1.5 % there). A barrier is taken only in the steps where every row group of the workgroup
+    // has a tile, a condition that is the same for all of its waves (as n is), so they all meet
+    // the same barriers.
+    constexpr bool kDeep = PF == kDeepPrefetch;
+    const bool lock_reads = WPR == 1 && (kDeep || n >= kLockMinSources);
     const int64_t last_group =
         p.tile_begin +
         (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + kWavesPerBlock - 1) / WPR;
@@ -569,7 +574,8 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       TileGeom t;
       set_tile(t, tile);
       begin_tile(t);
-      const bool lockstep = kLockstep && (tile - group) + last_group < ntiles;
+      const bool lockstep = lock_reads && (tile - group) + last_group < ntiles;
+      if (!kDeep && lockstep) __syncthreads();
 #pragma unroll
       for (int b = 0; b < PF; ++b) {
         const int ia = clamp_src(b);
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
                                              p.src.ld[ia], t, key_base(ia), key_ld(ia),
                                              i + PF < n);
           if (i < n) {
-            if (b == 0 && lockstep) __syncthreads();
+            if (kDeep && b == 0 && lockstep) __syncthreads();
             fold_source(ring[b], t, i);
           }
         }
