@@ -576,6 +576,11 @@ __global__ __launch_bounds__(kBlock) void k_read_tile(ReadParams p, KeyTable<MOD
       begin_tile(t);
       const bool lockstep = lock_reads && (tile - group) + last_group < ntiles;
       if (!kDeep && lockstep) __syncthreads();
+      // Rows that span the workgroup's four waves with a spread key exchange no key sums, so
+      // nothing else keeps their waves together: they meet once per tile (+1 % at d = 7168,
+      // +3 % at d = 4096, r = 64; once per source gained less). All four waves hold the same
+      // tiles.
+      if constexpr (WPR == kWavesPerBlock && KS > 0) __syncthreads();
 #pragma unroll
       for (int b = 0; b < PF; ++b) {
         const int ia = clamp_src(b);
