@@ -515,6 +515,9 @@ KERNEL_STREAMS = {
         ("backward_d4096", "backward_bf16_grads_r1024_n10"),
         ("backward_d4096", "backward_saved_bf16_grads_r1024_n10")]),
 }
+# The streams' waves kept apart (0), or meeting at a workgroup barrier once per row (1) or
+# once per group of sources loaded together (2), as the reads keep theirs in lockstep.
+STREAM_LOCKSTEP = (0, 1, 2)
 KERNEL_STREAM_LAUNCHES = [(w, p, c) for w in (4, 8, 12, 16, 24, 32) for p in (1, 2) for c in (0, 2, 4)]
 
 
@@ -530,28 +533,30 @@ def stream_slots(d):
 
 def best_stream(torch, lrar, ev, srcs, outs, launches, slots):
     """Times lrar_mix_stream over every launch shape (waves per CU, sources loaded together,
-    rows per wave per launch) and units a lane, 4 launches each, then the fastest like the
-    rows: (its timing, its launch shape)."""
+    rows per wave per launch), units a lane and lockstep (none, per row, per source group),
+    4 launches each, then the fastest like the rows: (its timing, its launch shape)."""
     best = None
     for w, pdep, c in launches:
         for u in slots:
             if pdep * u > 16:
                 continue
-            call = lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep, slots=u,
-                                        rows_per_wave=c, prepare=True)
-            tm = Timer(torch)
-            ev()
-            call()
-            for _ in range(4):
+            for lk in STREAM_LOCKSTEP:
+                call = lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep, slots=u,
+                                            rows_per_wave=c, lockstep=lk, prepare=True)
+                tm = Timer(torch)
                 ev()
-                tm.run(call)
-            ms = _median(tm.collect_ms())
-            if best is None or ms < best[0]:
-                best = (ms, w, pdep, u, c)
-    _, w, pdep, u, c = best
+                call()
+                for _ in range(4):
+                    ev()
+                    tm.run(call)
+                ms = _median(tm.collect_ms())
+                if best is None or ms < best[0]:
+                    best = (ms, w, pdep, u, c, lk)
+    _, w, pdep, u, c, lk = best
     ms = time_calls(torch, ev, lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep,
-                                                    slots=u, rows_per_wave=c, prepare=True))
-    return ms, dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c)
+                                                    slots=u, rows_per_wave=c, lockstep=lk,
+                                                    prepare=True))
+    return ms, dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c, lockstep=lk)
 
 
 def stream_ceilings(torch, lrar, ev):

@@ -296,13 +296,15 @@ size_t lrar_read_stream_sink_bytes(void);
  * every pointer is 16-byte aligned; no output may overlap a source or another output. The
  * launch shape is the caller's: waves_per_cu (4, 8, ..., 32) waves per compute unit; slots
  * (2, 4, 8 or 16) 16-byte units a lane, so a wave takes a row in groups of 64 x slots units;
- * depth (1, 2 or 4, with depth x slots <= 16) sources loaded together before any is added; and
- * rows_per_wave (> 0: launches of that many rows per wave; 0: one launch). Errors as for
- * lrar_forward. */
+ * depth (1, 2 or 4, with depth x slots <= 16) sources loaded together before any is added;
+ * rows_per_wave (> 0: launches of that many rows per wave; 0: one launch); and lockstep (0:
+ * none; 1 or 2: the waves of a workgroup meet at a barrier once per row, or once per group of
+ * depth sources, as the reads keep their waves together). Errors as for lrar_forward. */
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
                             const int64_t* src_ld, int32_t nout, void* const* out,
                             const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
-                            int32_t depth, int32_t slots, int32_t rows_per_wave, void* stream);
+                            int32_t depth, int32_t slots, int32_t rows_per_wave,
+                            int32_t lockstep, void* stream);
 
 /* Static description of a status code. */
 const char* lrar_status_string(lrar_status status);

@@ -835,7 +835,8 @@ lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* st
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
                             const int64_t* src_ld, int32_t nout, void* const* out,
                             const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
-                            int32_t depth, int32_t slots, int32_t rows_per_wave, void* stream) {
+                            int32_t depth, int32_t slots, int32_t rows_per_wave, int32_t lockstep,
+                            void* stream) {
   const char* fn = "lrar_mix_stream";
   if (T < 0) return fail(LRAR_ERR_INVALID, "%s: T = %lld < 0", fn, (long long)T);
   if (d < 8 || d % 8 != 0)
@@ -851,6 +852,8 @@ lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* 
                 depth * slots);
   if (rows_per_wave < 0)
     return fail(LRAR_ERR_INVALID, "%s: rows_per_wave = %d < 0", fn, rows_per_wave);
+  if (lockstep < 0 || lockstep > 2)
+    return fail(LRAR_ERR_INVALID, "%s: lockstep = %d must be 0, 1 or 2", fn, lockstep);
   if (nout < 1 || nout > LRAR_MAX_SOURCES)
     return fail(LRAR_ERR_INVALID, "%s: nout = %d outside [1, %d]", fn, nout, LRAR_MAX_SOURCES);
   if (!dtype_ok(out_dtype)) return fail(LRAR_ERR_INVALID, "%s: unknown out dtype", fn);
@@ -884,7 +887,7 @@ lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* 
   if (st != LRAR_OK) return st;
   return device_status(lrar::launch_mix_stream(S, n, T, d, O, nout, out_dtype == LRAR_F32,
                                                waves_per_cu, depth, slots, rows_per_wave,
-                                               static_cast<hipStream_t>(stream)),
+                                               lockstep, static_cast<hipStream_t>(stream)),
                        fn);
 }
 
@@ -967,15 +970,21 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
 // r0 + w + k * waves, as the read's tiles) and a row in groups of up to NU chunks of 64 16-byte
 // units, NU units a lane; DEPTH sources are loaded before any is added, and the loads are
 // waited for together. One bf16 output is a read's traffic; more outputs, or float32 ones,
-// give the write-heavy mixes of Phase 1 and the backward.
+// give the write-heavy mixes of Phase 1 and the backward. lock = 1 or 2: the workgroup's waves
+// meet at a barrier once per row or once per group of DEPTH sources, as the reads keep their
+// waves in lockstep, in the steps where every wave of the workgroup has a row (a condition all
+// of them compute alike, so they meet the same barriers).
 template <int DEPTH, int NU, bool F32OUT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NU >= 16 ? 2 : 1)))
 void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList out, int nout,
-                  float w) {
+                  float w, int lock) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block();
   const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  const int64_t last_wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + kWavesPerBlock - 1;
   for (int64_t row = r0 + wave; row < r1; row += waves) {
+    const bool all_rows = (row - wave) + last_wave < r1;
+    if (lock == 1 && all_rows) __syncthreads();
     for (int g = 0; g < nur; g += NU * kWave) {
       float acc[NU][8];
 #pragma unroll
@@ -983,6 +992,7 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       for (int i0 = 0; i0 < n; i0 += DEPTH) {
+        if (lock == 2 && all_rows) __syncthreads();
         Unit<bf16_bits, 8> v[DEPTH][NU];
 #pragma unroll
         for (int b = 0; b < DEPTH; ++b) {
@@ -1050,19 +1060,19 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
 
 template <int DEPTH, int NU>
 void launch_mix_stream_t(const SrcList& src, int n, int64_t r0, int64_t r1, int nur,
-                         const DstList& out, int nout, bool f32_out, float w, unsigned blocks,
-                         hipStream_t s) {
+                         const DstList& out, int nout, bool f32_out, float w, int lock,
+                         unsigned blocks, hipStream_t s) {
   if (f32_out)
     hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, true>), dim3(blocks), dim3(kBlock), 0, s, src, n,
-                       r0, r1, nur, out, nout, w);
+                       r0, r1, nur, out, nout, w, lock);
   else
     hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, false>), dim3(blocks), dim3(kBlock), 0, s, src,
-                       n, r0, r1, nur, out, nout, w);
+                       n, r0, r1, nur, out, nout, w, lock);
 }
 
 hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const DstList& out,
                              int nout, bool f32_out, int waves_per_cu, int depth, int slots,
-                             int rows_per_wave, hipStream_t s) {
+                             int rows_per_wave, int lockstep, hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1075,7 +1085,8 @@ hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const 
   for (int64_t r0 = 0; r0 < T; r0 += span) {
     const int64_t r1 = r0 + span < T ? r0 + span : T;
     const int key = 10 * depth + slots;
-#define LRAR_MIX(D, U) launch_mix_stream_t<D, U>(src, n, r0, r1, nur, out, nout, f32_out, w, g, s)
+#define LRAR_MIX(D, U) \
+  launch_mix_stream_t<D, U>(src, n, r0, r1, nur, out, nout, f32_out, w, lockstep, g, s)
     switch (key) {
       case 12: LRAR_MIX(1, 2); break;
       case 14: LRAR_MIX(1, 4); break;

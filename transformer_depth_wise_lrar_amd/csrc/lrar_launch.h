@@ -150,6 +150,6 @@ hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStre
 // A kernel's traffic as a plain stream (lrar_mix_stream), in the launch shape given.
 hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const DstList& out,
                              int nout, bool f32_out, int waves_per_cu, int depth, int slots,
-                             int rows_per_wave, hipStream_t s);
+                             int rows_per_wave, int lockstep, hipStream_t s);
 
 }  // namespace lrar
