@@ -714,7 +714,10 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
     cached_per_cu = per;
     cached_lds = lds;
   }
-  const int per_cu = cached_per_cu;
+  // The drained one-ahead reads of one-wave rows run two workgroups (8 waves) per CU, as their
+  // same-traffic stream runs fastest: +1 % at d = 2048 (r = 16, 64; 9 and 10 sources) against
+  // the 3 that fit; the four-wave rows of that ring measured 2.6 % slower so capped.
+  const int per_cu = kDrained && WPR == 1 && cached_per_cu > 2 ? 2 : cached_per_cu;
   // As many row groups as fit at once, trimmed so that no group gets more tiles than needed:
   // each launch runs in one round and the groups' tile counts differ by at most one. The reads
   // of cut_into_launches are cut into launches of at most max_tiles_per_group tiles per group,
