@@ -680,11 +680,16 @@ constexpr bool spread_drained(int ks, int nu, int mode, bool deep) {
 // reads: at 64 tiles per group they measured 4-7 % slower than cut into launches of 16 tiles per
 // group (d = 1024 to 7168, 9 sources), and 8 tiles per group measured 1-2 % faster again (d =
 // 2048, r = 16 and 64; d = 7168, r = 64); the drained reads above take 4 (as did the plain
-// stream). Keys read from the row units of one wave (rows of up to 4 chunks): 8 tiles per group
-// measured 4 % faster than one launch (r = d = 2048) and 3 % faster than 4; where several waves
-// share a row (d = 7168) such cuts measured 3-7 % slower, as did the two-pass read and the
-// merges (2-10 % at 12 tiles per group), so those run as one launch.
-constexpr int64_t max_tiles_per_group(bool drained) { return drained ? 4 : 8; }
+// stream) where several waves share a row, and 8 for one-wave rows, which the lockstep and the
+// 8-wave cap keep together (+2 % at d = 2048, r = 16 and 64; 4 there before the lockstep; the
+// four-wave rows measured 2 % slower at 8). Keys read from the row units of one wave (rows of
+// up to 4 chunks): 8 tiles per group measured 4 % faster than one launch (r = d = 2048) and 3 %
+// faster than 4; where several waves share a row (d = 7168) such cuts measured 3-7 % slower, as
+// did the two-pass read and the merges (2-10 % at 12 tiles per group), so those run as one
+// launch.
+constexpr int64_t max_tiles_per_group(bool drained, int wpr) {
+  return drained && wpr > 1 ? 4 : 8;
+}
 constexpr bool cut_into_launches(int mode, int ks, int wpr) {
   return (ks > 0 && (mode == kTileOnline || mode == kTileKeys)) ||
          (ks == 0 && mode == kTileOnline && wpr == 1);
@@ -728,7 +733,8 @@ hipError_t launch_tile_t(const ReadParams& p, const KeyTable<MODE>& kt, hipStrea
   const int64_t per_group_all = (tiles + resident - 1) / resident;
   const int64_t launches =
       cut_into_launches(MODE, KS, WPR)
-          ? (per_group_all + max_tiles_per_group(kDrained) - 1) / max_tiles_per_group(kDrained)
+          ? (per_group_all + max_tiles_per_group(kDrained, WPR) - 1) /
+                max_tiles_per_group(kDrained, WPR)
           : 1;
   const int64_t per_launch = ((per_group_all + launches - 1) / launches) * resident;
   constexpr int kGroupsPerBlock = kWavesPerBlock / WPR;
