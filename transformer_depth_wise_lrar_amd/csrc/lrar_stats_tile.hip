@@ -4,7 +4,8 @@
 // valid).
 //
 // For up to kStatsMaxSrc cached sources and a group of up to kStatsMaxQ site queries:
-//   * one workgroup per CU (12 wavefronts, or 16 for bf16 sources with bf16 accumulators)
+//   * one workgroup per CU (12 wavefronts; 16 for bf16 sources with bf16 accumulators, 8 with
+//     float32 ones)
 //     shares one LDS copy of the group's queries, laid out from the first key unit's column
 //     (columns of that unit before the key hold zero), so each key element is dotted with
 //     every query of the group from LDS;
@@ -40,11 +41,12 @@ namespace lrar {
 
 namespace {
 
-// Waves per workgroup (one workgroup per CU: the staged queries take most of the LDS). bf16
+// Waves per workgroup (one workgroup per CU: the staged queries take most of the LDS), at
+// d = 7168, r = 1792, 8 sources x 12 queries, 32768 rows, measured on the same buffers: bf16
 // sources with bf16 accumulators fit 4 waves per SIMD (at most 128 registers) and run 16,
-// 3-6 % faster than 12 at d = 7168, r = 1792, 8 sources x 12 queries, and 32768 rows split
-// evenly over the 4096 waves; float32 accumulators of bf16 sources need more registers than
-// 4 waves allow, and float32 sources measured no faster with 16.
+// 3-6 % faster than 12 and 5 % faster than 8; with float32 accumulators, whose writes are
+// twice as wide, 8 waves run 2.4 % faster than 12 and 10 % faster than 4 (their plain stream
+// is fastest with few waves too). float32 sources keep 12 (16 measured no faster).
 constexpr int kStatsWavesMax = 16;
 static_assert(kStatsMaxQ <= 16 && kStatsMaxSrc % 4 == 0,
               "a query group fills at most the 16 rows of a matrix product, sources come in fours");
@@ -396,7 +398,7 @@ int stats_tile_query_group(int d, int r, int vec) {
 hipError_t launch_stats_tile(const StatsParams& p, int io_bf16, int acc_bf16, int qg,
                              hipStream_t s) {
   if (io_bf16) return acc_bf16 ? launch_stats_tile_t<bf16_bits, 8, bf16_bits, 16>(p, qg, s)
-                               : launch_stats_tile_t<bf16_bits, 8, float, 12>(p, qg, s);
+                               : launch_stats_tile_t<bf16_bits, 8, float, 8>(p, qg, s);
   return acc_bf16 ? launch_stats_tile_t<float, 4, bf16_bits, 12>(p, qg, s)
                   : launch_stats_tile_t<float, 4, float, 12>(p, qg, s);
 }
