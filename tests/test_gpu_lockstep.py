@@ -1,0 +1,79 @@
+"""Reads whose waves meet at workgroup barriers (the lockstep of the one-wave rows through the
+three-deep ring, once per ring cycle; of the shallower rings from 8 sources, once per tile; and
+of the four-wave rows with a spread key, once per tile), on row counts whose last step leaves
+some row groups of a workgroup without a tile, where the barrier must be skipped by all of the
+workgroup's waves alike.
+
+Each test fills the output with NaN, then checks that every row was written, that every row's
+weights sum to 1, and that sampled rows (the ends, the ragged tail and random rows) match the
+oracle element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import transformer_depth_wise_lrar_amd as lrar
+from gpu_util import f64, needs_gpu, sample_rows, say
+from transformer_depth_wise_lrar_amd import synth
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def rows64(t, rows):
+    idx = torch.as_tensor(rows, device=t.device)
+    return f64(t.index_select(0, idx))
+
+
+def check(out, alpha, T, rows, ref_fn, srcs, where):
+    assert not torch.isnan(out.float()).any(), where + ": a row was not written"
+    sums = alpha.double().sum(dim=1)
+    assert torch.all((sums - 1.0).abs() < 1e-5), where + ": weights do not sum to 1"
+    s64 = [rows64(s, rows) for s in srcs]
+    h_ref, a_ref = ref_fn(s64)
+    parity.assert_weights(rows64(alpha, rows), a_ref, where + " alpha")
+    parity.assert_read(rows64(out, rows), h_ref, a_ref, s64, "bf16", where + " h")
+
+
+@pytest.mark.parametrize("d,r,n,T", [
+    (1024, 64, 20, 16384 + 37),    # three-deep ring: a barrier per ring cycle
+    (1024, 64, 49, 16384 + 37),    # the same over 12 ring cycles a tile
+    (1024, 64, 9, 16384 + 37),     # two-deep ring, 8+ sources: a barrier per tile
+    (1024, 64, 7, 16384 + 37),     # below 8 sources: no barrier
+    (2048, 64, 10, 65536 + 37),    # drained one ahead, one-wave rows: per tile, 8-tile launches
+    (2048, 2048, 8, 65536 + 37),   # key from the row units of one wave: per tile
+    (4096, 64, 10, 16384 + 37),    # four-wave rows with a spread key: per tile
+])
+def test_lockstep_reads(d, r, n, T):
+    eps = 1e-6
+    srcs = synth.values(n, T, d, "bf16", seed=950 + n, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=951 + r, device="cuda")[0].contiguous()
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    alpha = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    where = f"lockstep d={d} r={r} n={n} T={T}"
+    say(f"[lockstep] {where}")
+    lrar.lrar_forward(srcs, q, r, eps, out=out, alpha=alpha, variant="online")
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 40, seed=T + n)
+    check(out, alpha, T, rows, lambda s64: oracle.forward(s64, f64(q), r, eps), srcs, where)
+
+
+@pytest.mark.parametrize("n", [8, 20])
+def test_lockstep_separate_keys(n):
+    """The separate-key read takes the three-deep ring from 8 sources, with its per-cycle
+    barrier."""
+    T, d, r, eps = 16384 + 37, 1024, 32, 1e-6
+    srcs = synth.values(n, T, d, "bf16", seed=960 + n, scale=(0.5, 4.0), device="cuda")
+    keys = synth.values(n, T, r, "bf16", seed=961 + n, scale=(0.5, 2.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=962, device="cuda")[0].contiguous()
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    alpha = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    where = f"lockstep keys n={n} T={T}"
+    say(f"[lockstep] {where}")
+    lrar.lrar_forward_keys(srcs, keys, q, r, eps, out=out, alpha=alpha)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 40, seed=T + n)
+    k64 = [rows64(k, rows) for k in keys]
+    check(out, alpha, T, rows, lambda s64: oracle.forward_keys(s64, k64, f64(q), r, eps), srcs,
+          where)
