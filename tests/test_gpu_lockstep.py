@@ -1,6 +1,7 @@
 """Reads whose waves meet at workgroup barriers (the lockstep of the one-wave rows through the
-three-deep ring, once per ring cycle; of the shallower rings from 8 sources, once per tile; and
-of the four-wave rows with a spread key, once per tile), on row counts whose last step leaves
+three-deep ring, once per ring cycle; of the shallower rings from 8 sources, once per tile; of
+the four-wave rows with a spread key, once per tile; and of the fused Phase-2 update's one-wave
+rows, once per tile), on row counts whose last step leaves
 some row groups of a workgroup without a tile, where the barrier must be skipped by all of the
 workgroup's waves alike.
 
@@ -77,3 +78,36 @@ def test_lockstep_separate_keys(n):
     k64 = [rows64(k, rows) for k in keys]
     check(out, alpha, T, rows, lambda s64: oracle.forward_keys(s64, k64, f64(q), r, eps), srcs,
           where)
+
+
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+def test_lockstep_fused_update(acc_dtype):
+    """The fused Phase-2 update's one-wave rows meet once per tile: b' = b + o bit for bit and h
+    within the merge's bar on sampled rows, every row written."""
+    T, d, r, eps = 65536 + 37, 2048, 64, 1e-6
+    b, o = synth.values(2, T, d, "bf16", seed=970, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=971, device="cuda")[0].contiguous()
+    g = torch.Generator(device="cuda").manual_seed(972)
+    m = (10.0 + torch.randn((T,), generator=g, device="cuda")).float()
+    l = (1.0 + torch.rand((T,), generator=g, device="cuda")).float()
+    acc = torch.randn((T, d), generator=g, device="cuda").to(acc_dtype)
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    b_out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    where = f"lockstep fused update acc={acc_dtype} T={T}"
+    say(f"[lockstep] {where}")
+    lrar.lrar_merge_accumulate(m, l, acc, b, o, q, r, eps, out=out, b_out=b_out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any(), where + ": a row of h was not written"
+    assert not torch.isnan(b_out.float()).any(), where + ": a row of b' was not written"
+    rows = sample_rows(T, 40, seed=T)
+    m_in = rows64(m[:, None], rows)[:, 0]
+    l_in = rows64(l[:, None], rows)[:, 0]
+    acc_in = rows64(acc, rows)
+    h_ref, bref, m_ref, l_ref = oracle.merge_accumulate(m_in, l_in, acc_in, rows64(b, rows),
+                                                        rows64(o, rows), f64(q), r, eps, 8)
+    assert np.array_equal(rows64(b_out, rows), bref), where + ": b' differs from round(b + o)"
+    z_e, _ = oracle.scores([bref], f64(q), r, eps)
+    w_extra = np.exp(z_e - m_ref[:, None]) / l_ref[:, None]
+    w_prior = l_in * np.exp(m_in - m_ref) / l_ref
+    parity.assert_merge(rows64(out, rows), h_ref, w_prior, acc_in / l_in[:, None], w_extra,
+                        [bref], "bf16", where + " h")
