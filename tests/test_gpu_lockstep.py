@@ -111,3 +111,42 @@ def test_lockstep_fused_update(acc_dtype):
     w_prior = l_in * np.exp(m_in - m_ref) / l_ref
     parity.assert_merge(rows64(out, rows), h_ref, w_prior, acc_in / l_in[:, None], w_extra,
                         [bref], "bf16", where + " h")
+
+
+@pytest.mark.parametrize("grad", ["f32", "bf16"])
+def test_lockstep_backward_d1024(grad):
+    """The backward's one-wave rows of up to two chunks meet once per row: source gradients on
+    sampled rows and dq over every row (the oracle in chunks of rows), T ragged."""
+    T, d, r, n, eps = 16384 + 37, 1024, 64, 10, 1e-6
+    srcs = synth.values(n, T, d, "bf16", seed=980, scale=(0.5, 4.0), device="cuda")
+    q = synth.queries(1, r, 1.0, seed=981, device="cuda")[0].contiguous()
+    g = synth.upstream(T, d, seed=982, device="cuda")
+    if grad == "bf16":
+        g = g.to(torch.bfloat16)
+    dsrc = [torch.full((T, d), float("nan"), dtype=g.dtype, device="cuda") for _ in range(n)]
+    where = f"lockstep backward d={d} n={n} T={T} grad={grad}"
+    say(f"[lockstep] {where}")
+    dsrc, dq = lrar.lrar_backward_grad(srcs, q, g, r, eps, dsrc=dsrc)
+    torch.cuda.synchronize()
+    for i in range(n):
+        assert not torch.isnan(dsrc[i].float()).any(), f"{where}: a row of dsrc[{i}] not written"
+    rows = sample_rows(T, 24, seed=T)
+    s64 = [rows64(s, rows) for s in srcs]
+    ds_ref, _ = oracle.backward(s64, f64(q), rows64(g, rows), r, eps)
+    for i in range(n):
+        if grad == "f32":
+            parity.assert_dsrc(rows64(dsrc[i], rows), ds_ref[i], f"{where} dsrc[{i}]")
+        else:
+            parity.assert_dsrc_bf16(rows64(dsrc[i], rows), ds_ref[i], f"{where} dsrc[{i}]")
+    dq_ref = np.zeros(r)
+    bound = 0.0
+    q64 = f64(q)
+    for c0 in range(0, T, 4096):
+        sl = slice(c0, c0 + 4096)
+        c64 = [f64(s[sl]) for s in srcs]
+        g64 = f64(g[sl])
+        _, dq_c = oracle.backward(c64, q64, g64, r, eps)
+        dq_ref += dq_c
+        h_c, a_c = oracle.forward(c64, q64, r, eps)
+        bound += parity.dq_bound(c64, q64, g64, a_c, h_c, r, eps)
+    parity.assert_dq(f64(dq), dq_ref, bound, where + " dq")

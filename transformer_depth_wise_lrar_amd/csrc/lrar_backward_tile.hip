@@ -75,7 +75,16 @@ __global__ __launch_bounds__(kBlock) void k_backward_tile(BwdParams p, double* _
 
   int parity = 0;
   const auto src_base = [&](int i) { return static_cast<const IO*>(p.src.ptr[i]); };
+  // One-wave rows of up to two chunks (d <= 1024 bf16) meet at a workgroup barrier once per
+  // row, as the reads keep their waves in lockstep: +7 % (fp32 gradients, 10 sources) and +1 %
+  // (49 sources) at d = 1024, bf16 gradients level; at d = 2048 it measured 1.9 % slower with
+  // fp32 gradients. It is taken only in the steps where every row group of the workgroup has a
+  // row, a condition the same for all of its waves.
+  constexpr bool kLockRows = WPR == 1 && NU <= 2;
+  const int64_t last_group =
+      (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + kWavesPerBlock - 1) / WPR;
   for (int64_t row = group; row < p.T; row += ngroups) {
+    if (kLockRows && (row - group) + last_group < p.T) __syncthreads();
     g.r0 = row;
     g.nrow = 1;
     // upstream gradient of the row
