@@ -244,3 +244,50 @@ def test_random_keys(d, r, io, n, T, ld, k):
     h_ref, a_ref = oracle.forward_keys(s64, [f64(x) for x in keys], f64(q), r, eps)
     parity.assert_weights(f64(alpha), a_ref, where + " alpha")
     parity.assert_read(f64(out), h_ref, a_ref, s64, io, where + " h")
+
+
+BWD2 = [draw_keyed(np.random.default_rng(7403 + i)) for i in range(24)]
+BWD2 = [c for c in BWD2 if c[0] <= 4104 or c[0] in (7168, 8192)]
+
+
+@pytest.mark.parametrize("d,r,io,n,T,ld,k", BWD2, ids=kids(BWD2))
+def test_random_backward_grad_saved(d, r, io, n, T, ld, k):
+    """lrar_backward_grad (fp32 or bf16 gradients, with or without accumulation) and the same
+    from lrar_forward_save's statistics (lrar_backward_saved), against the oracle."""
+    rng = np.random.default_rng(k)
+    grad = str(rng.choice(["f32", "bf16"]))
+    accumulate = bool(rng.integers(0, 2))
+    saved_stats = bool(rng.integers(0, 2))
+    eps = 1e-6
+    srcs = sources(n, T, d, io, seed=k % 9973, scale=(0.5, 4.0), row_stride=ld)
+    q = query(r, seed=k % 991)
+    gdt = torch.float32 if grad == "f32" else torch.bfloat16
+    dout = synth.upstream(T, d, k % 9967, device="cpu").to(gdt).cuda()
+    prior = dsrc = None
+    if accumulate:
+        prior = [torch.randn((T, d), generator=torch.Generator().manual_seed(k % 997 + i))
+                 .to(gdt).cuda() for i in range(n)]
+        dsrc = [p.clone() for p in prior]
+    where = (f"d={d} r={r} {io} n={n} T={T} ld={ld} grad={grad} acc={accumulate} "
+             f"saved={saved_stats}")
+    say(f"[random] backward_grad {where}")
+    if saved_stats:
+        _, saved = lrar.lrar_forward_save(srcs, q, r, eps)
+        dsrc, dq = lrar.lrar_backward_saved(srcs, q, saved, dout, r, dsrc=dsrc,
+                                            accumulate=accumulate)
+    else:
+        dsrc, dq = lrar.lrar_backward_grad(srcs, q, dout, r, eps, dsrc=dsrc,
+                                           accumulate=accumulate)
+    torch.cuda.synchronize()
+    s64 = [f64(s) for s in srcs]
+    g64 = f64(dout)
+    ds_ref, dq_ref = oracle.backward(s64, f64(q), g64, r, eps)
+    for i in range(n):
+        ref = ds_ref[i] + (f64(prior[i]) if accumulate else 0.0)
+        if grad == "f32":
+            parity.assert_dsrc(f64(dsrc[i]), ref, f"{where} dsrc[{i}]")
+        else:
+            parity.assert_dsrc_bf16(f64(dsrc[i]), ref, f"{where} dsrc[{i}]")
+    h, al = oracle.forward(s64, f64(q), r, eps)
+    parity.assert_dq(f64(dq), dq_ref, parity.dq_bound(s64, f64(q), g64, al, h, r, eps),
+                     f"{where} dq")
