@@ -531,18 +531,28 @@ def stream_slots(d):
     return (4,)
 
 
+def stream_row_waves(d):
+    """Waves sharing a row in the same-traffic stream of width d: from d = 4096 (512 units) a
+    row also goes to 2 or 4 waves of a workgroup, as the reads of such rows share theirs."""
+    return (1, 2, 4) if d >= 4096 else (1,)
+
+
 def best_stream(torch, lrar, ev, srcs, outs, launches, slots):
     """Times lrar_mix_stream over every launch shape (waves per CU, sources loaded together,
-    rows per wave per launch), units a lane and lockstep (none, per row, per source group),
-    4 launches each, then the fastest like the rows: (its timing, its launch shape)."""
+    rows per row group per launch), units a lane, lockstep (none, per row, per source group)
+    and waves per row (stream_row_waves; a shared row takes 4 units a lane), 4 launches each,
+    then the fastest like the rows: (its timing, its launch shape)."""
+    d = srcs[0].shape[1]
+    shapes = [(u, 1) for u in slots] + [(4, g) for g in stream_row_waves(d) if g > 1]
     best = None
     for w, pdep, c in launches:
-        for u in slots:
+        for u, g in shapes:
             if pdep * u > 16:
                 continue
             for lk in STREAM_LOCKSTEP:
                 call = lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep, slots=u,
-                                            rows_per_wave=c, lockstep=lk, prepare=True)
+                                            rows_per_wave=c, lockstep=lk, waves_per_row=g,
+                                            prepare=True)
                 tm = Timer(torch)
                 ev()
                 call()
@@ -551,12 +561,13 @@ def best_stream(torch, lrar, ev, srcs, outs, launches, slots):
                     tm.run(call)
                 ms = _median(tm.collect_ms())
                 if best is None or ms < best[0]:
-                    best = (ms, w, pdep, u, c, lk)
-    _, w, pdep, u, c, lk = best
+                    best = (ms, w, pdep, u, c, lk, g)
+    _, w, pdep, u, c, lk, g = best
     ms = time_calls(torch, ev, lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=w, depth=pdep,
                                                     slots=u, rows_per_wave=c, lockstep=lk,
-                                                    prepare=True))
-    return ms, dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c, lockstep=lk)
+                                                    waves_per_row=g, prepare=True))
+    return ms, dict(waves_per_cu=w, depth=pdep, slots=u, rows_per_wave=c, lockstep=lk,
+                    waves_per_row=g)
 
 
 def stream_ceilings(torch, lrar, ev):

@@ -294,17 +294,20 @@ size_t lrar_read_stream_sink_bytes(void);
  * read: it is the reference kernel for the same-traffic bandwidth ceiling a kernel is measured
  * against. d and every src_ld are multiples of 8, every out_ld a multiple of 16 bytes, and
  * every pointer is 16-byte aligned; no output may overlap a source or another output. The
- * launch shape is the caller's: waves_per_cu (4, 8, ..., 32) waves per compute unit; slots
- * (2, 4, 8 or 16) 16-byte units a lane, so a wave takes a row in groups of 64 x slots units;
- * depth (1, 2 or 4, with depth x slots <= 16) sources loaded together before any is added;
- * rows_per_wave (> 0: launches of that many rows per wave; 0: one launch); and lockstep (0:
- * none; 1 or 2: the waves of a workgroup meet at a barrier once per row, or once per group of
- * depth sources, as the reads keep their waves together). Errors as for lrar_forward. */
+ * launch shape is the caller's: waves_per_cu (4, 8, ..., 32) waves per compute unit;
+ * waves_per_row (1, 2 or 4) waves of one workgroup sharing each row, as the reads of wide
+ * rows share theirs; slots (2, 4, 8 or 16) 16-byte units a lane, so the waves of a row take it
+ * in passes of 64 x slots x waves_per_row units, 64-unit chunks dealt to them in turn; depth
+ * (1, 2 or 4, with depth x slots <= 16) sources loaded together before any is added;
+ * rows_per_wave (> 0: launches of that many rows per row group; 0: one launch); and lockstep
+ * (0: none; 1 or 2: the waves of a workgroup meet at a barrier once per row, or once per
+ * group of depth sources, as the reads keep their waves together). Errors as for
+ * lrar_forward. */
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
                             const int64_t* src_ld, int32_t nout, void* const* out,
                             const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
-                            int32_t depth, int32_t slots, int32_t rows_per_wave,
-                            int32_t lockstep, void* stream);
+                            int32_t waves_per_row, int32_t depth, int32_t slots,
+                            int32_t rows_per_wave, int32_t lockstep, void* stream);
 
 /* Static description of a status code. */
 const char* lrar_status_string(lrar_status status);

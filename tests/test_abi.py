@@ -333,7 +333,7 @@ def test_read_stream_rejects(L):
 
 
 def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=4, rows=4,
-        ptr=FAKE, odt=lrar.LRAR_BF16, nout=None, table=True, lock=0):
+        ptr=FAKE, odt=lrar.LRAR_BF16, nout=None, table=True, lock=0, wpr=1):
     """lrar_mix_stream through ctypes; out and out_ld may be one value or a list per output."""
     p = (ctypes.c_void_p * max(n, 1))(*([ptr] * max(n, 1)))
     l = (ctypes.c_int64 * max(n, 1))(*([ld] * max(n, 1)))
@@ -343,7 +343,7 @@ def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=
     ol = (ctypes.c_int64 * len(outs))(*lds)
     k = len(outs) if nout is None else nout
     return L.lrar_mix_stream(T, d, n, p, l, k, o if table else None, ol if table else None, odt,
-                             waves, depth, slots, rows, lock, None)
+                             waves, wpr, depth, slots, rows, lock, None)
 
 
 @pytest.mark.parametrize("kw", [
@@ -358,7 +358,8 @@ def mix(L, T=4, d=8, n=2, ld=8, out=FAKE * 2, out_ld=8, waves=8, depth=1, slots=
     dict(out=[FAKE * 2, FAKE * 2 + 16]),                        # two outputs overlap
     dict(out=[FAKE * 2, FAKE * 3], odt=lrar.LRAR_F32, out_ld=[8, 8], T=4,
          ptr=FAKE * 3 + 16),                                    # an output overlaps a source
-    dict(out=[FAKE * 2, None]), dict(lock=-1), dict(lock=3),
+    dict(out=[FAKE * 2, None]), dict(lock=-1), dict(lock=3), dict(wpr=0), dict(wpr=3),
+    dict(wpr=8),
 ])
 def test_mix_stream_rejects(L, kw):
     assert mix(L, **kw) == lrar.LRAR_ERR_INVALID, kw
@@ -370,6 +371,7 @@ def test_mix_stream_empty_is_ok(L):
     assert mix(L, T=0, out=None) == lrar.LRAR_OK
     assert mix(L, T=0, table=False) == lrar.LRAR_OK
     assert mix(L, T=0, lock=2) == lrar.LRAR_OK
+    assert mix(L, T=0, wpr=4, lock=1) == lrar.LRAR_OK
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -12,9 +12,11 @@ from gpu_util import f64, needs_gpu, say, sources
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-# (waves per CU, sources loaded together, units a lane, rows per wave per launch, lockstep)
-SHAPES = [(8, 1, 4, 4, 0), (4, 2, 2, 0, 1), (12, 4, 4, 2, 2), (32, 1, 16, 1, 1), (8, 2, 8, 3, 2)]
-SHAPE_IDS = [f"w{w}-p{p}-s{u}-c{c}-l{k}" for w, p, u, c, k in SHAPES]
+# (waves per CU, sources loaded together, units a lane, rows per row group per launch,
+# lockstep, waves per row)
+SHAPES = [(8, 1, 4, 4, 0, 1), (4, 2, 2, 0, 1, 1), (12, 4, 4, 2, 2, 1), (32, 1, 16, 1, 1, 1),
+          (8, 2, 8, 3, 2, 1), (8, 1, 4, 2, 1, 4), (12, 2, 2, 0, 2, 2), (16, 1, 8, 3, 0, 4)]
+SHAPE_IDS = [f"w{w}-p{p}-s{u}-c{c}-l{k}-r{g}" for w, p, u, c, k, g in SHAPES]
 
 
 def check_mean(srcs, outs, bf16):
@@ -35,12 +37,12 @@ def check_mean(srcs, outs, bf16):
                                       (129, 1024, 49, 1032)])
 @pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
 def test_mix_stream_mean(T, d, n, ld, shape):
-    waves, depth, slots, rows, lock = shape
+    waves, depth, slots, rows, lock, wpr = shape
     say(f"mix_stream T={T} d={d} n={n} ld={ld} shape={shape}")
     srcs = sources(n, T, d, "bf16", seed=40 + n, row_stride=ld)
     out = torch.full((T, d + 8), float("nan"), dtype=torch.bfloat16, device="cuda")[:, :d]
     lrar.lrar_mix_stream(srcs, out=out, waves_per_cu=waves, depth=depth, slots=slots,
-                         rows_per_wave=rows, lockstep=lock)
+                         rows_per_wave=rows, lockstep=lock, waves_per_row=wpr)
     torch.cuda.synchronize()
     check_mean(srcs, [out], True)
 
@@ -48,16 +50,16 @@ def test_mix_stream_mean(T, d, n, ld, shape):
 @pytest.mark.parametrize("T,d,n,nout,dt", [(300, 7168, 8, 12, "f32"), (300, 7168, 8, 12, "bf16"),
                                            (61, 4096, 12, 10, "f32"), (33, 2056, 3, 1, "f32"),
                                            (17, 1032, 4, 2, "bf16")])
-@pytest.mark.parametrize("shape", SHAPES[:3], ids=SHAPE_IDS[:3])
+@pytest.mark.parametrize("shape", SHAPES[:3] + SHAPES[5:7], ids=SHAPE_IDS[:3] + SHAPE_IDS[5:7])
 def test_mix_stream_outputs(T, d, n, nout, dt, shape):
     """Several outputs (of Phase 1's and the backward's mixes), float32 or bf16, some strided."""
-    waves, depth, slots, rows, lock = shape
+    waves, depth, slots, rows, lock, wpr = shape
     say(f"mix_stream outputs T={T} d={d} n={n} nout={nout} {dt} shape={shape}")
     srcs = sources(n, T, d, "bf16", seed=60 + n)
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     outs = [torch.full((T, d + 8 * (j % 2)), float("nan"), dtype=tdt, device="cuda")[:, :d]
             for j in range(nout)]
     lrar.lrar_mix_stream(srcs, out=outs, waves_per_cu=waves, depth=depth, slots=slots,
-                         rows_per_wave=rows, lockstep=lock)
+                         rows_per_wave=rows, lockstep=lock, waves_per_row=wpr)
     torch.cuda.synchronize()
     check_mean(srcs, outs, dt == "bf16")

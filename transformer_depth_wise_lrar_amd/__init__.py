@@ -92,7 +92,7 @@ def lib():
             L.lrar_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
             L.lrar_read_stream.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
             L.lrar_mix_stream.argtypes = [_i64, _i32, _i32, _vpp, _i64p, _i32, _vpp, _i64p,
-                                          _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
             L.lrar_read_stream_sink_bytes.argtypes = []
             L.lrar_read_stream_sink_bytes.restype = ctypes.c_size_t
             for fn in ("lrar_forward", "lrar_forward_save", "lrar_backward_saved",
@@ -527,14 +527,14 @@ def lrar_copy(dst, src, stream=None, prepare: bool = False):
 
 
 def lrar_mix_stream(srcs: Sequence, out=None, waves_per_cu: int = 8, depth: int = 1,
-                    slots: int = 4, rows_per_wave: int = 4, lockstep: int = 0, stream=None,
-                    prepare: bool = False):
+                    slots: int = 4, rows_per_wave: int = 4, lockstep: int = 0,
+                    waves_per_row: int = 1, stream=None, prepare: bool = False):
     """A plain stream with a kernel's traffic: reads srcs (n bf16 tensors [T, d]) and writes
     their mean to each tensor of out (a tensor [T, d], or a list of them, all float32 or all
     bf16; default one bf16 tensor). The reference kernel for the same-traffic bandwidth
     ceiling; the launch shape (waves per CU, sources loaded together, 16-byte units a lane,
-    rows per wave per launch, lockstep 0 / per row / per source group) is the caller's. Returns
-    out."""
+    rows per row group per launch, lockstep 0 / per row / per source group, waves sharing a
+    row) is the caller's. Returns out."""
     torch = _torch()
     ptrs, lds, io, T, d = _src_table(srcs, LRAR_BF16)
     if out is None:
@@ -551,8 +551,9 @@ def lrar_mix_stream(srcs: Sequence, out=None, waves_per_cu: int = 8, depth: int 
         _need(o, (T, d), odt, f"out[{j}]")
         optrs[j], olds[j] = _rows(o, f"out[{j}]")
     args = (T, d, len(srcs), ptrs, lds, len(outs), optrs, olds,
-            LRAR_F32 if odt == torch.float32 else LRAR_BF16, int(waves_per_cu), int(depth),
-            int(slots), int(rows_per_wave), int(lockstep), _stream(stream))
+            LRAR_F32 if odt == torch.float32 else LRAR_BF16, int(waves_per_cu),
+            int(waves_per_row), int(depth), int(slots), int(rows_per_wave), int(lockstep),
+            _stream(stream))
     return _run(lib().lrar_mix_stream, args, out, (srcs, outs), prepare)
 
 

@@ -835,14 +835,16 @@ lrar_status lrar_read_stream(const void* src, size_t bytes, void* sink, void* st
 lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* src,
                             const int64_t* src_ld, int32_t nout, void* const* out,
                             const int64_t* out_ld, lrar_dtype out_dtype, int32_t waves_per_cu,
-                            int32_t depth, int32_t slots, int32_t rows_per_wave, int32_t lockstep,
-                            void* stream) {
+                            int32_t waves_per_row, int32_t depth, int32_t slots,
+                            int32_t rows_per_wave, int32_t lockstep, void* stream) {
   const char* fn = "lrar_mix_stream";
   if (T < 0) return fail(LRAR_ERR_INVALID, "%s: T = %lld < 0", fn, (long long)T);
   if (d < 8 || d % 8 != 0)
     return fail(LRAR_ERR_INVALID, "%s: d = %d must be a positive multiple of 8", fn, d);
   if (waves_per_cu < 4 || waves_per_cu > 32 || waves_per_cu % 4 != 0)
     return fail(LRAR_ERR_INVALID, "%s: waves_per_cu = %d must be 4, 8, ..., 32", fn, waves_per_cu);
+  if (waves_per_row != 1 && waves_per_row != 2 && waves_per_row != 4)
+    return fail(LRAR_ERR_INVALID, "%s: waves_per_row = %d must be 1, 2 or 4", fn, waves_per_row);
   if (depth != 1 && depth != 2 && depth != 4)
     return fail(LRAR_ERR_INVALID, "%s: depth = %d must be 1, 2 or 4", fn, depth);
   if (slots != 2 && slots != 4 && slots != 8 && slots != 16)
@@ -886,8 +888,9 @@ lrar_status lrar_mix_stream(int64_t T, int32_t d, int32_t n, const void* const* 
   st = check_disjoint(fn, R);
   if (st != LRAR_OK) return st;
   return device_status(lrar::launch_mix_stream(S, n, T, d, O, nout, out_dtype == LRAR_F32,
-                                               waves_per_cu, depth, slots, rows_per_wave,
-                                               lockstep, static_cast<hipStream_t>(stream)),
+                                               waves_per_cu, waves_per_row, depth, slots,
+                                               rows_per_wave, lockstep,
+                                               static_cast<hipStream_t>(stream)),
                        fn);
 }
 
@@ -966,10 +969,11 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
 
 // A kernel's traffic with next to no arithmetic: for the rows [r0, r1), the n bf16 source rows
 // are read and their mean (float32 sums in source order) written to each of the nout output
-// rows, as float32 (F32OUT) or rounded to nearest-even bf16. A wave takes rows in bands (row
-// r0 + w + k * waves, as the read's tiles) and a row in groups of up to NU chunks of 64 16-byte
-// units, NU units a lane; DEPTH sources are loaded before any is added, and the loads are
-// waited for together. One bf16 output is a read's traffic; more outputs, or float32 ones,
+// rows, as float32 (F32OUT) or rounded to nearest-even bf16. A row goes to wpr waves of one
+// workgroup (1, 2 or 4; the row group g of the launch takes rows r0 + g + k * groups, as the
+// read's tiles), which take its chunks of 64 16-byte units in turn, NU chunks a wave per
+// pass (NU units a lane, chunk k * wpr + w of the pass to wave w of the row); DEPTH sources
+// are loaded before any is added, and the loads are waited for together. One bf16 output is a read's traffic; more outputs, or float32 ones,
 // give the write-heavy mixes of Phase 1 and the backward. lock = 1 or 2: the workgroup's waves
 // meet at a barrier once per row or once per group of DEPTH sources, as the reads keep their
 // waves in lockstep, in the steps where every wave of the workgroup has a row (a condition all
@@ -977,15 +981,19 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
 template <int DEPTH, int NU, bool F32OUT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NU >= 16 ? 2 : 1)))
 void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList out, int nout,
-                  float w, int lock) {
+                  float w, int wpr, int lock) {
   const int lane = threadIdx.x & (kWave - 1);
+  // wpr divides the workgroup's 4 waves, so a row group never spans two workgroups
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_in_block();
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  const int64_t last_wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + kWavesPerBlock - 1;
-  for (int64_t row = r0 + wave; row < r1; row += waves) {
-    const bool all_rows = (row - wave) + last_wave < r1;
+  const int64_t group = wave / wpr;
+  const int wr = static_cast<int>(wave % wpr);
+  const int64_t groups = static_cast<int64_t>(gridDim.x) * (kWavesPerBlock / wpr);
+  const int64_t last_group =
+      (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + kWavesPerBlock - 1) / wpr;
+  for (int64_t row = r0 + group; row < r1; row += groups) {
+    const bool all_rows = (row - group) + last_group < r1;
     if (lock == 1 && all_rows) __syncthreads();
-    for (int g = 0; g < nur; g += NU * kWave) {
+    for (int g = 0; g < nur; g += NU * kWave * wpr) {
       float acc[NU][8];
 #pragma unroll
       for (int k = 0; k < NU; ++k)
@@ -1004,7 +1012,7 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
               // two runs of 4 columns, 256 apart: each 16-byte float32 store then lands next
               // to its neighbour lanes' (1 KiB a store instruction). d is a multiple of 8, so
               // a run lies wholly inside the row or wholly past it.
-              const int c0 = (g + k * kWave) * 8 + 4 * lane;
+              const int c0 = (g + (k * wpr + wr) * kWave) * 8 + 4 * lane;
               const u32x2 lo = c0 < nur * 8
                   ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rp + c0))
                   : u32x2{0u, 0u};
@@ -1013,7 +1021,7 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
                   : u32x2{0u, 0u};
               v[b][k].raw = u32x4{lo.x, lo.y, hi.x, hi.y};
             } else {
-              const int u = g + k * kWave + lane;
+              const int u = g + (k * wpr + wr) * kWave + lane;
               if (u < nur) v[b][k].load(rp + static_cast<int64_t>(u) * 8);
               else v[b][k].zero();
             }
@@ -1035,7 +1043,7 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
 #pragma unroll
         for (int k = 0; k < NU; ++k) {
           if constexpr (F32OUT) {
-            const int c0 = (g + k * kWave) * 8 + 4 * lane;
+            const int c0 = (g + (k * wpr + wr) * kWave) * 8 + 4 * lane;
             float* op = static_cast<float*>(out.ptr[j]) + row * out.ld[j] + c0;
             if (c0 < nur * 8)
               out_store(f32x4{acc[k][0], acc[k][1], acc[k][2], acc[k][3]},
@@ -1044,7 +1052,7 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
               out_store(f32x4{acc[k][4], acc[k][5], acc[k][6], acc[k][7]},
                         reinterpret_cast<f32x4*>(op + 256));
           } else {
-            const int u = g + k * kWave + lane;
+            const int u = g + (k * wpr + wr) * kWave + lane;
             if (u < nur) {
               Unit<bf16_bits, 8> y;
               y.set(acc[k]);
@@ -1060,25 +1068,28 @@ void k_mix_stream(SrcList src, int n, int64_t r0, int64_t r1, int nur, DstList o
 
 template <int DEPTH, int NU>
 void launch_mix_stream_t(const SrcList& src, int n, int64_t r0, int64_t r1, int nur,
-                         const DstList& out, int nout, bool f32_out, float w, int lock,
+                         const DstList& out, int nout, bool f32_out, float w, int wpr, int lock,
                          unsigned blocks, hipStream_t s) {
   if (f32_out)
     hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, true>), dim3(blocks), dim3(kBlock), 0, s, src, n,
-                       r0, r1, nur, out, nout, w, lock);
+                       r0, r1, nur, out, nout, w, wpr, lock);
   else
     hipLaunchKernelGGL((k_mix_stream<DEPTH, NU, false>), dim3(blocks), dim3(kBlock), 0, s, src,
-                       n, r0, r1, nur, out, nout, w, lock);
+                       n, r0, r1, nur, out, nout, w, wpr, lock);
 }
 
 hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const DstList& out,
-                             int nout, bool f32_out, int waves_per_cu, int depth, int slots,
-                             int rows_per_wave, int lockstep, hipStream_t s) {
+                             int nout, bool f32_out, int waves_per_cu, int waves_per_row,
+                             int depth, int slots, int rows_per_wave, int lockstep,
+                             hipStream_t s) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t blocks = static_cast<int64_t>(cus) * waves_per_cu / kWavesPerBlock;
-  const int64_t span = rows_per_wave > 0 ? blocks * kWavesPerBlock * rows_per_wave : T;
+  // rows_per_wave rows for each row group of the launch
+  const int64_t span =
+      rows_per_wave > 0 ? blocks * (kWavesPerBlock / waves_per_row) * rows_per_wave : T;
   const int nur = d / 8;
   const float w = 1.0f / static_cast<float>(n);
   const unsigned g = static_cast<unsigned>(blocks);
@@ -1086,7 +1097,8 @@ hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const 
     const int64_t r1 = r0 + span < T ? r0 + span : T;
     const int key = 10 * depth + slots;
 #define LRAR_MIX(D, U) \
-  launch_mix_stream_t<D, U>(src, n, r0, r1, nur, out, nout, f32_out, w, lockstep, g, s)
+  launch_mix_stream_t<D, U>(src, n, r0, r1, nur, out, nout, f32_out, w, waves_per_row, lockstep, \
+                            g, s)
     switch (key) {
       case 12: LRAR_MIX(1, 2); break;
       case 14: LRAR_MIX(1, 4); break;

@@ -149,7 +149,8 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStream_t s);
 // A kernel's traffic as a plain stream (lrar_mix_stream), in the launch shape given.
 hipError_t launch_mix_stream(const SrcList& src, int n, int64_t T, int d, const DstList& out,
-                             int nout, bool f32_out, int waves_per_cu, int depth, int slots,
-                             int rows_per_wave, int lockstep, hipStream_t s);
+                             int nout, bool f32_out, int waves_per_cu, int waves_per_row,
+                             int depth, int slots, int rows_per_wave, int lockstep,
+                             hipStream_t s);
 
 }  // namespace lrar
