@@ -973,8 +973,9 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
 // workgroup (1, 2 or 4; the row group g of the launch takes rows r0 + g + k * groups, as the
 // read's tiles), which take its chunks of 64 16-byte units in turn, NU chunks a wave per
 // pass (NU units a lane, chunk k * wpr + w of the pass to wave w of the row); DEPTH sources
-// are loaded before any is added, and the loads are waited for together. One bf16 output is a read's traffic; more outputs, or float32 ones,
-// give the write-heavy mixes of Phase 1 and the backward. lock = 1 or 2: the workgroup's waves
+// are loaded before any is added, and the loads are waited for together. One bf16 output is a
+// read's traffic; more outputs, or float32 ones, give the write-heavy mixes of Phase 1 and the
+// backward. lock = 1 or 2: the workgroup's waves
 // meet at a barrier once per row or once per group of DEPTH sources, as the reads keep their
 // waves in lockstep, in the steps where every wave of the workgroup has a row (a condition all
 // of them compute alike, so they meet the same barriers).
