@@ -8,7 +8,8 @@ column of its h are NaN. Rows without such values match the oracle as usual.
 
 Every kernel shape of the forward read is taken: one-wave rows (d = 1024, 2048), rows shared
 by four waves with a spread key (d = 7168, r = 64) and by two waves with the key in the row
-units (d = 7168, r = 1792), in the online and the two-pass variant, bf16 and fp32.
+units (d = 7168, r = 1792), in the online and the two-pass variant, bf16 and fp32. Phase 1 and
+the Phase-2 merge take non-finite value columns the same way.
 """
 import numpy as np
 import pytest
@@ -82,3 +83,81 @@ def test_nonfinite_values_and_keys(d, r, n, io, variant):
     lrar.lrar_forward(srcs, q, r, eps, out=out, alpha=alpha, variant=variant)
     torch.cuda.synchronize()
     check(out, alpha, srcs, q, r, eps, io, where)
+
+
+def same_nonfinite(y, ref, where):
+    for name, test in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        got, want = test(y), test(ref)
+        assert np.array_equal(got, want), (
+            f"{where}: {name} at {np.argwhere(got != want)[:4].tolist()} differs")
+
+
+def finite_part(*arrays):
+    return [np.where(np.isfinite(a), a, 0.0) for a in arrays]
+
+
+@pytest.mark.parametrize("nq", [3, 12])
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d,r", [(1024, 64), (7168, 1792)])
+def test_stats_nonfinite_values(d, r, acc_dtype, nq):
+    """Phase 1 (the technical-report summary, "Method"): a NaN in a value column of one source
+    makes that column of every query's accumulator NaN, an infinity makes it an infinity of
+    the same sign; m and l are untouched."""
+    Tq, n, eps = 40, 8, 1e-6
+    where = f"stats nonfinite d={d} r={r} acc={acc_dtype} nq={nq}"
+    say(f"[nonfinite] {where}")
+    srcs = sources(n, Tq, d, "bf16", seed=995 + d)
+    qs = query(r, seed=996 + r, std=0.1, nq=nq)
+    with torch.no_grad():
+        srcs[1][5, 3] = float("nan")
+        srcs[2][17, 3] = float("inf")
+        srcs[3][23, 4] = float("-inf")
+    m, l, acc = lrar.lrar_forward_stats(srcs, qs, r, eps, acc_dtype=acc_dtype)
+    torch.cuda.synchronize()
+    s64 = [f64(s) for s in srcs]
+    q64 = f64(qs)
+    m_o, l_o, acc_o = oracle.stats(s64, q64, r, eps)
+    m_g, l_g, acc_g = f64(m), f64(l), f64(acc)
+    io = "bf16" if acc_dtype == torch.bfloat16 else "f32"
+    for s in range(nq):
+        same_nonfinite(acc_g[s], acc_o[s], f"{where} query {s} acc")
+        assert np.isnan(acc_o[s][5, 3]) and np.isposinf(acc_o[s][17, 3])
+        z_o, _ = oracle.scores(s64, q64[s], r, eps)
+        a_g, a_o = finite_part(acc_g[s], acc_o[s])
+        parity.assert_stats(m_g[s], l_g[s], a_g, m_o[s], l_o[s], a_o, z_o, finite_part(*s64),
+                            io, f"{where} query {s}")
+
+
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d,r", [(1024, 64), (7168, 1792)])
+def test_merge_nonfinite_values(d, r, acc_dtype):
+    """Phase 2: a NaN in the prior accumulator or an infinity in the partial sum's value
+    columns reaches only that column of h."""
+    Tm, eps = 41, 1e-6
+    where = f"merge nonfinite d={d} r={r} acc={acc_dtype}"
+    say(f"[nonfinite] {where}")
+    inter = sources(4, Tm, d, "bf16", seed=997)
+    extra = sources(1, Tm, d, "bf16", seed=998)
+    q = query(r, seed=999, std=0.1)
+    s64 = [f64(s) for s in inter]
+    m_o, l_o, acc_o = oracle.stats(s64, f64(q)[None, :], r, eps)
+    acc_o = acc_o[0].copy()
+    acc_o[5, 3] = np.nan
+    m = torch.tensor(m_o[0], dtype=torch.float32, device="cuda")
+    l = torch.tensor(l_o[0], dtype=torch.float32, device="cuda")
+    acc = torch.tensor(acc_o, dtype=torch.float32).to(acc_dtype).cuda()
+    with torch.no_grad():
+        extra[0][17, 3] = float("inf")
+    out = lrar.lrar_merge(m, l, acc, extra, q, r, eps, io_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e64 = [f64(s) for s in extra]
+    m_in, l_in, acc_in = f64(m), f64(l), f64(acc)
+    h_ref, m_ref, l_ref = oracle.merge(m_in, l_in, acc_in, e64, f64(q), r, eps)
+    y = f64(out)
+    same_nonfinite(y, h_ref, where)
+    assert np.isnan(h_ref[5, 3]) and np.isposinf(h_ref[17, 3])
+    z_e, _ = oracle.scores(e64, f64(q), r, eps)
+    w_extra = np.exp(z_e - m_ref[:, None]) / l_ref[:, None]
+    w_prior = l_in * np.exp(m_in - m_ref) / l_ref
+    y_f, h_f, an_f = finite_part(y, h_ref, acc_in / l_in[:, None])
+    parity.assert_merge(y_f, h_f, w_prior, an_f, w_extra, finite_part(*e64), "bf16", where)
