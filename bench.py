@@ -418,8 +418,6 @@ def cpu_baseline(torch, budget_s=15.0):
     """The fp64 oracle on the first R rows of the headline workload, all 49 sites, run on the
     host cores this process may use (the oracle itself is single-threaded), at most the host
     CPU share of one GPU."""
-    import numpy as np
-
     import oracle
     from transformer_depth_wise_lrar_amd import synth
 
